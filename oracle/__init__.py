@@ -1,0 +1,213 @@
+"""CPU oracle for Reduced Matrix Multiplication -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library and its Python binding
+never import it, and it imports nothing from them: the two sides share only
+the seeded inputs of the ``synthetic`` package.
+
+What it computes (fp64 throughout; C code in ``rmm_oracle.c``), following
+"Reduced Matrix Multiplication: Input-Adaptive Matrix-Product Reduction for
+LLM Inference":
+
+* ``k_of``       -- |I| = ceil(rho d)                       (Sec. 3.2)
+* ``colnorm``    -- s_j = ||A[:, j]||_2                     (Sec. 3.2)
+* ``topk``       -- I = TopK(s, k), ties to the lower index, listed ascending
+* ``reduced_product`` -- alpha * A[:, I] B[I, :]            (Sec. 3.2, 3.3)
+* ``rmm``        -- the four steps in the paper's order
+* ``attention_scores`` -- per-Q-head selection applied to the matching GQA
+  K head, scaled by 1/sqrt(d_h)                             (Sec. 3.3)
+* ``diagnostics`` -- retained energy (App. B.4 / eq. 16), the Prop. 1 bound
+  (eq. 12), the Cor. 1 bound (eq. 14) and the relative bound (eq. 17).
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against closed
+forms, library routines, brute force or invariants that the paper fixes.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rmm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (-O2, no BLAS, no intrinsics)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared", "-pthread",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64, f64, i32p = ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)
+        f64p, i64p = ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_k.argtypes = [f64, i64]
+        lib.oracle_k.restype = i64
+        lib.oracle_colnorm.argtypes = [f64p, i64, i64, i64, f64p]
+        lib.oracle_colnorm.restype = None
+        lib.oracle_topk.argtypes = [f64p, i64, i64, i32p]
+        lib.oracle_topk.restype = ctypes.c_int
+        lib.oracle_reduced_product.argtypes = [f64p, i64, f64p, i64, i64, i32p, i64, f64, i64p, i64,
+                                               f64p, ctypes.c_int]
+        lib.oracle_reduced_product.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def k_of(rho: float, d: int) -> int:
+    """|I| = ceil(rho d); 0 for an invalid rho or d (see rmm_oracle.c)."""
+    return int(_load().oracle_k(float(rho), int(d)))
+
+
+def colnorm(A: np.ndarray) -> np.ndarray:
+    """Column L2 norms of a 2-D array, fp64."""
+    A64 = _f64(A)
+    if A64.ndim != 2:
+        raise ValueError("colnorm expects a 2-D array")
+    n, d = A64.shape
+    s = np.empty(d, dtype=np.float64)
+    _load().oracle_colnorm(_ptr(A64, ctypes.c_double), n, d, d, _ptr(s, ctypes.c_double))
+    return s
+
+
+def topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores (ties -> lower index), ascending, int32."""
+    s64 = _f64(s)
+    idx = np.empty(int(k), dtype=np.int32)
+    if _load().oracle_topk(_ptr(s64, ctypes.c_double), s64.size, int(k), _ptr(idx, ctypes.c_int32)) != 0:
+        raise ValueError(f"bad topk arguments d={s64.size} k={k}")
+    return idx
+
+
+def reduced_product(A: np.ndarray, B: np.ndarray, idx: np.ndarray, alpha: float = 1.0,
+                    rows: Optional[Sequence[int]] = None, threads: Optional[int] = None) -> np.ndarray:
+    """alpha * A[rows][:, idx] @ B[idx, :] by the plain triple loop, fp64."""
+    A64, B64 = _f64(A), _f64(B)
+    n, d = A64.shape
+    d2, m = B64.shape
+    if d != d2:
+        raise ValueError("inner dimensions differ")
+    idx32 = np.ascontiguousarray(idx, dtype=np.int32)
+    if idx32.size and (idx32.min() < 0 or idx32.max() >= d):
+        raise ValueError("index out of range")
+    if rows is None:
+        rows_arr = None
+        nrows = n
+        rows_p = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        if rows_arr.size and (rows_arr.min() < 0 or rows_arr.max() >= n):
+            raise ValueError("row out of range")
+        nrows = rows_arr.size
+        rows_p = _ptr(rows_arr, ctypes.c_int64)
+    Y = np.empty((nrows, m), dtype=np.float64)
+    rc = _load().oracle_reduced_product(_ptr(A64, ctypes.c_double), d, _ptr(B64, ctypes.c_double), m, m,
+                                        _ptr(idx32, ctypes.c_int32), idx32.size, float(alpha), rows_p,
+                                        nrows, _ptr(Y, ctypes.c_double), int(threads or host_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle_reduced_product failed")
+    return Y
+
+
+@dataclasses.dataclass
+class Result:
+    k: int
+    s: np.ndarray      # fp64 column norms
+    idx: np.ndarray    # int32, ascending
+    Y: Optional[np.ndarray]  # fp64 (rows requested) or None
+
+
+def rmm(A: np.ndarray, B: Optional[np.ndarray], rho: float, alpha: float = 1.0,
+        rows: Optional[Sequence[int]] = None, threads: Optional[int] = None) -> Result:
+    """RMM_rho(A, B) in the paper's order: score, TopK, gather, reduced product.
+
+    ``B=None`` stops after the selection.
+    """
+    d = np.shape(A)[1]
+    k = k_of(rho, d)
+    if k == 0:
+        raise ValueError(f"invalid rho={rho!r} for d={d}")
+    s = colnorm(A)
+    idx = topk(s, k)
+    Y = None if B is None else reduced_product(A, B, idx, alpha, rows, threads)
+    return Result(k, s, idx, Y)
+
+
+def attention_scores(Q: np.ndarray, K: np.ndarray, rho: float, alpha: float,
+                     heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
+                     threads: Optional[int] = None, with_product: bool = True):
+    """Reduced QK^T per query head with grouped-query attention (Sec. 3.3).
+
+    Q is (H_q, L_q, d_h), K is (H_kv, L_k, d_h).  For head h the score is
+    computed from Q_h's column norms only and the same dimensions are taken
+    from K head g = h // (H_q / H_kv) (reading: contiguous grouping).  The
+    product is alpha * Q_h[:, I] K_g[:, I]^T with alpha = 1/sqrt(d_h).
+    Returns a list of Result (one per requested head).
+    """
+    hq, hkv = Q.shape[0], K.shape[0]
+    if hq % hkv:
+        raise ValueError("query heads must be a multiple of key heads")
+    group = hq // hkv
+    out = []
+    for h in (range(hq) if heads is None else heads):
+        Bt = np.ascontiguousarray(np.asarray(K[h // group], dtype=np.float64).T)  # d_h x L_k
+        out.append(rmm(Q[h], Bt if with_product else None, rho, alpha, rows, threads))
+    return out
+
+
+def diagnostics(A: np.ndarray, B: np.ndarray, idx: np.ndarray) -> dict:
+    """Error-bound quantities of App. E for a selection ``idx``.
+
+    retained_energy = sum_{j in I} s_j^2 / sum_j s_j^2 (App. B.4) = 1 - eps_A;
+    prop1 = sum_{j not in I} ||A_j|| ||B_j||          (eq. 12);
+    cor1  = ||A[:, Ic]||_F ||B[Ic, :]||_F             (eq. 14);
+    rel17 = sqrt(eps_A eps_B)                         (eq. 17).
+    """
+    a = colnorm(A)
+    b = colnorm(np.ascontiguousarray(np.asarray(B, dtype=np.float64).T))  # row norms of B
+    keep = np.zeros(a.size, dtype=bool)
+    keep[np.asarray(idx)] = True
+    drop = ~keep
+    ea_tot, eb_tot = float(np.sum(a * a)), float(np.sum(b * b))
+    ea_drop, eb_drop = float(np.sum(a[drop] ** 2)), float(np.sum(b[drop] ** 2))
+    eps_a = ea_drop / ea_tot if ea_tot > 0 else 0.0
+    eps_b = eb_drop / eb_tot if eb_tot > 0 else 0.0
+    return {
+        "retained_energy": 1.0 - eps_a,
+        "eps_A": eps_a,
+        "eps_B": eps_b,
+        "prop1": float(np.sum(a[drop] * b[drop])),
+        "cor1": float(np.sqrt(ea_drop) * np.sqrt(eb_drop)),
+        "rel17": float(np.sqrt(eps_a * eps_b)),
+        "normA_F": float(np.sqrt(ea_tot)),
+        "normB_F": float(np.sqrt(eb_tot)),
+    }

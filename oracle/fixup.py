@@ -1,0 +1,78 @@
+"""Boundary-gap fix-up of synthetic activations -- TEST INFRASTRUCTURE ONLY.
+
+The GPU ranks fp32 column norms and the oracle ranks fp64 ones.  Both see the
+same stored values, but the two sums round differently, so two columns whose
+norms agree to ~1e-7 could swap places at the TopK boundary.  To make the
+index-set comparison exact by construction, every test input is nudged until,
+for every k the test uses, the k-th largest norm exceeds the (k+1)-th by a
+relative gap of at least ``rel_gap`` (1e-3, far above either side's rounding
+error): the dropped columns that sit inside the gap are multiplied by 0.99
+(then re-rounded to the storage precision) and the norms recomputed, until
+every boundary passes.
+
+The norms come from this package's own fp64 ``colnorm``.  A single row
+(n = 1, decode) needs no fix-up: there s_j = |a_j| is exact in both
+precisions and both sides break exact ties toward the lower index.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Tuple
+
+import numpy as np
+
+from synthetic import round_to_bf16
+
+from . import colnorm
+
+
+def _boundary_ok(s: np.ndarray, order: np.ndarray, k: int, rel_gap: float) -> Tuple[bool, np.ndarray]:
+    sk = s[order[k - 1]]
+    sk1 = s[order[k]]
+    if sk <= 0.0:
+        raise ValueError("k-th largest norm is zero; the gap cannot be opened by scaling")
+    if (sk - sk1) / sk >= rel_gap:
+        return True, order[:0]
+    dropped = order[k:]
+    inside = dropped[s[dropped] >= sk * (1.0 - rel_gap)]
+    return False, inside
+
+
+def enforce_gap(A: np.ndarray, ks: Iterable[int], dtype: str, rel_gap: float = 1e-3,
+                max_iter: int = 1000) -> Tuple[np.ndarray, int]:
+    """Return (A', touched) with every TopK boundary in ``ks`` separated.
+
+    ``A`` is a 2-D float32 array of values exact in ``dtype`` ("bf16" or
+    "f32"); a copy is modified.  ``touched`` counts column scalings applied.
+    """
+    A = np.array(A, dtype=np.float32, copy=True)
+    if A.ndim != 2:
+        raise ValueError("enforce_gap expects a 2-D array")
+    d = A.shape[1]
+    ks = sorted({int(k) for k in ks if 0 < int(k) < d})
+    touched = 0
+    for _ in range(max_iter):
+        s = colnorm(A)
+        order = np.lexsort((np.arange(d), -s))
+        bad = []
+        for k in ks:
+            ok, inside = _boundary_ok(s, order, k, rel_gap)
+            if not ok:
+                bad.append(inside)
+        if not bad:
+            return A, touched
+        cols = np.unique(np.concatenate(bad))
+        scaled = A[:, cols] * np.float32(0.99)
+        A[:, cols] = round_to_bf16(scaled) if dtype == "bf16" else scaled.astype(np.float32)
+        touched += cols.size
+    raise RuntimeError("gap fix-up did not converge")
+
+
+def enforce_gap_batched(A: np.ndarray, ks: Iterable[int], dtype: str, rel_gap: float = 1e-3):
+    """Apply ``enforce_gap`` to every matrix of a (batch, n, d) array."""
+    out = np.empty_like(A, dtype=np.float32)
+    touched = 0
+    ks = list(ks)
+    for b in range(A.shape[0]):
+        out[b], t = enforce_gap(A[b], ks, dtype, rel_gap)
+        touched += t
+    return out, touched

@@ -1,0 +1,237 @@
+"""Seeded synthetic inputs for the reduced-matrix-multiplication workloads.
+
+This module only draws random numbers and rounds them to the storage
+precision.  It holds none of the method's arithmetic (no norms, no ranking,
+no products): both the GPU path's tests and the CPU oracle take their inputs
+from here, so nothing here may depend on either of them.
+
+The shapes stand in for the activation/weight products of Llama-3.1-8B and
+70B layers that the paper "Reduced Matrix Multiplication: Input-Adaptive
+Matrix-Product Reduction for LLM Inference" reduces (Sec. 3.1 writes every
+product as Y = A B with A the n x d activation block and B the d x m weight or
+intermediate; Sec. 3.3 applies it to projections, MLPs and QK^T).  The real
+weights and prompts are not available, so the value distributions imitate
+what those layers look like: per-column log-normal activation scales with a
+few large outlier columns, Gaussian weights with variance 1/d, and a
+SwiGLU-like gated activation for the down projection.
+
+Recipe (one numpy ``Generator(PCG64(seed))`` per configuration, float64 draws
+rounded to float32 and then, for bf16 configurations, to bf16 with
+round-to-nearest-even).  Draw order within a configuration: column scales,
+outlier picks, A row-major, B row-major.  Large arrays are drawn in row
+chunks; numpy's ``standard_normal`` consumes its stream element by element,
+so chunking does not change the values.
+
+Every array is returned as float32 whose values are exactly representable in
+the configuration's storage dtype; ``as_bf16_bits`` gives the raw bf16 bit
+patterns for the device side.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Case",
+    "round_to_bf16",
+    "as_bf16_bits",
+    "lognormal_outlier_activations",
+    "gated_activations",
+    "gaussian_weights",
+    "make_case",
+    "make_decode_case",
+    "CONFIGS",
+    "sha256_of",
+]
+
+_CHUNK_ELEMS = 1 << 24  # rows per draw chunk are chosen so a chunk holds ~16M values
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32.
+
+    bf16 keeps the upper 16 bits of the IEEE-754 binary32 pattern.  Adding
+    0x7FFF plus the lowest kept bit and truncating implements
+    round-to-nearest-even for finite values.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def as_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Raw bf16 bit patterns (uint16) of float32 values that are bf16-exact."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("values are not exactly representable in bf16")
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(x32)
+    if dtype == "f32":
+        return x32
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _rows_per_chunk(cols: int) -> int:
+    return max(1, _CHUNK_ELEMS // max(1, cols))
+
+
+def _column_scales(rng: np.random.Generator, d: int, n_outliers: int, outlier_factor: float) -> np.ndarray:
+    """Log-normal per-column scales c_j = exp(N(0,1)) with a few columns boosted."""
+    c = np.exp(rng.standard_normal(d))
+    if n_outliers > 0:
+        picks = rng.choice(d, size=n_outliers, replace=False)
+        c[picks] *= outlier_factor
+    return c
+
+
+def lognormal_outlier_activations(rng: np.random.Generator, n: int, d: int, dtype: str,
+                                  n_outliers: int, outlier_factor: float = 20.0,
+                                  scales: Optional[np.ndarray] = None):
+    """A[i, j] = N(0,1) * c_j.  Returns (A, c)."""
+    c = _column_scales(rng, d, n_outliers, outlier_factor) if scales is None else scales
+    out = np.empty((n, d), dtype=np.float32)
+    step = _rows_per_chunk(d)
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        z = rng.standard_normal((r1 - r0, d))
+        out[r0:r1] = _store(z * c[None, :], dtype)
+    return out, c
+
+
+def gated_activations(rng: np.random.Generator, n: int, d: int, dtype: str):
+    """Post-SwiGLU-like block: A[i,j] = c_j * N(0,1) * sigmoid(N(0,1)).
+
+    The two normals are independent per element (value draw, then gate draw,
+    interleaved per row chunk).  Returns (A, c).
+    """
+    c = np.exp(rng.standard_normal(d))
+    out = np.empty((n, d), dtype=np.float32)
+    step = _rows_per_chunk(2 * d)
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        v = rng.standard_normal((r1 - r0, d))
+        g = rng.standard_normal((r1 - r0, d))
+        out[r0:r1] = _store(c[None, :] * v / (1.0 + np.exp(-g)), dtype)
+    return out, c
+
+
+def gaussian_weights(rng: np.random.Generator, d: int, m: int, dtype: str) -> np.ndarray:
+    """B ~ N(0, 1/d), d x m row-major."""
+    sigma = 1.0 / math.sqrt(d)
+    out = np.empty((d, m), dtype=np.float32)
+    step = _rows_per_chunk(m)
+    for r0 in range(0, d, step):
+        r1 = min(d, r0 + step)
+        out[r0:r1] = _store(rng.standard_normal((r1 - r0, m)) * sigma, dtype)
+    return out
+
+
+@dataclasses.dataclass
+class Case:
+    """One workload instance.
+
+    ``A``/``B`` are float32 arrays holding values exact in ``dtype``.
+    For the batched attention case ``A`` is (H_q, L, d_h) queries and ``B`` is
+    (H_kv, L, d_h) keys; the product is Q_h K_g^T with g = h // group.
+    """
+    name: str
+    dtype: str
+    A: np.ndarray
+    B: np.ndarray
+    rhos: tuple
+    alpha: float = 1.0
+    transB: bool = False
+    group: int = 1
+    scales: Optional[np.ndarray] = None
+
+    @property
+    def batched(self) -> bool:
+        return self.A.ndim == 3
+
+
+# name -> (seed, description); sizes are the ones the workloads are quoted at.
+CONFIGS = {
+    "c1": "tiny fp32: A 64x256 lognormal+4 outliers, B 256x128 ~N(0,1/256), rho 0.5",
+    "c2": "8B projection: A 4096x4096 lognormal+0.5% outliers, B 4096x4096, bf16, rho .5/.7/.8/1",
+    "c3": "8B MLP down: A 2048x14336 gated lognormal, B 14336x4096, bf16, rho .5/.7/.8/1",
+    "c4": "QK^T GQA: Q 32x4096x128, K 8x4096x128, per-(head,dim) lognormal, bf16, rho .5 (+1)",
+    "c5": "70B MLP up: A 4096x8192 lognormal+4 outliers, B 8192x28672, bf16, rho .8 (+1)",
+}
+
+
+def make_case(name: str, scale: Optional[dict] = None) -> Case:
+    """Build configuration ``name`` (c1..c5).
+
+    ``scale`` optionally overrides sizes (keys n, d, m, heads, kv_heads, L,
+    dh) to get a smaller instance of the same distribution for quick tests;
+    the draw order is unchanged.
+    """
+    s = dict(scale or {})
+    if name == "c1":
+        rng = np.random.Generator(np.random.PCG64(1))
+        n, d, m = s.get("n", 64), s.get("d", 256), s.get("m", 128)
+        A, c = lognormal_outlier_activations(rng, n, d, "f32", n_outliers=min(4, d))
+        B = gaussian_weights(rng, d, m, "f32")
+        return Case("c1", "f32", A, B, (0.5,), scales=c)
+    if name == "c2":
+        rng = np.random.Generator(np.random.PCG64(2))
+        n, d, m = s.get("n", 4096), s.get("d", 4096), s.get("m", 4096)
+        A, c = lognormal_outlier_activations(rng, n, d, "bf16", n_outliers=math.ceil(0.005 * d))
+        B = gaussian_weights(rng, d, m, "bf16")
+        return Case("c2", "bf16", A, B, (0.5, 0.7, 0.8, 1.0), scales=c)
+    if name == "c3":
+        rng = np.random.Generator(np.random.PCG64(3))
+        n, d, m = s.get("n", 2048), s.get("d", 14336), s.get("m", 4096)
+        A, c = gated_activations(rng, n, d, "bf16")
+        B = gaussian_weights(rng, d, m, "bf16")
+        return Case("c3", "bf16", A, B, (0.5, 0.7, 0.8, 1.0), scales=c)
+    if name == "c4":
+        rng = np.random.Generator(np.random.PCG64(4))
+        hq, hkv = s.get("heads", 32), s.get("kv_heads", 8)
+        L, dh = s.get("L", 4096), s.get("dh", 128)
+        cq = np.exp(rng.standard_normal((hq, dh)))
+        ck = np.exp(rng.standard_normal((hkv, dh)))
+        Q = np.empty((hq, L, dh), dtype=np.float32)
+        K = np.empty((hkv, L, dh), dtype=np.float32)
+        for h in range(hq):
+            Q[h], _ = lognormal_outlier_activations(rng, L, dh, "bf16", 0, scales=cq[h])
+        for g in range(hkv):
+            K[g], _ = lognormal_outlier_activations(rng, L, dh, "bf16", 0, scales=ck[g])
+        return Case("c4", "bf16", Q, K, (0.5, 1.0), alpha=1.0 / math.sqrt(dh),
+                    transB=True, group=hq // hkv, scales=cq)
+    if name == "c5":
+        rng = np.random.Generator(np.random.PCG64(5))
+        n, d, m = s.get("n", 4096), s.get("d", 8192), s.get("m", 28672)
+        A, c = lognormal_outlier_activations(rng, n, d, "bf16", n_outliers=min(4, d))
+        B = gaussian_weights(rng, d, m, "bf16")
+        return Case("c5", "bf16", A, B, (0.8, 1.0), scales=c)
+    raise KeyError(name)
+
+
+def make_decode_case(case: Case, seed: int = 55) -> Case:
+    """n = 1 decode row for a linear case: a fresh N(0,1) row times the same c_j."""
+    if case.scales is None or case.A.ndim != 2:
+        raise ValueError("decode rows need a linear case with column scales")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d = case.A.shape[1]
+    a = _store(rng.standard_normal((1, d)) * case.scales[None, :], case.dtype)
+    return Case(case.name + "_decode", case.dtype, a, case.B, case.rhos, scales=case.scales)
+
+
+def sha256_of(*arrays: np.ndarray) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
