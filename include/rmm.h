@@ -1,0 +1,195 @@
+/*
+ * rmm.h -- C ABI of the MI355X (gfx950) Reduced Matrix Multiplication library.
+ *
+ * Reduced Matrix Multiplication (RMM), as defined in "Reduced Matrix
+ * Multiplication: Input-Adaptive Matrix-Product Reduction for LLM Inference"
+ * (arXiv 2608.13426), Sec. 3.2: for Y = A B with activations A (n x d) and a
+ * weight or intermediate B (d x m), score every contraction index by the
+ * column norm s_j = ||A[:, j]||_2, keep the index set I of the ceil(rho d)
+ * largest scores (rho in (0, 1] is the retention ratio) and compute only
+ * A[:, I] B[I, :].  Sec. 3.3 applies the same rule per attention head to
+ * Q K^T (select on Q's columns, gather the same dimensions of the shared GQA
+ * K head, scale by 1/sqrt(d_h) with the full d_h) and to linear/MLP
+ * projections.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named A, B, Y, s, idx, workspace are DEVICE pointers on the
+ *    current HIP device; descriptors are HOST pointers read during the call.
+ *    The caller owns every buffer; the library keeps no pointer after return.
+ *  - Matrices are row-major with leading dimensions in elements.
+ *  - bf16 is IEEE binary32 truncated to its upper 16 bits (stored as 2-byte
+ *    words); bf16 results are rounded to nearest-even from fp32 accumulators.
+ *  - All arguments are checked on the host before anything is enqueued; on
+ *    any error nothing is launched and no output is written.
+ *  - Work is enqueued on `stream` (0 = the null stream); the calls never
+ *    synchronize the host.  Device faults surface at the caller's next sync.
+ *  - Selection is deterministic: the same inputs give bit-identical indices,
+ *    norms and outputs on every call (no atomics in any reduction).
+ *  - Index sets are int32, listed in ascending order.  Among equal scores the
+ *    lower index is kept.  Scores are ranked as fp32 values with -0 treated as
+ *    +0 and NaN above +Inf (finite inputs are the supported case).
+ *  - Outputs must not overlap inputs.  Calls that share a workspace must be
+ *    ordered (same stream); concurrent calls need separate workspaces.
+ */
+#ifndef RMM_H
+#define RMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMM_OK = 0,
+    RMM_ERR_INVALID_ARG = 1, /* a size, pointer, stride or rho is invalid */
+    RMM_ERR_UNSUPPORTED = 2, /* valid request this build cannot run */
+    RMM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    RMM_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} rmm_status_t;
+
+typedef enum {
+    RMM_F32 = 0,  /* fp32 inputs, fp32 FMA accumulation, fp32 output */
+    RMM_BF16 = 1  /* bf16 inputs, fp32 accumulation (MFMA), bf16 output */
+} rmm_dtype_t;
+
+/* Run the whole path (norms, selection, gather) even when rho = 1.  Without
+ * it rho = 1 takes the shortcut I = [0, d) of Sec. 3.2 (every index kept),
+ * which gives the same result. */
+#define RMM_FLAG_FULL_PATH 0x1
+
+/*
+ * |I| = ceil(rho d)  (Sec. 3.2).  rho*d within 1e-9 relative of an integer is
+ * taken as that integer (so 0.07 * 100 gives 7, not 8).  Returns 0 when rho
+ * is NaN or outside (0, 1], or d < 1; otherwise a value in [1, d].
+ */
+int64_t rmm_k(double rho, int64_t d);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *rmm_status_string(rmm_status_t status);
+
+/* Name of the last HIP error this thread saw inside the library ("no error"
+ * when none): the detail behind RMM_ERR_HIP. */
+const char *rmm_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t rmm_version(void);
+
+/*
+ * Column norms s_j = ||A[:, j]||_2 for j < d  (Sec. 3.2 importance score).
+ *   A        device, n x d row-major, leading dimension lda >= d, dtype dt
+ *   s_out    device, d floats; fp32 sums of squares in a fixed order, then a
+ *            correctly rounded sqrt
+ *   workspace device scratch of at least rmm_colnorm_workspace_size(dt,n,d)
+ *            bytes (may be NULL when that size is 0); contents on entry do
+ *            not matter
+ * Errors: RMM_ERR_INVALID_ARG for n < 1, d < 1, lda < d, NULL A or s_out, or
+ * an unknown dtype; RMM_ERR_WORKSPACE for a short workspace.
+ */
+size_t rmm_colnorm_workspace_size(rmm_dtype_t dt, int64_t n, int64_t d);
+rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
+                         float *s_out, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * I = TopK(s, k)  (Sec. 3.2) for `batch` independent score vectors.
+ *   s        device, batch x d floats (row b at s + b*d)
+ *   idx_out  device, batch x k int32 (row b at idx_out + b*k), ascending
+ * Exact: an LDS radix select finds the k-th largest score, then an
+ * ascending-index compaction keeps every larger score and the lowest-indexed
+ * scores equal to it.
+ * Errors: RMM_ERR_INVALID_ARG for batch < 1, d < 1, d > 2^31-1, k < 1,
+ * k > d, or NULL pointers.
+ */
+rmm_status_t rmm_select(const float *s, int64_t batch, int64_t d, int64_t k, int32_t *idx_out,
+                        hipStream_t stream);
+
+/*
+ * Problem descriptor for rmm_matmul (host memory).
+ *   dtype        RMM_BF16 or RMM_F32 (A, B and Y share it)
+ *   n, d, m      A is n x d, B is d x m, Y is n x m; d is the contraction axis
+ *   lda          >= d
+ *   ldb          >= m when transB = 0; >= d when transB = 1
+ *   ldy          >= m
+ *   transB       0: B is stored d x m row-major (weights as in Y = A B);
+ *                1: B is stored as B^T, m x d row-major (keys K for
+ *                   S = Q K^T, or nn.Linear weights)
+ *   batch        >= 1 independent products; entry b uses
+ *                A + b*strideA, B + (b / b_group)*strideB, Y + b*strideY
+ *                (strides in elements; b_group > 1 shares one B among
+ *                b_group consecutive entries: grouped-query attention)
+ *   alpha        Y = alpha * A[:, I] B[I, :] (1/sqrt(d_h) for scores, Sec. 3.3)
+ *   flags        RMM_FLAG_* bits
+ */
+typedef struct {
+    rmm_dtype_t dtype;
+    int32_t transB;
+    int64_t n, d, m;
+    int64_t lda, ldb, ldy;
+    int64_t batch;
+    int64_t strideA, strideB, strideY;
+    int64_t b_group;
+    float alpha;
+    int32_t flags;
+} rmm_desc_t;
+
+/* Fill a descriptor for one product with dense leading dimensions. */
+void rmm_desc_init(rmm_desc_t *desc, rmm_dtype_t dtype, int64_t n, int64_t d, int64_t m);
+
+/*
+ * Bytes of device workspace rmm_matmul needs for (desc, rho); 0 means none.
+ * Returns SIZE_MAX when the descriptor or rho is invalid.
+ */
+size_t rmm_workspace_size(const rmm_desc_t *desc, double rho);
+
+/*
+ * The whole reduced product  (Sec. 3.2, 3.3):
+ *   1. s_j = ||A_b[:, j]||_2 for every batch entry b,
+ *   2. I_b = TopK(s, k) with k = rmm_k(rho, d),
+ *   3. gather A_b[:, I_b] and B_g[I_b, :] (g = b / b_group),
+ *   4. Y_b = alpha * A_b[:, I_b] B_g[I_b, :].
+ *   A, B, Y   device pointers laid out as the descriptor says
+ *   idx_out   device, batch x k int32 (row b at idx_out + b*k), or NULL
+ *   workspace device scratch of rmm_workspace_size(desc, rho) bytes; any
+ *             contents on entry
+ * Precision: bf16 inputs are contracted on bf16 MFMA with fp32 accumulation
+ * (decode, n = 1: fp32 FMA); fp32 inputs with fp32 FMA.  Each output sums
+ * its k terms in a fixed order, so repeated calls are bit-identical.
+ * Errors: RMM_ERR_INVALID_ARG for an invalid descriptor, rho, or NULL
+ * A, B, Y; RMM_ERR_WORKSPACE when ws_bytes is too small; RMM_ERR_HIP when a
+ * launch fails (outputs may then be partly written).
+ */
+rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,
+                        int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Optional per-kernel timing for measurement tools.  While enabled, every
+ * kernel rmm_matmul enqueues is bracketed by a pair of HIP events recorded
+ * on the call's stream (at most `capacity` pairs are kept; later kernels are
+ * not timed).  rmm_timing_collect synchronizes those events and returns, for
+ * each kernel kind k (RMM_KERNEL_*), the summed milliseconds in ms[k] and
+ * the launch count in count[k] (arrays of RMM_KERNEL_KINDS entries), then
+ * clears the record.  Not thread-safe; meant for a single benchmarking
+ * thread.  Enabling allocates the events (host call, outside any capture).
+ */
+enum {
+    RMM_KERNEL_COLNORM = 0,
+    RMM_KERNEL_FINALIZE = 1,
+    RMM_KERNEL_SELECT = 2,
+    RMM_KERNEL_PACK = 3,
+    RMM_KERNEL_GEMM = 4,
+    RMM_KERNEL_REDUCE = 5,
+    RMM_KERNEL_GEMV = 6,
+    RMM_KERNEL_OTHER = 7,
+    RMM_KERNEL_KINDS = 8
+};
+rmm_status_t rmm_timing_enable(int32_t enable, int32_t capacity);
+rmm_status_t rmm_timing_collect(double *ms, int64_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMM_H */

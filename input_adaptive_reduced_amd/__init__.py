@@ -1,0 +1,297 @@
+"""Reduced Matrix Multiplication (RMM) on MI355X (gfx950).
+
+A thin ctypes binding over ``librmm.so`` (C ABI in ``include/rmm.h``).  Every
+step of the path -- column norms, TopK selection, gather and the reduced
+product -- runs in the library's HIP kernels; this module only marshals
+arguments: it reads shapes and strides from torch tensors, allocates outputs
+and scratch through torch's caching allocator, and passes device pointers and
+the current HIP stream.  There is no CPU fallback: without the built library
+every call raises.
+
+The method is the one of "Reduced Matrix Multiplication: Input-Adaptive
+Matrix-Product Reduction for LLM Inference" (Sec. 3.2): for Y = A B keep the
+ceil(rho d) contraction indices with the largest column norms of A and
+compute A[:, I] B[I, :].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
+    "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librmm.so")
+
+F32, BF16 = 0, 1
+FLAG_FULL_PATH = 0x1
+KERNEL_KINDS = ("colnorm", "finalize", "select", "pack", "gemm", "reduce", "gemv", "other")
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
+
+
+class RMMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = ""
+        if status == 4 and _lib is not None:
+            detail = ": " + _lib.rmm_last_hip_error().decode()
+        super().__init__(f"{where}: {status_string(status)} (status {status}){detail}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    """Mirror of rmm_desc_t (include/rmm.h)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("transB", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("d", ctypes.c_int64), ("m", ctypes.c_int64),
+        ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldy", ctypes.c_int64),
+        ("batch", ctypes.c_int64),
+        ("strideA", ctypes.c_int64), ("strideB", ctypes.c_int64), ("strideY", ctypes.c_int64),
+        ("b_group", ctypes.c_int64),
+        ("alpha", ctypes.c_float), ("flags", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _hip_runtimes():
+    """Distinct HIP runtime libraries mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:  # pragma: no cover
+        return []
+
+
+def load():
+    """Load librmm.so (raises if it has not been built).
+
+    torch is imported first: it ships its own HIP runtime, and librmm must
+    bind to that same runtime (same soname) so that torch's streams and
+    allocations are valid in the library.  Loading librmm first would map a
+    second runtime from /opt/rocm next to torch's; that state is refused.
+    """
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with input_adaptive_reduced_amd/build.py")
+    try:
+        import torch  # noqa: F401  (binds the process to torch's HIP runtime)
+    except ImportError:
+        pass
+    L = ctypes.CDLL(_LIB_PATH)
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise RuntimeError("two HIP runtimes are loaded (%s); import torch before anything loads "
+                           "librmm.so" % ", ".join(rts))
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.rmm_k.argtypes, L.rmm_k.restype = [ctypes.c_double, i64], i64
+    L.rmm_status_string.argtypes, L.rmm_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.rmm_version.argtypes, L.rmm_version.restype = [], i32
+    L.rmm_last_hip_error.argtypes, L.rmm_last_hip_error.restype = [], ctypes.c_char_p
+    L.rmm_colnorm_workspace_size.argtypes, L.rmm_colnorm_workspace_size.restype = [ctypes.c_int, i64, i64], sz
+    L.rmm_colnorm.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, sz, vp]
+    L.rmm_colnorm.restype = ctypes.c_int
+    L.rmm_select.argtypes, L.rmm_select.restype = [vp, i64, i64, i64, vp, vp], ctypes.c_int
+    L.rmm_desc_init.argtypes, L.rmm_desc_init.restype = [ctypes.POINTER(Desc), ctypes.c_int, i64, i64, i64], None
+    L.rmm_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_double]
+    L.rmm_workspace_size.restype = sz
+    L.rmm_matmul.argtypes = [ctypes.POINTER(Desc), vp, vp, ctypes.c_double, vp, vp, vp, sz, vp]
+    L.rmm_matmul.restype = ctypes.c_int
+    L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
+    L.rmm_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.rmm_timing_collect.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().rmm_status_string(int(status)).decode()
+    except ImportError:
+        return _STATUS.get(int(status), "unknown")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RMMError(status, where)
+
+
+def version() -> int:
+    return int(load().rmm_version())
+
+
+def k_of(rho: float, d: int) -> int:
+    """|I| = ceil(rho d) as the library computes it (0 = invalid)."""
+    return int(load().rmm_k(float(rho), int(d)))
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _stream(t) -> ctypes.c_void_p:
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device), int(nbytes)
+
+
+def colnorm(A) -> "torch.Tensor":
+    """s_j = ||A[:, j]||_2 (fp32) of a 2-D bf16/fp32 tensor with unit column stride."""
+    torch = _torch()
+    _require_gpu(A)
+    if A.dim() != 2 or A.stride(1) != 1:
+        raise ValueError("A must be 2-D with unit column stride")
+    n, d = A.shape
+    L = load()
+    dt = _dtype_code(A)
+    s = torch.empty(d, dtype=torch.float32, device=A.device)
+    ws, wsb = _workspace(L.rmm_colnorm_workspace_size(dt, n, d), A.device)
+    _check(L.rmm_colnorm(A.data_ptr(), dt, n, d, A.stride(0), s.data_ptr(),
+                         None if ws is None else ws.data_ptr(), wsb, _stream(A)), "rmm_colnorm")
+    return s
+
+
+def select(s, k: int) -> "torch.Tensor":
+    """Indices of the k largest scores (ties -> lower index), ascending int32.
+
+    ``s`` is (d,) or (batch, d) fp32, contiguous.
+    """
+    torch = _torch()
+    _require_gpu(s)
+    if s.dtype != torch.float32 or not s.is_contiguous() or s.dim() not in (1, 2):
+        raise ValueError("s must be a contiguous fp32 tensor of shape (d,) or (batch, d)")
+    batch, d = (1, s.shape[0]) if s.dim() == 1 else s.shape
+    out = torch.empty((batch, int(k)), dtype=torch.int32, device=s.device)
+    _check(load().rmm_select(s.data_ptr(), batch, d, int(k), out.data_ptr(), _stream(s)), "rmm_select")
+    return out[0] if s.dim() == 1 else out
+
+
+def _desc_for(A, B, transB: bool, b_group: int, alpha: float, full_path: bool, Y=None) -> Tuple[Desc, tuple]:
+    if A.dim() not in (2, 3) or B.dim() != A.dim():
+        raise ValueError("A and B must both be 2-D, or both 3-D (batched)")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    if A.stride(-1) != 1 or B.stride(-1) != 1:
+        raise ValueError("A and B need unit stride along their last dimension")
+    batched = A.dim() == 3
+    batch = A.shape[0] if batched else 1
+    n, d = A.shape[-2], A.shape[-1]
+    if transB:
+        m, d2 = B.shape[-2], B.shape[-1]
+    else:
+        d2, m = B.shape[-2], B.shape[-1]
+    if d != d2:
+        raise ValueError(f"contraction sizes differ: {d} vs {d2}")
+    nb = B.shape[0] if batched else 1
+    if batched and batch != nb * b_group:
+        raise ValueError(f"batch {batch} must equal B batch {nb} x b_group {b_group}")
+    ds = Desc()
+    ds.dtype = _dtype_code(A)
+    ds.transB = 1 if transB else 0
+    ds.n, ds.d, ds.m = n, d, m
+    ds.lda, ds.ldb = A.stride(-2), B.stride(-2)
+    ds.ldy = m if Y is None else Y.stride(-2)
+    ds.batch = batch
+    ds.strideA = A.stride(0) if batched else 0
+    ds.strideB = B.stride(0) if batched else 0
+    ds.strideY = (n * ds.ldy if Y is None else Y.stride(0)) if batched else 0
+    ds.b_group = b_group if batched else 1
+    ds.alpha = float(alpha)
+    ds.flags = FLAG_FULL_PATH if full_path else 0
+    shape = (batch, n, m) if batched else (n, m)
+    return ds, shape
+
+
+def workspace_size(A, B, rho: float, transB: bool = False, b_group: int = 1, full_path: bool = False) -> int:
+    ds, _ = _desc_for(A, B, transB, b_group, 1.0, full_path)
+    w = load().rmm_workspace_size(ctypes.byref(ds), float(rho))
+    if w == ctypes.c_size_t(-1).value:
+        raise RMMError(1, "rmm_workspace_size")
+    return int(w)
+
+
+def matmul(A, B, rho: float, *, transB: bool = False, b_group: int = 1, alpha: float = 1.0,
+           out=None, idx_out=None, return_idx: bool = True, full_path: bool = False, workspace=None):
+    """Y = alpha * A[:, I] B[I, :] with I = TopK(||A[:, j]||_2, ceil(rho d)).
+
+    A: (n, d) or (batch, n, d).  B: (d, m), or (m, d) with ``transB``; batched
+    B has batch / b_group entries, entry b of A pairs with B[b // b_group]
+    (grouped-query attention).  Returns (Y, idx) with idx of shape (k,) or
+    (batch, k), int32 ascending (None when ``return_idx`` is false and no
+    ``idx_out`` was given).
+    """
+    torch = _torch()
+    _require_gpu(A, B)
+    L = load()
+    ds, shape = _desc_for(A, B, transB, b_group, alpha, full_path, out)
+    k = int(L.rmm_k(float(rho), ds.d))
+    if k < 1:
+        raise RMMError(1, f"rho={rho!r}")
+    if out is None:
+        out = torch.empty(shape, dtype=A.dtype, device=A.device)
+    elif tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if idx_out is None and return_idx:
+        idx_out = torch.empty((ds.batch, k) if A.dim() == 3 else (k,), dtype=torch.int32, device=A.device)
+    if idx_out is not None and (idx_out.dtype != torch.int32 or not idx_out.is_contiguous()
+                                or idx_out.numel() != ds.batch * k):
+        raise ValueError("idx_out must be a contiguous int32 tensor with batch*k elements")
+    need = L.rmm_workspace_size(ctypes.byref(ds), float(rho))
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(1, "rmm_workspace_size")
+    if workspace is None:
+        ws, wsb = _workspace(need, A.device)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.rmm_matmul(ctypes.byref(ds), A.data_ptr(), B.data_ptr(), float(rho), out.data_ptr(),
+                      None if idx_out is None else idx_out.data_ptr(),
+                      None if ws is None else ws.data_ptr(), wsb, _stream(A))
+    _check(st, "rmm_matmul")
+    return out, idx_out
+
+
+def timing_enable(enable: bool = True, capacity: int = 4096):
+    _check(load().rmm_timing_enable(1 if enable else 0, int(capacity)), "rmm_timing_enable")
+
+
+def timing_collect() -> dict:
+    """Per kernel kind: (total milliseconds, launches) since the last collect."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(load().rmm_timing_collect(ms, cnt), "rmm_timing_collect")
+    return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n)}

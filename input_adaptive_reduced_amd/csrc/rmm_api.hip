@@ -1,0 +1,459 @@
+// C ABI of librmm: argument checks, planning, workspace layout and launch
+// order for reduced matrix multiplication on gfx950 (see include/rmm.h).
+//
+// The path follows "Reduced Matrix Multiplication: Input-Adaptive
+// Matrix-Product Reduction for LLM Inference", Sec. 3.2 and 3.3, in the
+// paper's order: column norms -> TopK -> gather -> reduced product.
+//
+// Routes (chosen on the host from shapes and alignment, never from data):
+//   MFMA    bf16, 16-byte aligned operands, leading dims and m multiples of 8:
+//           colnorm_partial -> colnorm_finalize -> select -> pack A (and B^T
+//           when transB) -> MFMA GEMM (-> split-K reduce when K is split).
+//   DECODE  bf16, n = 1, B stored d x m, aligned: select on |a| (writes the
+//           kept values) -> gathered GEMV partials -> ordered reduce.
+//   GENERIC everything else (fp32, odd shapes, unaligned): the same norm and
+//           select kernels, then a SIMT gathered GEMM with fp32 FMA.
+// rho = 1 without RMM_FLAG_FULL_PATH keeps every index (I = [0, d)): the norm
+// and select steps are skipped, idx_out receives 0..d-1, and A is used in
+// place when its rows are already MFMA-ready.
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "rmm_internal.h"
+
+namespace rmm {
+
+// ---------------------------------------------------------------- timing hooks
+namespace {
+struct TimingState {
+    bool enabled = false;
+    int capacity = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> kind;
+    int open_kind = -1;
+};
+TimingState g_timing;
+}  // namespace
+
+void timing_begin(hipStream_t s, int kind) {
+    if (!g_timing.enabled || g_timing.used >= g_timing.capacity) {
+        g_timing.open_kind = -1;
+        return;
+    }
+    if (hipEventRecord(g_timing.ev[2 * g_timing.used], s) != hipSuccess) {
+        g_timing.open_kind = -1;
+        return;
+    }
+    g_timing.open_kind = kind;
+}
+
+void timing_end(hipStream_t s, int kind) {
+    if (g_timing.open_kind != kind) return;
+    if (hipEventRecord(g_timing.ev[2 * g_timing.used + 1], s) == hipSuccess) {
+        g_timing.kind[g_timing.used] = kind;
+        ++g_timing.used;
+    }
+    g_timing.open_kind = -1;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t &out) {
+    if (a < 0 || b < 0) return false;
+    return !__builtin_mul_overflow(a, b, &out);
+}
+
+// Highest element offset touched by a strided batch of row-major matrices, +1.
+bool extent(int64_t rows, int64_t cols, int64_t ld, int64_t batch, int64_t stride, int64_t &out) {
+    int64_t a, c;
+    if (!mul_ok(rows - 1, ld, a)) return false;
+    if (!mul_ok(batch - 1, stride, c)) return false;
+    if (__builtin_add_overflow(a, cols, &out)) return false;
+    if (__builtin_add_overflow(out, c, &out)) return false;
+    return true;
+}
+
+bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
+}
+
+enum Route { ROUTE_GENERIC = 0, ROUTE_MFMA = 1, ROUTE_DECODE = 2 };
+
+struct Plan {
+    Route route;
+    int64_t k, kpad;
+    bool shortcut;   // rho = 1 fast path: no norms or selection
+    bool directA;    // MFMA reads A in place (no pack)
+    ColnormPlan cp;
+    GemmConfig gc;
+    int gsplits;
+    size_t off_part, off_s, off_idx, off_Ap, off_Bp, off_gpart, off_aval, total;
+};
+
+// Host-side rho -> k (Sec. 3.2); see rmm_k in rmm.h for the rounding rule.
+int64_t k_of(double rho, int64_t d) {
+    if (!(rho > 0.0) || !(rho <= 1.0) || d < 1) return 0;
+    const double p = rho * (double)d;
+    const double r = nearbyint(p);
+    const double tol = 1e-9 * (p > 1.0 ? p : 1.0);
+    double kk = fabs(p - r) <= tol ? r : ceil(p);
+    if (kk < 1.0) kk = 1.0;
+    if (kk > (double)d) kk = (double)d;
+    return (int64_t)kk;
+}
+
+// Validates the descriptor; fills element extents of A, B, Y.
+rmm_status_t check_desc(const rmm_desc_t *ds, int64_t &extA, int64_t &extB, int64_t &extY) {
+    if (!ds) return RMM_ERR_INVALID_ARG;
+    if (ds->dtype != RMM_F32 && ds->dtype != RMM_BF16) return RMM_ERR_INVALID_ARG;
+    if (ds->transB != 0 && ds->transB != 1) return RMM_ERR_INVALID_ARG;
+    if (ds->n < 1 || ds->d < 1 || ds->m < 1 || ds->batch < 1 || ds->b_group < 1) return RMM_ERR_INVALID_ARG;
+    if (ds->d > INT32_MAX) return RMM_ERR_INVALID_ARG;
+    if (ds->batch > 65535 || ds->n > INT32_MAX / 2 || ds->m > INT32_MAX / 2) return RMM_ERR_INVALID_ARG;
+    if (ds->lda < ds->d || ds->ldy < ds->m) return RMM_ERR_INVALID_ARG;
+    if (ds->ldb < (ds->transB ? ds->d : ds->m)) return RMM_ERR_INVALID_ARG;
+    if (ds->strideA < 0 || ds->strideB < 0 || ds->strideY < 0) return RMM_ERR_INVALID_ARG;
+    if (!isfinite(ds->alpha)) return RMM_ERR_INVALID_ARG;
+    if ((ds->flags & ~RMM_FLAG_FULL_PATH) != 0) return RMM_ERR_INVALID_ARG;
+    const int64_t nb = (ds->batch + ds->b_group - 1) / ds->b_group;
+    if (!extent(ds->n, ds->d, ds->lda, ds->batch, ds->strideA, extA)) return RMM_ERR_INVALID_ARG;
+    if (!extent(ds->transB ? ds->m : ds->d, ds->transB ? ds->d : ds->m, ds->ldb, nb, ds->strideB, extB))
+        return RMM_ERR_INVALID_ARG;
+    if (!extent(ds->n, ds->m, ds->ldy, ds->batch, ds->strideY, extY)) return RMM_ERR_INVALID_ARG;
+    // batch entries must not write overlapping outputs
+    if (ds->batch > 1) {
+        int64_t one;
+        if (!extent(ds->n, ds->m, ds->ldy, 1, 0, one)) return RMM_ERR_INVALID_ARG;
+        if (ds->strideY < one) return RMM_ERR_INVALID_ARG;
+    }
+    return RMM_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Alignment-based part of the route choice; pointers may be null when only
+// sizing (then alignment is assumed, which can only over-size).
+Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, const void *Y) {
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    p.k = k;
+    p.kpad = (k + 63) / 64 * 64;
+    p.shortcut = (k == ds->d) && !(ds->flags & RMM_FLAG_FULL_PATH);
+    const bool bf = ds->dtype == RMM_BF16;
+    const bool ptr_ok = (!A || aligned16(A)) && (!B || aligned16(B)) && (!Y || aligned16(Y));
+    const bool ld_ok = ds->lda % 8 == 0 && ds->ldb % 8 == 0 && ds->ldy % 8 == 0 && ds->m % 8 == 0 &&
+                       (ds->batch == 1 || (ds->strideA % 8 == 0 && ds->strideB % 8 == 0 && ds->strideY % 8 == 0));
+    if (bf && ptr_ok && ld_ok && ds->n == 1 && !ds->transB && ds->batch == 1) {
+        p.route = ROUTE_DECODE;
+        p.shortcut = false;  // the fused |a| selection also produces the kept values
+    } else if (bf && ptr_ok && ld_ok) {
+        p.route = ROUTE_MFMA;
+    } else {
+        p.route = ROUTE_GENERIC;
+    }
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const int64_t batch = ds->batch, d = ds->d, n = ds->n, m = ds->m;
+    const bool norms = !p.shortcut && p.route != ROUTE_DECODE;
+    if (norms) {
+        p.cp = colnorm_plan(ds->dtype, n, d, batch);
+        p.off_part = take((size_t)p.cp.chunks * d * batch * 4);
+        p.off_s = take((size_t)d * batch * 4);
+    }
+    p.off_idx = take((size_t)k * batch * 4);
+    if (p.route == ROUTE_MFMA) {
+        p.directA = p.shortcut && d % 64 == 0;
+        if (!p.directA) p.off_Ap = take((size_t)batch * n * p.kpad * 2);
+        if (ds->transB) p.off_Bp = take((size_t)batch * m * p.kpad * 2);
+        p.gc = gemm_choose(n, m, k, batch);
+        if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * batch * n * m * 4);
+    } else if (p.route == ROUTE_DECODE) {
+        p.gsplits = gemv_splits(m, k);
+        p.off_aval = take((size_t)k * 4);
+        p.off_gpart = take((size_t)p.gsplits * m * 4);
+    }
+    p.total = off;
+    return p;
+}
+
+thread_local hipError_t g_last_error = hipSuccess;
+
+#define RMM_LAUNCH(kind, call)              \
+    do {                                    \
+        timing_begin(stream, kind);         \
+        hipError_t e_ = (call);             \
+        timing_end(stream, kind);           \
+        if (e_ != hipSuccess) {             \
+            g_last_error = e_;              \
+            return RMM_ERR_HIP;             \
+        }                                   \
+    } while (0)
+
+}  // namespace
+}  // namespace rmm
+
+using namespace rmm;
+
+extern "C" {
+
+int64_t rmm_k(double rho, int64_t d) { return k_of(rho, d); }
+
+int32_t rmm_version(void) { return 100; }
+
+const char *rmm_last_hip_error(void) { return hipGetErrorString(g_last_error); }
+
+const char *rmm_status_string(rmm_status_t s) {
+    switch (s) {
+        case RMM_OK: return "ok";
+        case RMM_ERR_INVALID_ARG: return "invalid argument";
+        case RMM_ERR_UNSUPPORTED: return "unsupported";
+        case RMM_ERR_WORKSPACE: return "workspace missing or too small";
+        case RMM_ERR_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+void rmm_desc_init(rmm_desc_t *ds, rmm_dtype_t dtype, int64_t n, int64_t d, int64_t m) {
+    if (!ds) return;
+    memset(ds, 0, sizeof(*ds));
+    ds->dtype = dtype;
+    ds->n = n;
+    ds->d = d;
+    ds->m = m;
+    ds->lda = d;
+    ds->ldb = m;
+    ds->ldy = m;
+    ds->batch = 1;
+    ds->b_group = 1;
+    ds->alpha = 1.0f;
+}
+
+size_t rmm_colnorm_workspace_size(rmm_dtype_t dt, int64_t n, int64_t d) {
+    if ((dt != RMM_F32 && dt != RMM_BF16) || n < 1 || d < 1) return SIZE_MAX;
+    ColnormPlan p = colnorm_plan(dt, n, d, 1);
+    return (size_t)p.chunks * (size_t)d * 4;
+}
+
+rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda, float *s_out,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!A || !s_out || (dt != RMM_F32 && dt != RMM_BF16) || n < 1 || d < 1 || lda < d) return RMM_ERR_INVALID_ARG;
+    int64_t ext;
+    if (!extent(n, d, lda, 1, 0, ext) || n > INT32_MAX / 2) return RMM_ERR_INVALID_ARG;
+    ColnormPlan p = colnorm_plan(dt, n, d, 1);
+    const size_t need = (size_t)p.chunks * (size_t)d * 4;
+    if (ws_bytes < need || !workspace) return RMM_ERR_WORKSPACE;
+    float *part = static_cast<float *>(workspace);
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(A, dt, n, d, lda, 1, 0, p, part, stream));
+    RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.chunks, d, 1, s_out, stream));
+    return RMM_OK;
+}
+
+rmm_status_t rmm_select(const float *s, int64_t batch, int64_t d, int64_t k, int32_t *idx_out, hipStream_t stream) {
+    if (!s || !idx_out || batch < 1 || batch > 65535 || d < 1 || d > INT32_MAX || k < 1 || k > d)
+        return RMM_ERR_INVALID_ARG;
+    RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, nullptr, stream));
+    return RMM_OK;
+}
+
+size_t rmm_workspace_size(const rmm_desc_t *desc, double rho) {
+    int64_t ea, eb, ey;
+    if (check_desc(desc, ea, eb, ey) != RMM_OK) return SIZE_MAX;
+    const int64_t k = k_of(rho, desc->d);
+    if (k < 1) return SIZE_MAX;
+    return make_plan(desc, k, nullptr, nullptr, nullptr).total;
+}
+
+rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,
+                        int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    int64_t extA, extB, extY;
+    rmm_status_t st = check_desc(desc, extA, extB, extY);
+    if (st != RMM_OK) return st;
+    if (!A || !B || !Y) return RMM_ERR_INVALID_ARG;
+    const int64_t k = k_of(rho, desc->d);
+    if (k < 1) return RMM_ERR_INVALID_ARG;
+    const rmm_desc_t &ds = *desc;
+    const int64_t esz = ds.dtype == RMM_BF16 ? 2 : 4;
+    if (overlaps(Y, extY * esz, A, extA * esz) || overlaps(Y, extY * esz, B, extB * esz)) return RMM_ERR_INVALID_ARG;
+    if (idx_out && (overlaps(idx_out, k * ds.batch * 4, Y, extY * esz) ||
+                    overlaps(idx_out, k * ds.batch * 4, A, extA * esz) ||
+                    overlaps(idx_out, k * ds.batch * 4, B, extB * esz)))
+        return RMM_ERR_INVALID_ARG;
+
+    const Plan p = make_plan(desc, k, A, B, Y);
+    if (p.total > 0 && (!workspace || ws_bytes < p.total)) return RMM_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    if (p.total > 0 && (overlaps(ws, (int64_t)p.total, Y, extY * esz) || overlaps(ws, (int64_t)p.total, A, extA * esz) ||
+                        overlaps(ws, (int64_t)p.total, B, extB * esz)))
+        return RMM_ERR_INVALID_ARG;
+
+    const int64_t n = ds.n, d = ds.d, m = ds.m, batch = ds.batch;
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(ws + p.off_idx);
+
+    if (p.route == ROUTE_DECODE) {
+        float *aval = reinterpret_cast<float *>(ws + p.off_aval);
+        float *gpart = reinterpret_cast<float *>(ws + p.off_gpart);
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(nullptr, A, RMM_BF16, 0, 1, d, k, idx, k, aval, stream));
+        RMM_LAUNCH(RMM_KERNEL_GEMV, launch_gemv_partial(static_cast<const uint16_t *>(B), ds.ldb, m, idx, aval, k,
+                                                        p.gsplits, gpart, stream));
+        RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(gpart, p.gsplits, 1, m, 1, ds.alpha,
+                                                           static_cast<uint16_t *>(Y), ds.ldy, 0, stream));
+        return RMM_OK;
+    }
+
+    // steps 1-2: scores and selection (or every index at rho = 1)
+    const int32_t *gemm_idx = idx;
+    if (p.shortcut) {
+        if (idx_out) RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(idx_out, k, batch, stream));
+        gemm_idx = nullptr;  // identity
+    } else {
+        float *part = reinterpret_cast<float *>(ws + p.off_part);
+        float *s = reinterpret_cast<float *>(ws + p.off_s);
+        RMM_LAUNCH(RMM_KERNEL_COLNORM,
+                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx, k, nullptr, stream));
+    }
+
+    if (p.route == ROUTE_GENERIC) {
+        GenericArgs g;
+        g.dt = ds.dtype;
+        g.A = A;
+        g.lda = ds.lda;
+        g.strideA = ds.strideA;
+        g.B = B;
+        g.ldb = ds.ldb;
+        g.strideB = ds.strideB;
+        g.group = ds.b_group;
+        g.transB = ds.transB;
+        g.idx = gemm_idx;
+        g.ld_idx = k;
+        g.Y = Y;
+        g.ldy = ds.ldy;
+        g.strideY = ds.strideY;
+        g.n = n;
+        g.m = m;
+        g.k = k;
+        g.batch = batch;
+        g.alpha = ds.alpha;
+        RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_generic(g, stream));
+        return RMM_OK;
+    }
+
+    // ROUTE_MFMA: step 3 (gather) then step 4 (reduced product)
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    if (p.directA) {
+        g.A = static_cast<const uint16_t *>(A);
+        g.lda = ds.lda;
+        g.strideA = ds.strideA;
+    } else {
+        uint16_t *Ap = reinterpret_cast<uint16_t *>(ws + p.off_Ap);
+        if (p.shortcut) {
+            // identity gather: the pack needs an index list; reuse the workspace one
+            int32_t *iota = reinterpret_cast<int32_t *>(ws + p.off_idx);
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(iota, k, batch, stream));
+            gemm_idx = iota;
+        }
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(A, RMM_BF16, n, d, ds.lda, ds.strideA, 1, gemm_idx, k, k, p.kpad, Ap,
+                                                n * p.kpad, batch, stream));
+        g.A = Ap;
+        g.lda = p.kpad;
+        g.strideA = n * p.kpad;
+    }
+    if (ds.transB) {
+        uint16_t *Bp = reinterpret_cast<uint16_t *>(ws + p.off_Bp);
+        const int32_t *bidx = gemm_idx;
+        if (!bidx) {
+            int32_t *iota = reinterpret_cast<int32_t *>(ws + p.off_idx);
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(iota, k, batch, stream));
+            bidx = iota;
+        }
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(B, RMM_BF16, m, d, ds.ldb, ds.strideB, ds.b_group, bidx, k, k,
+                                                p.kpad, Bp, m * p.kpad, batch, stream));
+        g.B = Bp;
+        g.ldb = p.kpad;
+        g.strideB = m * p.kpad;
+        g.group = 1;
+        g.bmode = 1;
+        g.idx = nullptr;
+    } else {
+        g.B = static_cast<const uint16_t *>(B);
+        g.ldb = ds.ldb;
+        g.strideB = ds.strideB;
+        g.group = ds.b_group;
+        g.bmode = 0;
+        g.idx = gemm_idx;
+        g.ld_idx = k;
+    }
+    g.Y = static_cast<uint16_t *>(Y);
+    g.ldy = ds.ldy;
+    g.strideY = ds.strideY;
+    g.n = n;
+    g.m = m;
+    g.k = k;
+    g.kpad = p.directA ? d : p.kpad;
+    g.batch = batch;
+    g.alpha = ds.alpha;
+    g.splits = p.gc.splits;
+    g.part = p.gc.splits > 1 ? reinterpret_cast<float *>(ws + p.off_gpart) : nullptr;
+    RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
+    if (p.gc.splits > 1)
+        RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(g.part, p.gc.splits, n, m, batch, ds.alpha,
+                                                           static_cast<uint16_t *>(Y), ds.ldy, ds.strideY, stream));
+    return RMM_OK;
+}
+
+rmm_status_t rmm_timing_enable(int32_t enable, int32_t capacity) {
+    TimingState &t = g_timing;
+    if (!enable) {
+        t.enabled = false;
+        return RMM_OK;
+    }
+    if (capacity < 1 || capacity > (1 << 20)) return RMM_ERR_INVALID_ARG;
+    if ((int)t.ev.size() < 2 * capacity) {
+        for (size_t i = t.ev.size(); i < (size_t)2 * capacity; ++i) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return RMM_ERR_HIP;
+            t.ev.push_back(e);
+        }
+    }
+    t.kind.assign(capacity, 0);
+    t.capacity = capacity;
+    t.used = 0;
+    t.enabled = true;
+    return RMM_OK;
+}
+
+rmm_status_t rmm_timing_collect(double *ms, int64_t *count) {
+    if (!ms || !count) return RMM_ERR_INVALID_ARG;
+    for (int q = 0; q < RMM_KERNEL_KINDS; ++q) {
+        ms[q] = 0.0;
+        count[q] = 0;
+    }
+    TimingState &t = g_timing;
+    for (int i = 0; i < t.used; ++i) {
+        if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess) return RMM_ERR_HIP;
+        float e = 0.f;
+        if (hipEventElapsedTime(&e, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) return RMM_ERR_HIP;
+        ms[t.kind[i]] += e;
+        count[t.kind[i]] += 1;
+    }
+    t.used = 0;
+    return RMM_OK;
+}
+
+}  // extern "C"

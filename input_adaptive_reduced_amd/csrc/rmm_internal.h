@@ -1,0 +1,122 @@
+// Internal declarations shared by the HIP translation units of librmm.
+// Not installed; the public interface is include/rmm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmm.h"
+
+namespace rmm {
+
+// ---------------------------------------------------------------- bf16 helpers (device)
+// bf16 is carried as its raw 16-bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// Order-preserving map from an fp32 score to an unsigned key (larger score ->
+// larger key).  -0 is folded onto +0 and every NaN onto +qNaN, which ranks
+// above +Inf.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) u = 0x7fc00000u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- kernel kinds (timing)
+struct Timer;  // host-side per-launch event recorder (rmm_api.hip)
+void timing_begin(hipStream_t s, int kind);
+void timing_end(hipStream_t s, int kind);
+
+// ---------------------------------------------------------------- launchers (host)
+// All launchers enqueue on `stream` and return hipGetLastError().
+
+// Partial sums of squares per column: part[b][r][j] = sum over rows of chunk r.
+// Grid shape is chosen by colnorm_plan().
+struct ColnormPlan {
+    int tc;          // threads per row (columns / vec)
+    int strips;      // column strips
+    int chunks;      // row chunks R
+    int64_t rows_per_chunk;
+};
+ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch);
+hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
+                                  int64_t batch, int64_t strideA, const ColnormPlan &p, float *part,
+                                  hipStream_t stream);
+// s[b][j] = sqrt(sum_r part[b][r][j]) with r ascending.
+hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
+                                   hipStream_t stream);
+
+// Exact TopK by radix select; idx[b][0..k) ascending.  When `a_src` is given
+// the scores are |a_j| of a single bf16/f32 row per batch entry (decode) and
+// `aval` receives a[idx[t]] as fp32.  `idx_pad` > k extends each row of idx
+// with -1 up to idx_pad entries (for kernels that read whole chunks).
+hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, int64_t a_stride, int64_t batch,
+                         int64_t d, int64_t k, int32_t *idx, int64_t ld_idx, float *aval, hipStream_t stream);
+
+// dst[b][r][t] = src[b / group][r][idx[b][t]] for t < k, 0 for k <= t < kpad.
+hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src,
+                       int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t k,
+                       int64_t kpad, void *dst, int64_t dst_stride, int64_t batch, hipStream_t stream);
+
+// Iota index list 0..k-1 per batch entry (rho = 1 shortcut).
+hipError_t launch_iota(int32_t *idx, int64_t k, int64_t batch, hipStream_t stream);
+
+// bf16 MFMA GEMM  Y = alpha * Ap[:, 0:k] * Bsel  (see gemm.hip for operand modes).
+struct GemmArgs {
+    const uint16_t *A;   // packed/dense A, k-contiguous rows
+    int64_t lda, strideA;
+    const uint16_t *B;   // bmode 0: d x m row-major rows gathered by idx; bmode 1: m x k k-contiguous
+    int64_t ldb, strideB;
+    int64_t group;       // batch entries sharing one B (B + (b / group) * strideB)
+    const int32_t *idx;  // bmode 0: row list per entry (NULL = identity), ld_idx apart
+    int64_t ld_idx;
+    uint16_t *Y;
+    int64_t ldy, strideY;
+    float *part;         // split-K fp32 partials [split][batch][n][m] (NULL = no split)
+    int64_t n, m, k, kpad, batch;
+    int splits;
+    int bmode;
+    float alpha;
+};
+struct GemmConfig {
+    int tile;    // 0: 256x256, 1: 128x128, 2: 256x128
+    int splits;  // >= 1
+};
+GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch);
+hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream);
+// Y = alpha * sum_s part[s] (s ascending), rounded to bf16.
+hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,
+                                uint16_t *Y, int64_t ldy, int64_t strideY, hipStream_t stream);
+
+// Generic gathered GEMM for any dtype, alignment and shape (SIMT fp32 FMA).
+struct GenericArgs {
+    rmm_dtype_t dt;
+    const void *A;
+    int64_t lda, strideA;
+    const void *B;
+    int64_t ldb, strideB, group;
+    int transB;
+    const int32_t *idx;  // NULL = identity
+    int64_t ld_idx;
+    void *Y;
+    int64_t ldy, strideY;
+    int64_t n, m, k, batch;
+    float alpha;
+};
+hipError_t launch_gemm_generic(const GenericArgs &g, hipStream_t stream);
+
+// Decode: y = alpha * sum_t aval[t] * B[idx[t], :] (split over t, then reduce).
+int gemv_splits(int64_t m, int64_t k);
+hipError_t launch_gemv_partial(const uint16_t *B, int64_t ldb, int64_t m, const int32_t *idx, const float *aval,
+                               int64_t k, int splits, float *part, hipStream_t stream);
+
+}  // namespace rmm

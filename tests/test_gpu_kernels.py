@@ -1,0 +1,243 @@
+"""GPU tests of the single steps and of the boundary: column norms, exact
+selection (ties, plateaus, long score vectors), odd shapes and layouts that
+take the generic route, argument errors, determinism and stream ordering."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import assert_close, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rmm():
+    import input_adaptive_reduced_amd as r
+    r.load()
+    return r
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    return torch
+
+
+# --------------------------------------------------------------------------- column norms
+
+@pytest.mark.parametrize("n,d,dtype", [(1, 8, "bf16"), (3, 5, "f32"), (64, 256, "f32"), (300, 520, "bf16"),
+                                       (4096, 4096, "bf16"), (2048, 14336, "bf16"), (17, 1001, "bf16"),
+                                       (1000, 3, "f32"), (5000, 64, "bf16")])
+def test_colnorm(rmm, torch, n, d, dtype):
+    rng = np.random.default_rng(n * 7 + d)
+    A = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    if dtype == "bf16":
+        A = synthetic.round_to_bf16(A)
+    s = rmm.colnorm(to_device(A, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.colnorm(A)
+    got = s.cpu().numpy().astype(np.float64)
+    rel = np.max(np.abs(got - ref) / ref)
+    assert rel <= 1e-5, rel
+
+
+def test_colnorm_strided_and_unaligned(rmm, torch):
+    rng = np.random.default_rng(1)
+    W = synthetic.round_to_bf16(rng.standard_normal((70, 203)).astype(np.float32))
+    Wd = to_device(W, "bf16")
+    for sl in [(slice(None), slice(0, 200)), (slice(None), slice(1, 201)), (slice(3, 70), slice(5, 203))]:
+        s = rmm.colnorm(Wd[sl])
+        torch.cuda.synchronize()
+        ref = oracle.colnorm(W[sl])
+        assert np.max(np.abs(s.cpu().numpy() - ref) / ref) <= 1e-5
+
+
+# --------------------------------------------------------------------------- selection
+
+def _sel_case(rng, d, kind):
+    if kind == "random":
+        return np.abs(rng.standard_normal(d)).astype(np.float32)
+    if kind == "ties":
+        v = np.abs(rng.standard_normal(max(1, d // 10))).astype(np.float32)
+        return v[rng.integers(0, v.size, size=d)]
+    if kind == "const":
+        return np.full(d, 3.25, dtype=np.float32)
+    if kind == "zeros_and_inf":
+        s = np.abs(rng.standard_normal(d)).astype(np.float32)
+        s[rng.integers(0, d, size=max(1, d // 7))] = 0.0
+        s[rng.integers(0, d, size=max(1, d // 50))] = np.inf
+        return s
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("d", [1, 2, 7, 128, 1000, 2049, 4096, 14336, 30000])
+@pytest.mark.parametrize("kind", ["random", "ties", "const", "zeros_and_inf"])
+def test_select_exact(rmm, torch, d, kind):
+    rng = np.random.default_rng(d + len(kind))
+    s = _sel_case(rng, d, kind)
+    sd = torch.from_numpy(s).to("cuda:0")
+    for k in sorted({1, max(1, d // 3), max(1, d // 2), max(1, d - 1), d}):
+        got = rmm.select(sd, k)
+        torch.cuda.synchronize()
+        ref = oracle.topk(s.astype(np.float64), k)
+        assert np.array_equal(got.cpu().numpy(), ref), (d, kind, k)
+
+
+def test_select_batched(rmm, torch):
+    rng = np.random.default_rng(9)
+    s = np.abs(rng.standard_normal((32, 128))).astype(np.float32)
+    s[5] = 1.0  # a whole row of ties
+    got = rmm.select(torch.from_numpy(s).to("cuda:0"), 64)
+    torch.cuda.synchronize()
+    for b in range(32):
+        assert np.array_equal(got[b].cpu().numpy(), oracle.topk(s[b].astype(np.float64), 64)), b
+
+
+# --------------------------------------------------------------------------- odd shapes / generic route
+
+ODD = [
+    # (n, d, m, dtype, rho, note)
+    (1, 1, 1, "f32", 1.0, "scalar"),
+    (5, 37, 13, "bf16", 0.5, "m not a multiple of 8"),
+    (7, 9, 3, "f32", 0.2, "k = 2"),
+    (257, 300, 24, "bf16", 0.01, "k = 3, n one past a tile"),
+    (64, 4096, 64, "bf16", 1 / 4096, "k = 1"),
+    (33, 65, 72, "bf16", 0.999, "k = d - 0 (ceil)"),
+    (2, 100, 8, "bf16", 0.07, "rho*d just above an integer"),
+]
+
+
+@pytest.mark.parametrize("n,d,m,dtype,rho,note", ODD, ids=[o[-1] for o in ODD])
+def test_odd_shapes(rmm, torch, n, d, m, dtype, rho, note):
+    rng = np.random.default_rng(n + d + m)
+    A = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    B = rng.standard_normal((d, m)).astype(np.float32)
+    if dtype == "bf16":
+        A, B = synthetic.round_to_bf16(A), synthetic.round_to_bf16(B)
+    k = oracle.k_of(rho, d)
+    if n > 1 and k < d:
+        A, _ = enforce_gap_2d(A, k, dtype)
+    ref_idx = oracle.topk(oracle.colnorm(A), k)
+    Y, idx = rmm.matmul(to_device(A, dtype), to_device(B, dtype), rho)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    B64 = B.astype(np.float64)
+    assert_close(to_host(Y), oracle.reduced_product(A, B64, ref_idx),
+                 oracle.reduced_product(np.abs(A), np.abs(B64), ref_idx), k, dtype, note)
+
+
+def enforce_gap_2d(A, k, dtype):
+    from oracle.fixup import enforce_gap
+    return enforce_gap(A, [k], dtype)
+
+
+def test_strided_views_and_unaligned(rmm, torch):
+    """A column slice with lda > d (unaligned start, generic route), B offset by
+    one row, and an output with ldy > m: each agrees with the oracle, and the
+    untouched output columns keep their NaN fill."""
+    from oracle.fixup import enforce_gap
+    rng = np.random.default_rng(21)
+    n, d, m, rho = 200, 384, 96, 0.7
+    k = oracle.k_of(rho, d)
+    W = synthetic.round_to_bf16((rng.standard_normal((n, d + 9)) * np.exp(rng.standard_normal(d + 9))).astype(np.float32))
+    W[:, 1:1 + d], _ = enforce_gap(W[:, 1:1 + d], [k], "bf16")
+    A = np.ascontiguousarray(W[:, 1:1 + d])
+    B = synthetic.round_to_bf16(rng.standard_normal((d + 1, m)).astype(np.float32))
+    B64 = B[1:].astype(np.float64)
+    ref_idx = oracle.topk(oracle.colnorm(A), k)
+    ref_Y = oracle.reduced_product(A, B64, ref_idx)
+    ref_abs = oracle.reduced_product(np.abs(A), np.abs(B64), ref_idx)
+    Wd, Bd = to_device(W, "bf16"), to_device(B, "bf16")
+    Ad = Wd[:, 1:1 + d]
+    assert Ad.stride(0) == d + 9 and Ad.data_ptr() % 16 != 0
+    out = torch.full((n, m + 8), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    for a_t, o in [(Ad, None), (Ad.contiguous(), None), (Ad.contiguous(), out[:, :m])]:
+        Y, idx = rmm.matmul(a_t, Bd[1:], rho, out=o)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        assert_close(to_host(Y), ref_Y, ref_abs, k, "bf16", "strided")
+    assert torch.isnan(out[:, m:].float()).all(), "columns beyond m must stay untouched"
+
+
+# --------------------------------------------------------------------------- boundary
+
+def _desc(rmm, n, d, m, dtype=1):
+    ds = rmm.Desc()
+    rmm.load().rmm_desc_init(ctypes.byref(ds), dtype, n, d, m)
+    return ds
+
+
+def test_invalid_arguments_leave_outputs_untouched(rmm, torch):
+    L = rmm.load()
+    n, d, m = 64, 128, 64
+    A = torch.randn(n, d, device="cuda:0").to(torch.bfloat16)
+    B = torch.randn(d, m, device="cuda:0").to(torch.bfloat16)
+    Y = torch.full((n, m), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    idx = torch.full((d,), -7, dtype=torch.int32, device="cuda:0")
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda:0")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    good = _desc(rmm, n, d, m)
+    assert L.rmm_workspace_size(ctypes.byref(good), 0.5) <= ws.numel()
+
+    def call(ds, rho, a=A.data_ptr(), b=B.data_ptr(), y=Y.data_ptr(), w=ws.data_ptr(), wb=ws.numel()):
+        return L.rmm_matmul(ctypes.byref(ds), a, b, rho, y, idx.data_ptr(), w, wb, s)
+
+    for rho in (0.0, -1.0, 1.5, float("nan")):
+        assert call(good, rho) == 1
+    for field, val in [("n", 0), ("d", 0), ("m", -1), ("lda", 64), ("ldb", 3), ("ldy", 10), ("batch", 0),
+                       ("dtype", 7), ("b_group", 0), ("transB", 2), ("flags", 0x100), ("strideA", -1)]:
+        bad = _desc(rmm, n, d, m)
+        setattr(bad, field, val)
+        assert call(bad, 0.5) == 1, field
+    assert call(good, 0.5, a=0) == 1
+    assert call(good, 0.5, y=0) == 1
+    assert call(good, 0.5, y=A.data_ptr()) == 1, "output aliasing an input"
+    assert call(good, 0.5, w=0, wb=0) == 3
+    assert call(good, 0.5, wb=16) == 3
+    torch.cuda.synchronize()
+    assert torch.isnan(Y.float()).all()
+    assert (idx == -7).all()
+    # a valid call after the rejected ones works and writes only k indices
+    assert call(good, 0.5) == 0
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y.float()).any()
+    assert (idx[64:] == -7).all() and (idx[:64] >= 0).all()
+    # selection and norm entry points
+    sc = torch.rand(d, device="cuda:0")
+    assert L.rmm_select(sc.data_ptr(), 1, d, 0, idx.data_ptr(), s) == 1
+    assert L.rmm_select(sc.data_ptr(), 1, d, d + 1, idx.data_ptr(), s) == 1
+    assert L.rmm_colnorm(A.data_ptr(), 1, n, d, d - 1, sc.data_ptr(), ws.data_ptr(), ws.numel(), s) == 1
+    assert L.rmm_colnorm(A.data_ptr(), 1, n, d, d, sc.data_ptr(), 0, 0, s) == 3
+
+
+def test_repeat_calls_are_bitwise_identical(rmm, torch):
+    case = synthetic.make_case("c2", scale=dict(n=512, d=1024, m=512))
+    Ad, Bd = to_device(case.A, "bf16"), to_device(case.B, "bf16")
+    Y0, i0 = rmm.matmul(Ad, Bd, 0.7)
+    s0 = rmm.colnorm(Ad)
+    for _ in range(20):
+        Y, i = rmm.matmul(Ad, Bd, 0.7)
+        s = rmm.colnorm(Ad)
+        assert torch.equal(Y, Y0) and torch.equal(i, i0) and torch.equal(s, s0)
+
+
+def test_non_default_streams(rmm, torch):
+    case = synthetic.make_case("c2", scale=dict(n=256, d=512, m=256))
+    Ad, Bd = to_device(case.A, "bf16"), to_device(case.B, "bf16")
+    Y0, i0 = rmm.matmul(Ad, Bd, 0.5)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    A2 = (Ad.float() * 2).to(torch.bfloat16)
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        Y1, i1 = rmm.matmul(Ad, Bd, 0.5)
+    with torch.cuda.stream(s2):
+        Y2, i2 = rmm.matmul(A2, Bd, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y0) and torch.equal(i1, i0)
+    assert torch.equal(i2, i0)  # scaling A by 2 keeps the selection
+    assert torch.equal(Y2.float(), (Y0.float() * 2))

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Index sets must match bit for bit; outputs must satisfy the elementwise bound
+and relative Frobenius tolerance of ``gpu_util.assert_close``.  Inputs are the
+seeded synthetic workloads, with the TopK boundary gaps opened by
+``oracle.fixup`` so that fp32 (GPU) and fp64 (oracle) norms rank alike.
+
+Small instances cover every output element and span several tiles plus a
+ragged tail; the full-size workloads (the shapes the benchmark times, in the
+same launch configuration) compare every index and a sample of output rows.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import assert_close, sample_rows, to_device, to_host
+from oracle.fixup import enforce_gap, enforce_gap_batched
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rmm():
+    import input_adaptive_reduced_amd as r
+    r.load()
+    return r
+
+
+_CACHE = {}
+
+
+def linear_case(name, scale=None):
+    key = (name, tuple(sorted((scale or {}).items())))
+    if key not in _CACHE:
+        case = synthetic.make_case(name, scale)
+        d = case.A.shape[1]
+        ks = [oracle.k_of(r, d) for r in case.rhos]
+        A, _ = enforce_gap(case.A, ks, case.dtype)
+        _CACHE[key] = (case, A, np.ascontiguousarray(case.B, dtype=np.float64))
+    return _CACHE[key]
+
+
+def check_linear(rmm, case, A, B64, rho, rows=None, full_path=False):
+    torch = pytest.importorskip("torch")
+    d = A.shape[1]
+    k = oracle.k_of(rho, d)
+    assert rmm.k_of(rho, d) == k
+    ref_idx = oracle.topk(oracle.colnorm(A), k)
+    Ad, Bd = to_device(A, case.dtype), to_device(case.B, case.dtype)
+    Y, idx = rmm.matmul(Ad, Bd, rho, full_path=full_path)
+    torch.cuda.synchronize()
+    got_idx = idx.cpu().numpy()
+    assert np.array_equal(got_idx, ref_idx), f"{case.name} rho={rho}: index sets differ"
+    Yh = to_host(Y)
+    if rows is not None:
+        Yh = Yh[rows]
+    Y_ref = oracle.reduced_product(A, B64, ref_idx, 1.0, rows)
+    absprod = oracle.reduced_product(np.abs(A), np.abs(B64), ref_idx, 1.0, rows)
+    return assert_close(Yh, Y_ref, absprod, k, case.dtype, f"{case.name} rho={rho}")
+
+
+SMALL = [
+    ("c1", None),
+    ("c2", dict(n=300, d=520, m=264)),
+    ("c2", dict(n=512, d=1024, m=512)),
+    ("c3", dict(n=256, d=1792, m=512)),
+    ("c5", dict(n=130, d=640, m=776)),
+]
+
+
+@pytest.mark.parametrize("name,scale", SMALL, ids=[f"{n}-{s}" for n, s in SMALL])
+def test_small_linear_all_rho(rmm, name, scale):
+    case, A, B64 = linear_case(name, scale)
+    for rho in case.rhos:
+        check_linear(rmm, case, A, B64, rho)
+    check_linear(rmm, case, A, B64, 1.0, full_path=True)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_full_size_linear(rmm, name):
+    case, A, B64 = linear_case(name)
+    rows = sample_rows(A.shape[0], 12, seed=7)
+    for rho in case.rhos:
+        check_linear(rmm, case, A, B64, rho, rows=rows)
+
+
+def attention_case(scale=None):
+    key = ("c4", tuple(sorted((scale or {}).items())))
+    if key not in _CACHE:
+        case = synthetic.make_case("c4", scale)
+        dh = case.A.shape[2]
+        Q, _ = enforce_gap_batched(case.A, [oracle.k_of(r, dh) for r in case.rhos], "bf16")
+        _CACHE[key] = (case, Q)
+    return _CACHE[key]
+
+
+def check_attention(rmm, case, Q, rho, heads, rows):
+    torch = pytest.importorskip("torch")
+    K = case.B
+    hq, hkv = Q.shape[0], K.shape[0]
+    group = hq // hkv
+    dh = Q.shape[2]
+    k = oracle.k_of(rho, dh)
+    Qd, Kd = to_device(Q, "bf16"), to_device(K, "bf16")
+    S, idx = rmm.matmul(Qd, Kd, rho, transB=True, b_group=group, alpha=case.alpha)
+    torch.cuda.synchronize()
+    got_idx = idx.cpu().numpy()
+    for h in range(hq):
+        ref = oracle.topk(oracle.colnorm(Q[h]), k)
+        assert np.array_equal(got_idx[h], ref), f"head {h}: index sets differ"
+    for h in heads:
+        g = h // group
+        Kt = np.ascontiguousarray(K[g].astype(np.float64).T)
+        ref_idx = got_idx[h]
+        Y_ref = oracle.reduced_product(Q[h], Kt, ref_idx, case.alpha, rows)
+        absprod = oracle.reduced_product(np.abs(Q[h]), np.abs(Kt), ref_idx, abs(case.alpha), rows)
+        Sh = to_host(S[h])
+        if rows is not None:
+            Sh = Sh[rows]
+        assert_close(Sh, Y_ref, absprod, k, "bf16", f"c4 head {h} rho={rho}")
+
+
+def test_small_attention(rmm):
+    case, Q = attention_case(dict(heads=8, kv_heads=2, L=300))
+    for rho in case.rhos:
+        check_attention(rmm, case, Q, rho, heads=range(8), rows=None)
+
+
+def test_full_size_attention(rmm):
+    case, Q = attention_case()
+    rows = sample_rows(Q.shape[1], 6, seed=3)
+    for rho in case.rhos:
+        check_attention(rmm, case, Q, rho, heads=[0, 3, 4, 17, 31], rows=rows)
+
+
+@pytest.mark.parametrize("scale", [dict(n=4, d=640, m=776), None], ids=["small", "full"])
+def test_decode(rmm, scale):
+    torch = pytest.importorskip("torch")
+    case, _, B64 = linear_case("c5", scale)
+    dec = synthetic.make_decode_case(case)
+    a = dec.A  # no gap fix-up: |a_j| is exact on both sides, ties go to the lower index
+    d = a.shape[1]
+    for rho in dec.rhos:
+        k = oracle.k_of(rho, d)
+        ref_idx = oracle.topk(oracle.colnorm(a), k)
+        Y, idx = rmm.matmul(to_device(a, "bf16"), to_device(case.B, "bf16"), rho)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        Y_ref = oracle.reduced_product(a, B64, ref_idx)
+        absprod = oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx)
+        assert_close(to_host(Y), Y_ref, absprod, k, "bf16", f"decode rho={rho}")
+
+
+def test_decode_exact_ties(rmm):
+    """n = 1 with many equal |a_j| (bf16 has few values): ties -> lower index."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    d, m = 1000, 64
+    a = synthetic.round_to_bf16(rng.choice([-2.0, -1.0, 0.5, 1.0, 2.0], size=(1, d)).astype(np.float32))
+    B = synthetic.round_to_bf16(rng.standard_normal((d, m)).astype(np.float32))
+    for k in (1, 137, 500, 999, 1000):
+        rho = k / d
+        assert oracle.k_of(rho, d) == k
+        ref_idx = oracle.topk(np.abs(a[0]).astype(np.float64), k)
+        Y, idx = rmm.matmul(to_device(a, "bf16"), to_device(B, "bf16"), rho)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), k
+        B64 = B.astype(np.float64)
+        assert_close(to_host(Y), oracle.reduced_product(a, B64, ref_idx),
+                     oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx), k, "bf16", f"ties k={k}")
