@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Throughput of the reduced-matrix-multiplication path on one MI355X.
+
+A step is one whole rmm_matmul -- column norms, TopK, gather, reduced product
+-- on the Llama-3.1-8B-shaped projection A (4096 x 4096, bf16) x B
+(4096 x 4096, bf16) at rho = 0.8 (k = 3277), the retention ratio of the
+paper's latency experiments.  ``value`` is 2 n k m / t per step in TFLOP/s
+with every input resident in HBM: the steps rotate over enough distinct
+(A, B) pairs that the working set exceeds the 256 MB Infinity Cache.
+
+The same JSON line carries
+  * ``sweep``: the path at rho = 0.5, 0.7, 0.8, 1.0 (and rho = 1 with the
+    full path forced) with the dense bf16 torch.matmul (hipBLASLt) time and
+    the speedup over it;
+  * ``roofline``: the reduced-product GEMM kernel (the dominant kernel),
+    timed per launch with HIP events recorded around it on its own stream,
+    against the bf16 MFMA peak; ``traffic`` comes from committed rocprofv3
+    counters when they were taken on the current kernel source, else null;
+  * ``cpu_baseline``: the CPU oracle timed on this host on a bounded sample
+    (full norms and selection, a sample of output rows, extrapolated).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "RMM layer TFLOP/s (2n⌈ρd⌉m/t) and speedup vs dense GEMM at ρ=0.5–1.0"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
+MALL_BYTES = 256 << 20
+
+WORKLOADS = {
+    "c2": dict(case="c2", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0),
+               label="Llama-3.1-8B-shaped projection: A 4096x4096 bf16 x B 4096x4096 bf16"),
+    "c3": dict(case="c3", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0),
+               label="Llama-3.1-8B-shaped MLP down projection: A 2048x14336 bf16 x B 14336x4096 bf16"),
+    "c5": dict(case="c5", rho=0.8, sweep=(0.8, 1.0),
+               label="Llama-3.1-70B-shaped MLP up projection: A 4096x8192 bf16 x B 8192x28672 bf16"),
+    "c5-decode": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), decode=True,
+                      label="70B up projection decode: a 1x8192 bf16 x B 8192x28672 bf16"),
+    "c4": dict(case="c4", rho=0.5, sweep=(0.5, 1.0),
+               label="QK^T with head-dim selection: Q 32x4096x128, K 8 GQA heads x4096x128 bf16"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel_key, workload):
+    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(f"{kernel_key}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or source_digest(src) != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Runner:
+    """Prepared inputs, outputs and workspaces for one workload."""
+
+    def __init__(self, torch, rmm, case, decode, copies):
+        import numpy as np
+        import synthetic
+        self.torch, self.rmm = torch, rmm
+        dev = torch.device("cuda:0")
+        self.case = case
+        self.batched = case.A.ndim == 3
+        if decode:
+            case = synthetic.make_decode_case(case)
+        self.A_host = case.A
+        self.B_host = case.B
+
+        def up(x):
+            bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
+            return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+        A0, B0 = up(case.A), up(case.B)
+        per_set = A0.numel() * 2 + B0.numel() * 2
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2 * MALL_BYTES / per_set)))
+        self.copies = copies
+        self.A = [A0] + [A0.clone() for _ in range(copies - 1)]
+        self.B = [B0] + [B0.clone() for _ in range(copies - 1)]
+        self.transB = case.transB
+        self.group = case.group
+        self.alpha = case.alpha
+        if self.batched:
+            self.n, self.d, self.m = case.A.shape[1], case.A.shape[2], case.B.shape[1]
+            self.batch = case.A.shape[0]
+        else:
+            self.n, self.d = case.A.shape
+            self.m = case.B.shape[1]
+            self.batch = 1
+        shape = (self.batch, self.n, self.m) if self.batched else (self.n, self.m)
+        self.Y = [torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+        self.ws = {}
+        self.idx = {}
+
+    def flops(self, rho):
+        k = self.rmm.k_of(rho, self.d)
+        return 2.0 * self.batch * self.n * k * self.m
+
+    def call(self, i, rho, full_path=False):
+        rmm = self.rmm
+        key = (rho, full_path)
+        if key not in self.ws:
+            need = rmm.workspace_size(self.A[0], self.B[0], rho, transB=self.transB, b_group=self.group,
+                                      full_path=full_path)
+            self.ws[key] = self.torch.empty(max(1, need), dtype=self.torch.uint8, device="cuda:0")
+            k = rmm.k_of(rho, self.d)
+            self.idx[key] = self.torch.empty(self.batch * k, dtype=self.torch.int32, device="cuda:0")
+        rmm.matmul(self.A[i], self.B[i], rho, transB=self.transB, b_group=self.group, alpha=self.alpha,
+                   out=self.Y[i], idx_out=self.idx[key], workspace=self.ws[key], full_path=full_path)
+
+    def dense(self, i):
+        """Dense bf16 product of the same shape (hipBLASLt through torch)."""
+        torch = self.torch
+        if self.batched:
+            # K^T per query head, materialised once outside the timed region so
+            # the batched product's right operand is a plain contiguous tensor
+            if not hasattr(self, "_kt"):
+                self._kt = [b.transpose(1, 2).repeat_interleave(self.group, dim=0).contiguous() for b in self.B]
+            torch.baddbmm(self.Y[i], self.A[i], self._kt[i], beta=0.0, alpha=self.alpha, out=self.Y[i])
+            return
+        if self.transB:
+            torch.matmul(self.A[i], self.B[i].t(), out=self.Y[i])
+        else:
+            torch.matmul(self.A[i], self.B[i], out=self.Y[i])
+
+
+def time_steps(torch, fn, steps, warmup, copies, graph):
+    """Mean ms per step over `steps` calls of fn(i) rotating over copies."""
+    for i in range(warmup):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    if graph:
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(copies):
+                fn(i)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(i)
+            graphs.append(g)
+        for i in range(copies):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % copies].replay()  # noqa: E731
+    else:
+        run = lambda i: fn(i % copies)  # noqa: E731
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        run(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def kernel_times(torch, rmm, runner, rho, steps, copies):
+    """Per-kernel mean ms from HIP events the library records around each launch."""
+    rmm.timing_enable(True, capacity=steps * 16)
+    rmm.timing_collect()
+    for i in range(steps):
+        runner.call(i % copies, rho)
+    torch.cuda.synchronize()
+    rec = rmm.timing_collect()
+    rmm.timing_enable(False)
+    return {kname: (ms / cnt if cnt else 0.0, cnt / steps) for kname, (ms, cnt) in rec.items()}
+
+
+def cpu_baseline(runner, rho, budget_s=12.0):
+    """The oracle as it stands, on this host's cores: full norms and selection,
+    the product on a sample of output rows, extrapolated to the whole job."""
+    import numpy as np
+    import oracle
+    threads = oracle.host_threads()
+    A = runner.A_host if not runner.batched else runner.A_host[0]
+    B = runner.B_host if not runner.batched else np.ascontiguousarray(runner.B_host[0].T)
+    n, d = A.shape
+    m = B.shape[1]
+    A64 = np.ascontiguousarray(A, dtype=np.float64)
+    B64 = np.ascontiguousarray(B, dtype=np.float64)
+    k = oracle.k_of(rho, d)
+    t0 = time.perf_counter()
+    s = oracle.colnorm(A64)
+    idx = oracle.topk(s, k)
+    t_sel = time.perf_counter() - t0
+    probe = min(n, max(threads, 8))
+    t0 = time.perf_counter()
+    oracle.reduced_product(A64, B64, idx, 1.0, rows=list(range(probe)), threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(n, max(probe, probe * budget_s / max(t_probe, 1e-6))))
+    rows = max(threads, rows // threads * threads) if rows >= threads else rows
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(n, size=rows, replace=False))
+    t0 = time.perf_counter()
+    oracle.reduced_product(A64, B64, idx, 1.0, rows=sample, threads=threads)
+    t_rows = time.perf_counter() - t0
+    per_matrix = t_sel + t_rows * n / rows
+    total = per_matrix * runner.batch
+    value = 2.0 * runner.batch * n * k * m / total / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 oracle: full column norms + full-sort TopK of one {n}x{d} matrix "
+                       f"({t_sel:.2f} s) and the reduced product for {rows} of {n} output rows "
+                       f"({t_rows:.2f} s), extrapolated to all rows" +
+                       (f" and {runner.batch} heads" if runner.batch > 1 else "")),
+            "seconds_measured": t_sel + t_rows + t_probe}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=None, help="input sets rotated over (default: > 2x MALL)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--kernel-steps", type=int, default=50, help="steps for per-kernel event timing")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import input_adaptive_reduced_amd as rmm
+    import synthetic
+    rmm.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    wl = WORKLOADS[args.workload]
+    case = synthetic.make_case(wl["case"])
+    runner = Runner(torch, rmm, case, wl.get("decode", False), args.copies)
+    rho = wl["rho"]
+    graph = not args.no_graph
+    log(f"workload {args.workload}: {wl['label']}; copies={runner.copies} graph={graph}")
+
+    ms = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph)
+    value = runner.flops(rho) / (ms * 1e-3) / 1e12
+    k = rmm.k_of(rho, runner.d)
+    log(f"rho={rho} k={k}: {ms * 1e3:.1f} us/step, {value:.1f} TFLOP/s")
+
+    sweep = []
+    if not args.no_sweep:
+        runner.dense(0)
+        dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
+        log(f"dense torch.matmul: {dense_ms * 1e3:.1f} us/step")
+        for r in wl["sweep"]:
+            for full in ((False, True) if r == 1.0 else (False,)):
+                t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
+                               runner.copies, graph)
+                ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
+                       "tflops": runner.flops(r) / (t * 1e-3) / 1e12}
+                if dense_ms:
+                    ent["dense_ms"] = dense_ms
+                    ent["speedup_vs_dense"] = dense_ms / t
+                    ent["ideal_speedup"] = 1.0 / (ent["k"] / runner.d)
+                sweep.append(ent)
+                log(f"  rho={r}{' full' if full else ''}: {t * 1e3:.1f} us, {ent['tflops']:.1f} TFLOP/s"
+                    + (f", x{ent['speedup_vs_dense']:.2f} vs dense" if dense_ms else ""))
+
+    kt = kernel_times(torch, rmm, runner, rho, args.kernel_steps, runner.copies)
+    log("per-kernel mean us: " + ", ".join(f"{kk}={v[0] * 1e3:.1f}" for kk, v in kt.items() if v[1]))
+    if runner.n == 1:
+        dom, bound = "gemv", "hbm"
+        gemv_ms = kt["gemv"][0]
+        algo_bytes = k * runner.m * 2 + runner.d * 2 + runner.m * 4  # kept B rows + a + fp32 partial row
+        achieved = algo_bytes / (gemv_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "gemv_partial", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes,
+                "kernel_ms": gemv_ms}
+    else:
+        dom = "gemm"
+        gemm_ms = kt["gemm"][0]
+        achieved = runner.flops(rho) / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "gemm_bf16", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "algorithmic_flops": runner.flops(rho), "kernel_ms": gemm_ms}
+    roof["traffic"] = load_traffic(dom, args.workload)
+    roof["per_kernel_ms"] = {kk: v[0] for kk, v in kt.items() if v[1]}
+
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        cpu = cpu_baseline(runner, rho)
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl['label']}, rho={rho} (k={k})",
+                   "n": runner.n, "d": runner.d, "m": runner.m, "batch": runner.batch, "rho": rho, "k": k,
+                   "input_copies_rotated": runner.copies, "hip_graph": graph},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

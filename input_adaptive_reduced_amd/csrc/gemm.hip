@@ -81,12 +81,32 @@ __device__ __forceinline__ void tile_coords(int t, int T, int tiles_m, int tiles
     tn = in / gsz;
 }
 
+// Buffer resource for raw buffer loads on gfx9-family parts (gfx950): loads
+// at byte offsets at or beyond `bytes` return zero.  Offsets of rows that
+// must read as zero (rows past n, padding entries of the index list) are
+// pushed to kOob, which stays out of range while K steps are added.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int32_t nrec = (int32_t)min(bytes, (int64_t)0x7fffffff);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nrec, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding, other counters left unconstrained):
+// the next tile's loads must have landed before they are written to LDS.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 template <int BM, int BN, int WM, int WN, int BMODE, bool SPLIT>
 __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;
+    constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_PER = BM * 8 / NT;
+    constexpr int A_PER = BM * 8 / NT;  // 16-byte chunks per thread per K step
     constexpr int B_PER = BN * 8 / NT;  // bmode 1
     static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
     static_assert(BMODE == 1 || BN <= NT, "bmode 0 needs one 8x8 B block per thread at most");
@@ -107,27 +127,54 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int64_t b = blockIdx.z;
     const int split = blockIdx.y;
 
-    const uint16_t *A = g.A + b * g.strideA;
-    const uint16_t *B = g.B + (b / g.group) * g.strideB;
-    const int32_t *idx = g.idx ? g.idx + b * g.ld_idx : nullptr;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (b / g.group) * g.strideB, g.b_bytes);
+    const int32_t *idx = BMODE == 0 ? g.idx + b * g.ld_idx : nullptr;
 
     const int KT = (int)(g.kpad / BK);
     const int per = (KT + g.splits - 1) / g.splits;
     const int kt0 = split * per;
     const int kt1 = min(KT, kt0 + per);
 
+    // Staged chunk assignment: chunk c = tid + i*NT is row c/8, logical
+    // 16-byte chunk c%8 of the tile row; rows past n (or m) read as zero.
+    uint32_t aoff[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int c = tid + i * NT;
+        const int64_t gr = m0 + (c >> 3);
+        aoff[i] = gr < g.n ? (uint32_t)((gr * g.lda + (c & 7) * 8) * 2) : kOob;
+    }
+    uint32_t boff[BMODE == 1 ? B_PER : 1];
+    if constexpr (BMODE == 1) {
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            const int c = tid + i * NT;
+            const int64_t gr = n0 + (c >> 3);
+            boff[i] = gr < g.m ? (uint32_t)((gr * g.ldb + (c & 7) * 8) * 2) : kOob;
+        }
+    }
+    // bmode 0: thread owns the 8x8 block (k rows kq*8.., columns nc*8..)
+    const bool bthr = BMODE == 0 && (BN == NT || tid < BN);
+    const int kq = tid / (BN / 8), nc = tid % (BN / 8);
+    const int64_t bcol = n0 + nc * 8;
+
     uint4 ra[A_PER];
     uint4 rb[BMODE == 0 ? 8 : B_PER];
 
+    // Kept row numbers of B for one K step (8 per thread); -1 marks padding.
+    auto load_idx = [&](int kt, int32_t (&o)[8]) {
+        if (!bthr) return;
+        const int t0 = min(kt, KT - 1) * BK + kq * 8;
+        const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0);
+        const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + 4);
+        o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
+        o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
+    };
     auto load_a = [&](int kt) {
+        const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int c = tid + i * NT;
-            const int r = c >> 3, ch = c & 7;
-            const int64_t gr = m0 + r;
-            ra[i] = gr < g.n ? *reinterpret_cast<const uint4 *>(A + gr * g.lda + (int64_t)kt * BK + ch * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < A_PER; ++i) ra[i] = buf_load16(rA, aoff[i] + ko);
     };
     auto store_a = [&](int buf) {
 #pragma unroll
@@ -137,34 +184,24 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
             sA[buf][r * 8 + swz(r, ch)] = ra[i];
         }
     };
-    auto load_b = [&](int kt) {
+    auto load_b = [&](int kt, const int32_t (&ix)[8]) {
         if constexpr (BMODE == 0) {
-            if (tid < BN) {
-                const int kq = tid / (BN / 8), nc = tid % (BN / 8);
-                const int64_t col = n0 + nc * 8;
+            if (bthr) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    const int64_t t = (int64_t)kt * BK + kq * 8 + r;
-                    const int64_t gi = t < g.k ? (idx ? (int64_t)idx[t] : t) : -1;
-                    rb[r] = (gi >= 0 && col < g.m) ? *reinterpret_cast<const uint4 *>(B + gi * g.ldb + col)
-                                                   : make_uint4(0, 0, 0, 0);
+                    const uint32_t off = ix[r] >= 0 ? (uint32_t)(((int64_t)ix[r] * g.ldb + bcol) * 2) : kOob;
+                    rb[r] = buf_load16(rB, off);
                 }
             }
         } else {
+            const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) {
-                const int c = tid + i * NT;
-                const int r = c >> 3, ch = c & 7;
-                const int64_t gr = n0 + r;
-                rb[i] = gr < g.m ? *reinterpret_cast<const uint4 *>(B + gr * g.ldb + (int64_t)kt * BK + ch * 8)
-                                 : make_uint4(0, 0, 0, 0);
-            }
+            for (int i = 0; i < B_PER; ++i) rb[i] = buf_load16(rB, boff[i] + ko);
         }
     };
     auto store_b = [&](int buf) {
         if constexpr (BMODE == 0) {
-            if (tid < BN) {
-                const int kq = tid / (BN / 8), nc = tid % (BN / 8);
+            if (bthr) {
                 uint4 ob[8];
                 transpose8x8(rb, ob);
 #pragma unroll
@@ -191,63 +228,83 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    auto read_frags = [&](int buf, int ks, bf16x8_t (&fa)[FM], bf16x8_t (&fb)[FN]) {
+        const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WTM + i * 32 + (lane & 31);
+            fa[i] = as_bf16x8(sA[buf][r * 8 + swz(r, ch)]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int nn = wn * WTN + j * 32 + (lane & 31);
+            fb[j] = as_bf16x8(sB[buf][nn * 8 + swz(nn, ch)]);
+        }
+    };
+
+    // K loop on two LDS buffers.  Step kt contracts buffer `cur` while the
+    // next tile's loads are in flight into registers (gathered B rows are
+    // addressed by the row list loaded one step earlier, and the row list of
+    // step kt+2 is fetched), then publishes the next tile into buffer cur^1.
+    // Every step ends with vmcnt(0): nothing is in flight across the
+    // back-edge, so the compiler needs no conservative waits at the loop
+    // head.  The final step fetches a clamped tile that nobody reads.
     if (kt0 < kt1) {
+        int32_t ixn[8];
+        load_idx(kt0, ixn);
         load_a(kt0);
-        load_b(kt0);
+        load_b(kt0, ixn);
+        load_idx(kt0 + 1, ixn);
+        wait_vm0();
         store_a(0);
         store_b(0);
         __syncthreads();
         for (int kt = kt0; kt < kt1; ++kt) {
             const int cur = (kt - kt0) & 1;
-            const bool more = kt + 1 < kt1;
-            if (more) {
-                load_a(kt + 1);
-                load_b(kt + 1);
-            }
+            const int ktn = min(kt + 1, kt1 - 1);
+            load_a(ktn);
+            load_b(ktn, ixn);  // rows of step kt+1
+            load_idx(kt + 2, ixn);
 #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
-                const int ch = ks * 2 + (lane >> 5);
                 bf16x8_t fa[FM], fb[FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int r = wm * WTM + i * 32 + (lane & 31);
-                    fa[i] = as_bf16x8(sA[cur][r * 8 + swz(r, ch)]);
-                }
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int nn = wn * WTN + j * 32 + (lane & 31);
-                    fb[j] = as_bf16x8(sB[cur][nn * 8 + swz(nn, ch)]);
-                }
+                read_frags(cur, ks, fa, fb);
+                // operands swapped: each lane ends up holding four consecutive
+                // output columns of one output row
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
             }
-            if (more) {
-                store_a(cur ^ 1);
-                store_b(cur ^ 1);
-            }
+            wait_vm0();
+            store_a(cur ^ 1);
+            store_b(cur ^ 1);
             __syncthreads();
         }
     }
 
-    // epilogue: lane l, register e of a 32x32 block holds row
-    // (e/4)*8 + (l/32)*4 + e%4 and column l%32.
+    // epilogue: lane l, registers 4q..4q+3 of block (i, j) hold output row
+    // i*32 + l%32 and columns j*32 + 8q + 4(l/32) + 0..3.
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+        if (row >= g.n) continue;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                if (row < g.n && col < g.m) {
-                    if constexpr (SPLIT) {
-                        g.part[(((int64_t)split * g.batch + b) * g.n + row) * g.m + col] = acc[i][j][e];
-                    } else {
-                        g.Y[b * g.strideY + row * g.ldy + col] = f32_to_bf16(g.alpha * acc[i][j][e]);
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                if constexpr (SPLIT) {
+                    *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m + col) =
+                        make_float4(v0, v1, v2, v3);
+                } else {
+                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * v0)) | (uint32_t(f32_to_bf16(g.alpha * v1)) << 16);
+                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * v2)) | (uint32_t(f32_to_bf16(g.alpha * v3)) << 16);
+                    *reinterpret_cast<uint2 *>(g.Y + b * g.strideY + row * g.ldy + col) = make_uint2(lo, hi);
                 }
             }
         }
@@ -280,12 +337,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 // ------------------------------------------------------------------ pack
-// dst[b][r][t] = src[b/group][r][idx[b][t]] (t < k), 0 for k <= t < kpad.
-// Whole source rows are staged in LDS (16-byte loads when aligned) when
-// `rows_per_wg` rows of d elements fit; otherwise gathers go to global memory.
+// dst[b][r][t] = src[b/group][r][idx[b][t]] for t < kpad, 0 where idx is -1
+// (the padded index list is -1 beyond k).  Whole source rows are staged in
+// LDS with 16-byte loads when `rows_per_wg` rows fit; each thread then reads
+// the eight indices of one output chunk once and gathers that chunk for every
+// staged row.  Without LDS staging the gathers read global memory.
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ src, int64_t rows, int64_t d,
                                                    int64_t ld_src, int64_t src_stride, int64_t group,
-                                                   const int32_t *__restrict__ idx_all, int64_t ld_idx, int64_t k,
+                                                   const int32_t *__restrict__ idx_all, int64_t ld_idx,
                                                    int64_t kpad, uint16_t *__restrict__ dst, int64_t dst_stride,
                                                    int rows_per_wg, int use_lds, int vec_ok) {
     extern __shared__ uint16_t rowbuf[];
@@ -314,25 +373,21 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
         __syncthreads();
     }
     const int64_t cpr = kpad / 8;  // output chunks per row
-    for (int64_t q = tid; q < (int64_t)nr * cpr; q += 256) {
-        const int64_t rr = q / cpr, c = q - rr * cpr;
-        uint32_t w[4];
+    for (int64_t c = tid; c < cpr; c += 256) {
+        const int4 p0 = *reinterpret_cast<const int4 *>(idx + c * 8);
+        const int4 p1 = *reinterpret_cast<const int4 *>(idx + c * 8 + 4);
+        const int32_t j[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        for (int rr = 0; rr < nr; ++rr) {
+            uint32_t h[8];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t h[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int64_t t = c * 8 + 2 * p + e;
-                uint16_t v = 0;
-                if (t < k) {
-                    const int64_t j = idx[t];
-                    v = use_lds ? rowbuf[rr * d + j] : S[(r0 + rr) * ld_src + j];
-                }
-                h[e] = v;
+            for (int e = 0; e < 8; ++e) {
+                const int64_t jj = j[e] >= 0 ? j[e] : 0;
+                const uint16_t v = use_lds ? rowbuf[rr * d + jj] : S[(r0 + rr) * ld_src + jj];
+                h[e] = j[e] >= 0 ? v : 0;
             }
-            w[p] = h[0] | (h[1] << 16);
+            *reinterpret_cast<uint4 *>(D + (r0 + rr) * kpad + c * 8) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
-        *reinterpret_cast<uint4 *>(D + (r0 + rr) * kpad + c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
@@ -488,7 +543,7 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_
 static constexpr int64_t kPackLdsBytes = 64 * 1024;
 
 hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src, int64_t src_stride,
-                       int64_t group, const int32_t *idx, int64_t ld_idx, int64_t k, int64_t kpad, void *dst,
+                       int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad, void *dst,
                        int64_t dst_stride, int64_t batch, hipStream_t stream) {
     if (dt != RMM_BF16) return hipErrorInvalidValue;
     int dev = 0;
@@ -508,7 +563,7 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
     const size_t lds = use_lds ? (size_t)rpw * (size_t)row_bytes : 0;
     dim3 grid((unsigned)((rows + rpw - 1) / rpw), (unsigned)batch);
     pack_kernel<<<grid, 256, lds, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src, src_stride, group,
-                                            idx, ld_idx, k, kpad, static_cast<uint16_t *>(dst), dst_stride, rpw,
+                                            idx, ld_idx, kpad, static_cast<uint16_t *>(dst), dst_stride, rpw,
                                             use_lds, vec_ok);
     return hipGetLastError();
 }

@@ -79,20 +79,15 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
     if (vec_ok && j0 + V <= d) {
         const T *p = Ab + j0;
         int64_t i = r0 + ty;
-        // four rows in flight per iteration; each row's sum still runs in row order
-        for (; i + 3 * tr < r1; i += 4 * tr) {
-            float v0[V], v1[V], v2[V], v3[V];
-            Vec16<T>::load(p + i * lda, v0);
-            Vec16<T>::load(p + (i + tr) * lda, v1);
-            Vec16<T>::load(p + (i + 2 * tr) * lda, v2);
-            Vec16<T>::load(p + (i + 3 * tr) * lda, v3);
+        // eight rows in flight per iteration; each column's sum still runs in row order
+        for (; i + 7 * tr < r1; i += 8 * tr) {
+            float v[8][V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                acc[e] = fmaf(v0[e], v0[e], acc[e]);
-                acc[e] = fmaf(v1[e], v1[e], acc[e]);
-                acc[e] = fmaf(v2[e], v2[e], acc[e]);
-                acc[e] = fmaf(v3[e], v3[e], acc[e]);
-            }
+            for (int q = 0; q < 8; ++q) Vec16<T>::load(p + (i + q * tr) * lda, v[q]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[e] = fmaf(v[q][e], v[q][e], acc[e]);
         }
         for (; i < r1; i += tr) {
             float v0[V];
@@ -125,15 +120,22 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
     }
 }
 
+// 64 columns per workgroup; four row-chunk groups per column, each summing
+// every fourth chunk in ascending order, then combined 0 + 1 + 2 + 3.
 __global__ __launch_bounds__(256) void colnorm_finalize_kernel(const float *__restrict__ part, int64_t chunks,
-                                                               int64_t d, int64_t total, float *__restrict__ s) {
-    int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= total) return;
-    int64_t b = q / d, j = q - b * d;
-    const float *p = part + b * chunks * d + j;
+                                                               int64_t d, float *__restrict__ s) {
+    __shared__ float red[4][64];
+    const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int64_t b = blockIdx.y;
+    const int64_t j = (int64_t)blockIdx.x * 64 + c;
     float sum = 0.f;
-    for (int64_t r = 0; r < chunks; ++r) sum += p[r * d];
-    s[q] = __fsqrt_rn(sum);
+    if (j < d) {
+        const float *p = part + b * chunks * d + j;
+        for (int64_t r = g; r < chunks; r += 4) sum += p[r * d];
+    }
+    red[g][c] = sum;
+    __syncthreads();
+    if (g == 0 && j < d) s[b * d + j] = __fsqrt_rn(((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
 // ------------------------------------------------------------------ block scan
@@ -181,12 +183,15 @@ struct KeySource {
     __device__ __forceinline__ uint32_t key(int64_t j) const { return lds ? lds[j] : score_key(score(j)); }
 };
 
+// Long score vectors (beyond the register-resident kernel's reach): keys are
+// re-read from LDS (or global memory when d is very large) in every pass.
 // grid: batch; block: BS.  dynamic LDS: d keys when use_lds.
 template <int BS>
-__global__ __launch_bounds__(BS) void select_kernel(const float *__restrict__ s_all, const void *__restrict__ a_all,
-                                                     int a_bf16, int64_t a_stride, int64_t d, int64_t k,
-                                                     int32_t *__restrict__ idx_all, int64_t ld_idx,
-                                                     float *__restrict__ aval, int use_lds) {
+__global__ __launch_bounds__(BS) void select_big_kernel(const float *__restrict__ s_all, const void *__restrict__ a_all,
+                                                        int a_bf16, int64_t a_stride, int64_t d, int64_t k,
+                                                        int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                        int32_t *__restrict__ pad_all, int64_t ld_pad,
+                                                        float *__restrict__ aval, int use_lds) {
     extern __shared__ uint32_t keys[];
     __shared__ int hist[2048];
     __shared__ int scan_sm[BS / 64 + 1];
@@ -271,7 +276,10 @@ __global__ __launch_bounds__(BS) void select_kernel(const float *__restrict__ s_
         }
     }
     int pos = block_exclusive_scan<BS>(sel, scan_sm, tot);
-    int32_t *idx = idx_all + b * ld_idx;
+    int32_t *idx = idx_all ? idx_all + b * ld_idx : nullptr;
+    int32_t *pad = pad_all ? pad_all + b * ld_pad : nullptr;
+    if (pad)
+        for (int64_t q = k + tid; q < ld_pad; q += BS) pad[q] = -1;
     {
         int e = eq_before;
         for (int64_t j = j0; j < j1; ++j) {
@@ -282,7 +290,8 @@ __global__ __launch_bounds__(BS) void select_kernel(const float *__restrict__ s_
                 ++e;
             }
             if (take && pos < k) {
-                idx[pos] = (int32_t)j;
+                if (idx) idx[pos] = (int32_t)j;
+                if (pad) pad[pos] = (int32_t)j;
                 if (aval) {
                     float x = src.a_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(src.a)[j])
                                          : static_cast<const float *>(src.a)[j];
@@ -294,9 +303,155 @@ __global__ __launch_bounds__(BS) void select_kernel(const float *__restrict__ s_
     }
 }
 
-__global__ void iota_kernel(int32_t *idx, int64_t k, int64_t total) {
+// Register-resident exact TopK for d <= BS * E: thread t owns the contiguous
+// scores [t*E, t*E + E).  Three radix passes over 11/11/10-bit digits of the
+// order-preserving key, each: LDS histogram (ping-pong buffers, so the next
+// one is cleared while this one fills), per-thread bin sums from the top, a
+// wave scan plus wave totals to find the digit holding the k-th largest key.
+// The passes stop early once the digit's bin holds exactly the keys still
+// needed.  Compaction in ascending index order keeps every key whose resolved
+// prefix is larger and the lowest-indexed keys whose prefix equals it.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+template <int BS, int E>
+__global__ __launch_bounds__(BS) void select_reg_kernel(const float *__restrict__ s_all, const void *__restrict__ a_all,
+                                                        int a_bf16, int64_t a_stride, int d, int k,
+                                                        int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                        int32_t *__restrict__ pad_all, int64_t ld_pad,
+                                                        float *__restrict__ aval) {
+    constexpr int NW = BS / 64;
+    constexpr int NB = 2048 / BS;
+    __shared__ int hist[2][2048];
+    __shared__ int wsum[5][NW];
+    __shared__ int found[3][3];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t b = blockIdx.x;
+
+    KeySource src;
+    src.s = s_all ? s_all + b * d : nullptr;
+    src.a = a_all ? (a_bf16 ? (const void *)(static_cast<const uint16_t *>(a_all) + b * a_stride)
+                            : (const void *)(static_cast<const float *>(a_all) + b * a_stride))
+                  : nullptr;
+    src.a_bf16 = a_bf16;
+    src.lds = nullptr;
+
+    const int j0 = tid * E;
+    const int nv = max(0, min(E, d - j0));
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = e < nv ? score_key(src.score(j0 + e)) : 0u;
+
+    for (int q = tid; q < 2048; q += BS) hist[0][q] = 0;
+    __syncthreads();
+
+    uint32_t prefix = 0, pmask = 0;
+    int rem = k;
+    const int shifts[3] = {21, 10, 0};
+    const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+#pragma unroll 1
+    for (int p = 0; p < 3; ++p) {
+        int *H = hist[p & 1];
+        if (p < 2)
+            for (int q = tid; q < 2048; q += BS) hist[(p + 1) & 1][q] = 0;
+        const int sh = shifts[p];
+        const uint32_t dm = dmasks[p];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (e < nv && (key[e] & pmask) == prefix) atomicAdd(&H[(key[e] >> sh) & dm], 1);
+        __syncthreads();
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < NB; ++e) c += H[2047 - (tid * NB + e)];
+        const int incl = wave_incl_scan(c);
+        if (lane == 63) wsum[p][w] = incl;
+        __syncthreads();
+        int before = incl - c;
+        for (int v = 0; v < w; ++v) before += wsum[p][v];
+        if (before < rem && before + c >= rem) {
+            int cum = before;
+            for (int e = 0; e < NB; ++e) {
+                const int bin = 2047 - (tid * NB + e);
+                const int h = H[bin];
+                if (cum + h >= rem) {
+                    found[p][0] = bin;
+                    found[p][1] = rem - cum;
+                    found[p][2] = h;
+                    break;
+                }
+                cum += h;
+            }
+        }
+        __syncthreads();
+        prefix |= uint32_t(found[p][0]) << sh;
+        pmask |= dm << sh;
+        rem = found[p][1];
+        if (found[p][2] == rem) break;  // every key left in this bin is kept
+    }
+
+    // compaction: masked key above prefix -> kept; equal -> first `rem` by index
+    int eq = 0, gt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (e < nv) {
+            const uint32_t mk = key[e] & pmask;
+            eq += mk == prefix;
+            gt += mk > prefix;
+        }
+    }
+    int incl = wave_incl_scan(eq);
+    if (lane == 63) wsum[3][w] = incl;
+    __syncthreads();
+    int eqb = incl - eq;
+    for (int v = 0; v < w; ++v) eqb += wsum[3][v];
+    const int sel = gt + max(0, min(eq, rem - eqb));
+    incl = wave_incl_scan(sel);
+    if (lane == 63) wsum[4][w] = incl;
+    __syncthreads();
+    int pos = incl - sel;
+    for (int v = 0; v < w; ++v) pos += wsum[4][v];
+
+    int32_t *idx = idx_all ? idx_all + b * ld_idx : nullptr;
+    int32_t *pad = pad_all ? pad_all + b * ld_pad : nullptr;
+    if (pad)
+        for (int64_t q = k + tid; q < ld_pad; q += BS) pad[q] = -1;
+    int er = eqb;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (e < nv) {
+            const uint32_t mk = key[e] & pmask;
+            bool take = mk > prefix;
+            if (mk == prefix) {
+                take = er < rem;
+                ++er;
+            }
+            if (take && pos < k) {
+                const int j = j0 + e;
+                if (idx) idx[pos] = j;
+                if (pad) pad[pos] = j;
+                if (aval) {
+                    aval[b * k + pos] = src.a_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(src.a)[j])
+                                                   : static_cast<const float *>(src.a)[j];
+                }
+                ++pos;
+            }
+        }
+    }
+}
+
+__global__ void iota_kernel(int32_t *idx, int64_t k, int64_t ld, int64_t total) {
     int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q < total) idx[q] = (int32_t)(q % k);
+    if (q < total) {
+        const int64_t t = q % ld;
+        idx[q] = t < k ? (int32_t)t : -1;
+    }
 }
 
 unsigned g_select_attr_done = 0;  // bit per device
@@ -338,8 +493,8 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
 
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
                                    hipStream_t stream) {
-    int64_t total = d * batch;
-    colnorm_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(part, chunks, d, total, s);
+    dim3 grid((unsigned)((d + 63) / 64), (unsigned)batch);
+    colnorm_finalize_kernel<<<grid, 256, 0, stream>>>(part, chunks, d, s);
     return hipGetLastError();
 }
 
@@ -347,33 +502,43 @@ hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d,
 static constexpr int64_t kSelectLdsKeys = 24576;
 
 hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, int64_t a_stride, int64_t batch,
-                         int64_t d, int64_t k, int32_t *idx, int64_t ld_idx, float *aval, hipStream_t stream) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (dev < 32 && !(g_select_attr_done & (1u << dev))) {
-        hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<1024>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kSelectLdsKeys * 4));
-        hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<256>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kSelectLdsKeys * 4));
-        if (e1 != hipSuccess) return e1;
-        if (e2 != hipSuccess) return e2;
-        g_select_attr_done |= 1u << dev;
-    }
-    const int use_lds = d <= kSelectLdsKeys;
-    const size_t lds = use_lds ? (size_t)d * 4 : 0;
+                         int64_t d, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad, int64_t ld_pad,
+                         float *aval, hipStream_t stream) {
     const int a_bf16 = a_dt == RMM_BF16;
-    if (d > 2048)
-        select_kernel<1024><<<(unsigned)batch, 1024, lds, stream>>>(s, a_src, a_bf16, a_stride, d, k, idx, ld_idx,
-                                                                   aval, use_lds);
-    else
-        select_kernel<256><<<(unsigned)batch, 256, lds, stream>>>(s, a_src, a_bf16, a_stride, d, k, idx, ld_idx,
-                                                                 aval, use_lds);
+    const unsigned g = (unsigned)batch;
+    if (d <= 256) {
+        select_reg_kernel<64, 4><<<g, 64, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
+                                                       idx_pad, ld_pad, aval);
+    } else if (d <= 4096) {
+        select_reg_kernel<256, 16><<<g, 256, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
+                                                          idx_pad, ld_pad, aval);
+    } else if (d <= 8192) {
+        select_reg_kernel<512, 16><<<g, 512, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
+                                                          idx_pad, ld_pad, aval);
+    } else if (d <= 16384) {
+        select_reg_kernel<1024, 16><<<g, 1024, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx,
+                                                            ld_idx, idx_pad, ld_pad, aval);
+    } else {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+        if (dev < 32 && !(g_select_attr_done & (1u << dev))) {
+            hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_big_kernel<1024>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                (int)(kSelectLdsKeys * 4));
+            if (e1 != hipSuccess) return e1;
+            g_select_attr_done |= 1u << dev;
+        }
+        const int use_lds = d <= kSelectLdsKeys;
+        const size_t lds = use_lds ? (size_t)d * 4 : 0;
+        select_big_kernel<1024><<<g, 1024, lds, stream>>>(s, a_src, a_bf16, a_stride, d, k, idx, ld_idx, idx_pad,
+                                                          ld_pad, aval, use_lds);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_iota(int32_t *idx, int64_t k, int64_t batch, hipStream_t stream) {
-    int64_t total = k * batch;
-    iota_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(idx, k, total);
+hipError_t launch_iota(int32_t *idx, int64_t k, int64_t ld, int64_t batch, hipStream_t stream) {
+    int64_t total = ld * batch;
+    iota_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(idx, k, ld, total);
     return hipGetLastError();
 }
 

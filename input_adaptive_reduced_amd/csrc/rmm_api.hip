@@ -140,6 +140,18 @@ rmm_status_t check_desc(const rmm_desc_t *ds, int64_t &extA, int64_t &extB, int6
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The MFMA route addresses each operand with 32-bit byte offsets from a
+// per-entry base (buffer loads); every operand extent must stay below 2^31.
+constexpr int64_t kMaxBufferBytes = 0x7fffffffLL;
+int64_t a_extent_bytes(const rmm_desc_t *ds) { return ((ds->n - 1) * ds->lda + ds->d) * 2; }
+int64_t b_extent_bytes(const rmm_desc_t *ds) {
+    return ds->transB ? ((ds->m - 1) * ds->ldb + ds->d) * 2 : ((ds->d - 1) * ds->ldb + ds->m) * 2;
+}
+bool mfma_extents_ok(const rmm_desc_t *ds, int64_t kpad) {
+    return a_extent_bytes(ds) < kMaxBufferBytes && b_extent_bytes(ds) < kMaxBufferBytes &&
+           ds->n * kpad * 2 < kMaxBufferBytes && ds->m * kpad * 2 < kMaxBufferBytes;
+}
+
 // Alignment-based part of the route choice; pointers may be null when only
 // sizing (then alignment is assumed, which can only over-size).
 Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, const void *Y) {
@@ -155,7 +167,7 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     if (bf && ptr_ok && ld_ok && ds->n == 1 && !ds->transB && ds->batch == 1) {
         p.route = ROUTE_DECODE;
         p.shortcut = false;  // the fused |a| selection also produces the kept values
-    } else if (bf && ptr_ok && ld_ok) {
+    } else if (bf && ptr_ok && ld_ok && mfma_extents_ok(ds, p.kpad)) {
         p.route = ROUTE_MFMA;
     } else {
         p.route = ROUTE_GENERIC;
@@ -174,7 +186,7 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
         p.off_part = take((size_t)p.cp.chunks * d * batch * 4);
         p.off_s = take((size_t)d * batch * 4);
     }
-    p.off_idx = take((size_t)k * batch * 4);
+    p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
     if (p.route == ROUTE_MFMA) {
         p.directA = p.shortcut && d % 64 == 0;
         if (!p.directA) p.off_Ap = take((size_t)batch * n * p.kpad * 2);
@@ -265,7 +277,8 @@ rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, in
 rmm_status_t rmm_select(const float *s, int64_t batch, int64_t d, int64_t k, int32_t *idx_out, hipStream_t stream) {
     if (!s || !idx_out || batch < 1 || batch > 65535 || d < 1 || d > INT32_MAX || k < 1 || k > d)
         return RMM_ERR_INVALID_ARG;
-    RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, nullptr, stream));
+    RMM_LAUNCH(RMM_KERNEL_SELECT,
+               launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, nullptr, 0, nullptr, stream));
     return RMM_OK;
 }
 
@@ -301,13 +314,14 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         return RMM_ERR_INVALID_ARG;
 
     const int64_t n = ds.n, d = ds.d, m = ds.m, batch = ds.batch;
-    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(ws + p.off_idx);
+    int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);  // padded: kpad per row
 
     if (p.route == ROUTE_DECODE) {
         float *aval = reinterpret_cast<float *>(ws + p.off_aval);
         float *gpart = reinterpret_cast<float *>(ws + p.off_gpart);
-        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(nullptr, A, RMM_BF16, 0, 1, d, k, idx, k, aval, stream));
-        RMM_LAUNCH(RMM_KERNEL_GEMV, launch_gemv_partial(static_cast<const uint16_t *>(B), ds.ldb, m, idx, aval, k,
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_select(nullptr, A, RMM_BF16, 0, 1, d, k, idx_out, k, pidx, p.kpad, aval, stream));
+        RMM_LAUNCH(RMM_KERNEL_GEMV, launch_gemv_partial(static_cast<const uint16_t *>(B), ds.ldb, m, pidx, aval, k,
                                                         p.gsplits, gpart, stream));
         RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(gpart, p.gsplits, 1, m, 1, ds.alpha,
                                                            static_cast<uint16_t *>(Y), ds.ldy, 0, stream));
@@ -315,9 +329,9 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     }
 
     // steps 1-2: scores and selection (or every index at rho = 1)
-    const int32_t *gemm_idx = idx;
+    const int32_t *gemm_idx = pidx;
     if (p.shortcut) {
-        if (idx_out) RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(idx_out, k, batch, stream));
+        if (idx_out) RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(idx_out, k, k, batch, stream));
         gemm_idx = nullptr;  // identity
     } else {
         float *part = reinterpret_cast<float *>(ws + p.off_part);
@@ -325,7 +339,8 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         RMM_LAUNCH(RMM_KERNEL_COLNORM,
                    launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
         RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, stream));
-        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx, k, nullptr, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, pidx, p.kpad, nullptr, stream));
     }
 
     if (p.route == ROUTE_GENERIC) {
@@ -340,7 +355,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         g.group = ds.b_group;
         g.transB = ds.transB;
         g.idx = gemm_idx;
-        g.ld_idx = k;
+        g.ld_idx = p.kpad;
         g.Y = Y;
         g.ldy = ds.ldy;
         g.strideY = ds.strideY;
@@ -363,12 +378,11 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     } else {
         uint16_t *Ap = reinterpret_cast<uint16_t *>(ws + p.off_Ap);
         if (p.shortcut) {
-            // identity gather: the pack needs an index list; reuse the workspace one
-            int32_t *iota = reinterpret_cast<int32_t *>(ws + p.off_idx);
-            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(iota, k, batch, stream));
-            gemm_idx = iota;
+            // identity gather: the pack reads an index list; write 0..k-1 into the workspace one
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(pidx, k, p.kpad, batch, stream));
+            gemm_idx = pidx;
         }
-        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(A, RMM_BF16, n, d, ds.lda, ds.strideA, 1, gemm_idx, k, k, p.kpad, Ap,
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(A, RMM_BF16, n, d, ds.lda, ds.strideA, 1, pidx, p.kpad, p.kpad, Ap,
                                                 n * p.kpad, batch, stream));
         g.A = Ap;
         g.lda = p.kpad;
@@ -376,13 +390,11 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     }
     if (ds.transB) {
         uint16_t *Bp = reinterpret_cast<uint16_t *>(ws + p.off_Bp);
-        const int32_t *bidx = gemm_idx;
-        if (!bidx) {
-            int32_t *iota = reinterpret_cast<int32_t *>(ws + p.off_idx);
-            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(iota, k, batch, stream));
-            bidx = iota;
+        if (!gemm_idx) {
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(pidx, k, p.kpad, batch, stream));
+            gemm_idx = pidx;
         }
-        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(B, RMM_BF16, m, d, ds.ldb, ds.strideB, ds.b_group, bidx, k, k,
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(B, RMM_BF16, m, d, ds.ldb, ds.strideB, ds.b_group, pidx, p.kpad,
                                                 p.kpad, Bp, m * p.kpad, batch, stream));
         g.B = Bp;
         g.ldb = p.kpad;
@@ -391,13 +403,17 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         g.bmode = 1;
         g.idx = nullptr;
     } else {
+        if (!gemm_idx) {  // rho = 1 shortcut: the kernel reads rows 0..k-1 from the list
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(pidx, k, p.kpad, batch, stream));
+            gemm_idx = pidx;
+        }
         g.B = static_cast<const uint16_t *>(B);
         g.ldb = ds.ldb;
         g.strideB = ds.strideB;
         g.group = ds.b_group;
         g.bmode = 0;
         g.idx = gemm_idx;
-        g.ld_idx = k;
+        g.ld_idx = p.kpad;
     }
     g.Y = static_cast<uint16_t *>(Y);
     g.ldy = ds.ldy;
@@ -406,6 +422,8 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     g.m = m;
     g.k = k;
     g.kpad = p.directA ? d : p.kpad;
+    g.a_bytes = p.directA ? a_extent_bytes(desc) : n * p.kpad * 2;
+    g.b_bytes = ds.transB ? m * p.kpad * 2 : b_extent_bytes(desc);
     g.batch = batch;
     g.alpha = ds.alpha;
     g.splits = p.gc.splits;

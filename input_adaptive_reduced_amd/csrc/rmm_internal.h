@@ -55,20 +55,23 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
                                    hipStream_t stream);
 
-// Exact TopK by radix select; idx[b][0..k) ascending.  When `a_src` is given
-// the scores are |a_j| of a single bf16/f32 row per batch entry (decode) and
-// `aval` receives a[idx[t]] as fp32.  `idx_pad` > k extends each row of idx
-// with -1 up to idx_pad entries (for kernels that read whole chunks).
+// Exact TopK by radix select; rows of idx (ld_idx apart) and of idx_pad
+// (ld_pad apart, entries k..ld_pad-1 set to -1) receive the kept indices in
+// ascending order; either may be null.  When `a_src` is given the scores are
+// |a_j| of a single bf16/f32 row per batch entry (decode) and `aval[b*k + t]`
+// receives a[idx[t]] as fp32.
 hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, int64_t a_stride, int64_t batch,
-                         int64_t d, int64_t k, int32_t *idx, int64_t ld_idx, float *aval, hipStream_t stream);
+                         int64_t d, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad, int64_t ld_pad,
+                         float *aval, hipStream_t stream);
 
-// dst[b][r][t] = src[b / group][r][idx[b][t]] for t < k, 0 for k <= t < kpad.
+// dst[b][r][t] = src[b / group][r][idx[b][t]] for t < kpad, 0 where idx[b][t]
+// is -1.  idx rows are ld_idx apart (a multiple of 64, 256-byte aligned).
 hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src,
-                       int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t k,
-                       int64_t kpad, void *dst, int64_t dst_stride, int64_t batch, hipStream_t stream);
+                       int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad,
+                       void *dst, int64_t dst_stride, int64_t batch, hipStream_t stream);
 
-// Iota index list 0..k-1 per batch entry (rho = 1 shortcut).
-hipError_t launch_iota(int32_t *idx, int64_t k, int64_t batch, hipStream_t stream);
+// Index rows 0..k-1 then -1 up to ld, per batch entry (rho = 1 shortcut).
+hipError_t launch_iota(int32_t *idx, int64_t k, int64_t ld, int64_t batch, hipStream_t stream);
 
 // bf16 MFMA GEMM  Y = alpha * Ap[:, 0:k] * Bsel  (see gemm.hip for operand modes).
 struct GemmArgs {
@@ -77,12 +80,14 @@ struct GemmArgs {
     const uint16_t *B;   // bmode 0: d x m row-major rows gathered by idx; bmode 1: m x k k-contiguous
     int64_t ldb, strideB;
     int64_t group;       // batch entries sharing one B (B + (b / group) * strideB)
-    const int32_t *idx;  // bmode 0: row list per entry (NULL = identity), ld_idx apart
+    const int32_t *idx;  // bmode 0: padded row list per entry (-1 beyond k), ld_idx apart
     int64_t ld_idx;
     uint16_t *Y;
     int64_t ldy, strideY;
     float *part;         // split-K fp32 partials [split][batch][n][m] (NULL = no split)
     int64_t n, m, k, kpad, batch;
+    int64_t a_bytes;     // bytes readable from each entry's A base (< 2^31)
+    int64_t b_bytes;     // bytes readable from each B base (< 2^31)
     int splits;
     int bmode;
     float alpha;
