@@ -50,24 +50,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
     return x.b;
 }
 
-// 8x8 transpose of 2-byte elements: in[r] holds row r (8 columns); out[c]
-// receives column c (8 rows).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint4 &x = in[2 * p];
-            const uint4 &y = in[2 * p + 1];
-            uint32_t xd = (c >> 1) == 0 ? x.x : (c >> 1) == 1 ? x.y : (c >> 1) == 2 ? x.z : x.w;
-            uint32_t yd = (c >> 1) == 0 ? y.x : (c >> 1) == 1 ? y.y : (c >> 1) == 2 ? y.z : y.w;
-            w[p] = (c & 1) ? ((xd >> 16) | (yd & 0xffff0000u)) : ((xd & 0xffffu) | (yd << 16));
-        }
-        out[c] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
 // Tile index -> (tm, tn): XCD-compact, then grouped by GM tile rows.
 __device__ __forceinline__ void tile_coords(int t, int T, int tiles_m, int tiles_n, int &tm, int &tn) {
     if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
@@ -96,20 +78,38 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// s_waitcnt vmcnt(0) (gfx9 encoding, other counters left unconstrained):
-// the next tile's loads must have landed before they are written to LDS.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// One workgroup computes a BM x BN output tile over a range of 64-wide K
+// steps (an even number of them).  Pipeline per step kt, with two LDS
+// buffers and two register staging sets:
+//   * issue the global (buffer) loads of tile kt+2 into staging set kt&1
+//     (gathered B rows are addressed by the index chunk loaded two steps
+//     earlier) and the index chunk of tile kt+4;
+//   * four k16 sub-steps of 16 MFMAs each on LDS buffer kt&1, the fragment
+//     reads of the next sub-step interleaved with the current MFMAs;
+//   * during sub-step 1, write staging set (kt+1)&1 (tile kt+1, loaded a
+//     full step earlier) into the other LDS buffer;
+//   * barrier after sub-step 2, so sub-step 3 can already read the first
+//     fragments of the next buffer.
+// LDS layouts: A (and packed B^T) rows of 64 bf16 in eight 16-byte chunks,
+// chunk c of row r at c ^ ((r ^ r>>3) & 7); gathered B rows stay row-major
+// (k rows of BN columns), chunk c of row k at c ^ 2(k & 3), and its MFMA
+// operand is read with ds_read_b64_tr_b16 (lane i of a 16-lane group reads 4
+// columns of row k0 + i/4; lane j receives 4 consecutive k of column j).
+// Both layouts keep reads and writes free of bank conflicts.
 template <int BM, int BN, int WM, int WN, int BMODE, bool SPLIT>
 __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
-    constexpr int NW = WM * WN;
-    constexpr int NT = NW * 64;
+    constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_PER = BM * 8 / NT;  // 16-byte chunks per thread per K step
-    constexpr int B_PER = BN * 8 / NT;  // bmode 1
+    constexpr int A_PER = BM * 8 / NT;   // A chunks per thread per step
+    constexpr int B_PER = BMODE == 0 ? 8 : BN * 8 / NT;
+    constexpr int CPR = BN / 8;          // 16-byte chunks per row-major B row
+    constexpr int B_READS = BMODE == 0 ? 2 * FN : FN;
     static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
-    static_assert(BMODE == 1 || BN <= NT, "bmode 0 needs one 8x8 B block per thread at most");
+    static_assert(BMODE == 1 || BN * 8 == NT * 8 || BN < NT, "bmode 0: one 8-row B block per thread");
 
     __shared__ uint4 sA[2][BM * 8];
     __shared__ uint4 sB[2][BN * 8];
@@ -131,13 +131,15 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (b / g.group) * g.strideB, g.b_bytes);
     const int32_t *idx = BMODE == 0 ? g.idx + b * g.ld_idx : nullptr;
 
+    // K steps of this split: an even count (kpad is a multiple of 128 and
+    // the per-split share is rounded up to even).
     const int KT = (int)(g.kpad / BK);
-    const int per = (KT + g.splits - 1) / g.splits;
+    const int per = ((KT + g.splits - 1) / g.splits + 1) & ~1;
     const int kt0 = split * per;
     const int kt1 = min(KT, kt0 + per);
 
-    // Staged chunk assignment: chunk c = tid + i*NT is row c/8, logical
-    // 16-byte chunk c%8 of the tile row; rows past n (or m) read as zero.
+    // A (and bmode-1 B) staging: chunk c = tid + i*NT is tile row c/8, logical
+    // 16-byte chunk c%8; rows past n (or m) read as zero.
     uint32_t aoff[A_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
@@ -154,37 +156,28 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
             boff[i] = gr < g.m ? (uint32_t)((gr * g.ldb + (c & 7) * 8) * 2) : kOob;
         }
     }
-    // bmode 0: thread owns the 8x8 block (k rows kq*8.., columns nc*8..)
-    const bool bthr = BMODE == 0 && (BN == NT || tid < BN);
-    const int kq = tid / (BN / 8), nc = tid % (BN / 8);
+    // bmode 0: thread owns 8 consecutive B rows (kq*8..) of one 16-byte column chunk nc
+    const bool bthr = BMODE == 0 && (BN * 8 >= NT * 8 ? true : tid < BN);
+    const int kq = tid / CPR, nc = tid % CPR;
     const int64_t bcol = n0 + nc * 8;
 
-    uint4 ra[A_PER];
-    uint4 rb[BMODE == 0 ? 8 : B_PER];
+    uint4 ra0[A_PER], ra1[A_PER], rb0[B_PER], rb1[B_PER];
+    int32_t ix0[8], ix1[8];
 
-    // Kept row numbers of B for one K step (8 per thread); -1 marks padding.
     auto load_idx = [&](int kt, int32_t (&o)[8]) {
-        if (!bthr) return;
-        const int t0 = min(kt, KT - 1) * BK + kq * 8;
-        const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0);
-        const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + 4);
-        o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
-        o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
-    };
-    auto load_a = [&](int kt) {
-        const uint32_t ko = (uint32_t)kt * (BK * 2);
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) ra[i] = buf_load16(rA, aoff[i] + ko);
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int c = tid + i * NT;
-            const int r = c >> 3, ch = c & 7;
-            sA[buf][r * 8 + swz(r, ch)] = ra[i];
+        if constexpr (BMODE == 0) {
+            if (!bthr) return;
+            const int t0 = min(kt, KT - 1) * BK + kq * 8;
+            const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0);
+            const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + 4);
+            o[0] = p0.x; o[1] = p0.y; o[2] = p0.z; o[3] = p0.w;
+            o[4] = p1.x; o[5] = p1.y; o[6] = p1.z; o[7] = p1.w;
         }
     };
-    auto load_b = [&](int kt, const int32_t (&ix)[8]) {
+    auto load_tile = [&](int kt, uint4 (&ra)[A_PER], uint4 (&rb)[B_PER], const int32_t (&ix)[8]) {
+        const uint32_t ko = (uint32_t)min(kt, kt1 - 1) * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) ra[i] = buf_load16(rA, aoff[i] + ko);
         if constexpr (BMODE == 0) {
             if (bthr) {
 #pragma unroll
@@ -194,20 +187,23 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
                 }
             }
         } else {
-            const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
             for (int i = 0; i < B_PER; ++i) rb[i] = buf_load16(rB, boff[i] + ko);
         }
     };
-    auto store_b = [&](int buf) {
+    auto store_tile = [&](int buf, const uint4 (&ra)[A_PER], const uint4 (&rb)[B_PER]) {
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            const int c = tid + i * NT;
+            const int r = c >> 3, ch = c & 7;
+            sA[buf][r * 8 + swz(r, ch)] = ra[i];
+        }
         if constexpr (BMODE == 0) {
             if (bthr) {
-                uint4 ob[8];
-                transpose8x8(rb, ob);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const int nn = nc * 8 + c;
-                    sB[buf][nn * 8 + swz(nn, kq)] = ob[c];
+                for (int r = 0; r < 8; ++r) {
+                    const int k = kq * 8 + r;
+                    sB[buf][k * CPR + (nc ^ ((k & 3) << 1))] = rb[r];
                 }
             }
         } else {
@@ -235,52 +231,75 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
             const int r = wm * WTM + i * 32 + (lane & 31);
             fa[i] = as_bf16x8(sA[buf][r * 8 + swz(r, ch)]);
         }
+        if constexpr (BMODE == 0) {
+            const int gq = lane >> 4, li = lane & 15;
+            const int kbase = ks * 16 + 8 * (gq >> 1) + (li >> 2);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int nn = wn * WTN + j * 32 + (lane & 31);
-            fb[j] = as_bf16x8(sB[buf][nn * 8 + swz(nn, ch)]);
+            for (int j = 0; j < FN; ++j) {
+                const int nn = wn * WTN + j * 32 + 16 * (gq & 1) + 4 * (li & 3);
+                union {
+                    v4i16_t h[2];
+                    bf16x8_t v;
+                } u;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k = kbase + 4 * hh;
+                    const char *p = reinterpret_cast<const char *>(&sB[buf][k * CPR + ((nn >> 3) ^ ((k & 3) << 1))]) +
+                                    ((nn >> 2) & 1) * 8;
+                    u.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
+                }
+                fb[j] = u.v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nn = wn * WTN + j * 32 + (lane & 31);
+                fb[j] = as_bf16x8(sB[buf][nn * 8 + swz(nn, ch)]);
+            }
         }
     };
 
-    // K loop on two LDS buffers.  Step kt contracts buffer `cur` while the
-    // next tile's loads are in flight into registers (gathered B rows are
-    // addressed by the row list loaded one step earlier, and the row list of
-    // step kt+2 is fetched), then publishes the next tile into buffer cur^1.
-    // Every step ends with vmcnt(0): nothing is in flight across the
-    // back-edge, so the compiler needs no conservative waits at the loop
-    // head.  The final step fetches a clamped tile that nobody reads.
-    if (kt0 < kt1) {
-        int32_t ixn[8];
-        load_idx(kt0, ixn);
-        load_a(kt0);
-        load_b(kt0, ixn);
-        load_idx(kt0 + 1, ixn);
-        wait_vm0();
-        store_a(0);
-        store_b(0);
-        __syncthreads();
-        for (int kt = kt0; kt < kt1; ++kt) {
-            const int cur = (kt - kt0) & 1;
-            const int ktn = min(kt + 1, kt1 - 1);
-            load_a(ktn);
-            load_b(ktn, ixn);  // rows of step kt+1
-            load_idx(kt + 2, ixn);
+    bf16x8_t fa[2][FM], fb[2][FN];
+    auto step = [&](int kt, int buf, uint4 (&la)[A_PER], uint4 (&lb)[B_PER], int32_t (&lix)[8],
+                    const uint4 (&sa)[A_PER], const uint4 (&sb)[B_PER]) {
+        load_tile(kt + 2, la, lb, lix);
+        load_idx(kt + 4, lix);
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8_t fa[FM], fb[FN];
-                read_frags(cur, ks, fa, fb);
-                // operands swapped: each lane ends up holding four consecutive
-                // output columns of one output row
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            if (ks + 1 < BK / 16) read_frags(buf, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+            else read_frags(buf ^ 1, 0, fa[0], fb[0]);
+            if (ks == 1) store_tile(buf ^ 1, sa, sb);
+            // operands swapped: each lane ends up holding four consecutive
+            // output columns of one output row
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+            // spread the fragment reads over the MFMAs of this sub-step
+#pragma unroll
+            for (int q = 0; q < FM + B_READS; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, FM * FN >= 2 * (FM + B_READS) ? 2 : 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            wait_vm0();
-            store_a(cur ^ 1);
-            store_b(cur ^ 1);
-            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == 2) __syncthreads();
+        }
+    };
+
+    if (kt0 < kt1) {
+        load_idx(kt0, ix0);
+        load_idx(kt0 + 1, ix1);
+        load_tile(kt0, ra0, rb0, ix0);
+        load_tile(kt0 + 1, ra1, rb1, ix1);
+        load_idx(kt0 + 2, ix0);
+        load_idx(kt0 + 3, ix1);
+        store_tile(0, ra0, rb0);
+        __syncthreads();
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            step(kt, 0, ra0, rb0, ix0, ra1, rb1);      // tile kt on buffer 0; tile kt+1 -> buffer 1
+            step(kt + 1, 1, ra1, rb1, ix1, ra0, rb0);  // tile kt+1 on buffer 1; tile kt+2 -> buffer 0
         }
     }
 

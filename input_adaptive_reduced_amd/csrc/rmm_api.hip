@@ -158,7 +158,9 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     Plan p;
     memset(&p, 0, sizeof(p));
     p.k = k;
-    p.kpad = (k + 63) / 64 * 64;
+    // The MFMA kernel runs an even number of 64-wide K steps; the padded
+    // columns of packed operands are zero and padded index entries are -1.
+    p.kpad = (k + 127) / 128 * 128;
     p.shortcut = (k == ds->d) && !(ds->flags & RMM_FLAG_FULL_PATH);
     const bool bf = ds->dtype == RMM_BF16;
     const bool ptr_ok = (!A || aligned16(A)) && (!B || aligned16(B)) && (!Y || aligned16(Y));
@@ -188,7 +190,7 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     }
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
     if (p.route == ROUTE_MFMA) {
-        p.directA = p.shortcut && d % 64 == 0;
+        p.directA = p.shortcut && d % 128 == 0;
         if (!p.directA) p.off_Ap = take((size_t)batch * n * p.kpad * 2);
         if (ds->transB) p.off_Bp = take((size_t)batch * m * p.kpad * 2);
         p.gc = gemm_choose(n, m, k, batch);
