@@ -101,7 +101,8 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 // Both layouts keep reads and writes free of bank conflicts.
 template <int BM, int BN, int WM, int WN, int BMODE, bool SPLIT>
 __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;
+    constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int A_PER = BM * 8 / NT;   // A chunks per thread per step
@@ -305,27 +306,63 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
 
     // epilogue: lane l, registers 4q..4q+3 of block (i, j) hold output row
     // i*32 + l%32 and columns j*32 + 8q + 4(l/32) + 0..3.
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
-        if (row >= g.n) continue;
+        for (int i = 0; i < FM; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+            if (row >= g.n) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
-                if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
-                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                if constexpr (SPLIT) {
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                    if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
                     *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m + col) =
-                        make_float4(v0, v1, v2, v3);
-                } else {
-                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * v0)) | (uint32_t(f32_to_bf16(g.alpha * v1)) << 16);
-                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * v2)) | (uint32_t(f32_to_bf16(g.alpha * v3)) << 16);
-                    *reinterpret_cast<uint2 *>(g.Y + b * g.strideY + row * g.ldy + col) = make_uint2(lo, hi);
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                 }
             }
+        }
+    } else {
+        // bf16 results go through LDS so every global store is a full
+        // 16-byte piece of a row and each 16-lane group writes a contiguous
+        // 256-byte row segment.  Each wave stages its WTM x WTN block in its
+        // own LDS region (rows of WTN*2 bytes, 16-byte chunk c of row r at
+        // c ^ (r % CPW)), which is free of bank conflicts for both passes.
+        constexpr int CPW = WTN / 8;  // 16-byte chunks per staged row
+        static_assert(WTM * WTN * 2 * NW <= (int)sizeof(sA) + (int)sizeof(sB), "staging does not fit");
+        static_assert((CPW & (CPW - 1)) == 0, "chunks per row must be a power of two");
+        __syncthreads();  // every wave is done reading the operand tiles
+        uint4 *stage = (wave * WTM * CPW < 2 * BM * 8) ? &sA[0][0] + wave * WTM * CPW
+                                                      : &sB[0][0] + (wave * WTM * CPW - 2 * BM * 8);
+        char *st = reinterpret_cast<char *>(stage);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c4 = j * 8 + q * 2 + (lane >> 5);  // 4-column group within the wave row
+                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q])) |
+                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 1])) << 16);
+                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 2])) |
+                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 3])) << 16);
+                    const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
+                    *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        constexpr int RPI = 64 / CPW;  // rows per pass of the wave
+#pragma unroll 4
+        for (int it = 0; it < WTM / RPI; ++it) {
+            const int r = it * RPI + lane / CPW;
+            const int c = lane % CPW;
+            const uint4 v = stage[r * CPW + (c ^ (r & (CPW - 1)))];
+            const int64_t row = m0 + wm * WTM + r;
+            const int64_t col = n0 + wn * WTN + c * 8;
+            if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(g.Y + b * g.strideY + row * g.ldy + col) = v;
         }
     }
 }
@@ -502,6 +539,13 @@ GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch) {
     GemmConfig c;
     const int64_t big = ((n + 255) / 256) * ((m + 255) / 256) * batch;
     const int64_t ksteps = (k + BK - 1) / BK;
+    if (ksteps <= 4) {
+        // short contractions are bound by writing Y: 128x128 tiles (64 KB of
+        // LDS) let two workgroups share a CU and overlap stores with MFMAs
+        c.tile = 1;
+        c.splits = 1;
+        return c;
+    }
     if (big >= 192) {
         c.tile = 0;
         c.splits = 1;

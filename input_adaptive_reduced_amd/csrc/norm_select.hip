@@ -57,11 +57,14 @@ struct Vec16<float> {
 };
 
 // grid: (strips, chunks, batch); block: kNormThreads = tc column-lanes x tr row-lanes.
+// `counter` (one per batch entry, may be null) is cleared here for the
+// finalize kernel that follows in the same stream.
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *__restrict__ A, int64_t n, int64_t d,
                                                                        int64_t lda, int64_t strideA, int tc,
                                                                        int64_t rows_per_chunk, int vec_ok,
-                                                                       float *__restrict__ part) {
+                                                                       float *__restrict__ part,
+                                                                       unsigned *__restrict__ counter) {
     constexpr int V = Vec16<T>::N;
     __shared__ float red[kNormThreads * V];
     const int tid = threadIdx.x;
@@ -71,6 +74,7 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r1 = min(n, r0 + rows_per_chunk);
     const T *Ab = A + b * strideA;
+    if (counter && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) counter[b] = 0u;
 
     float acc[V];
 #pragma unroll
@@ -118,33 +122,6 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
         int64_t j = (int64_t)blockIdx.x * cols + c;
         if (j < d) part[(b * gridDim.y + blockIdx.y) * d + j] = sum;
     }
-}
-
-// 64 columns per workgroup; four row-chunk groups per column, each summing
-// every fourth chunk in ascending order (four loads in flight), then combined
-// as ((g0 + g1) + g2) + g3.
-__global__ __launch_bounds__(256) void colnorm_finalize_kernel(const float *__restrict__ part, int64_t chunks,
-                                                               int64_t d, float *__restrict__ s) {
-    __shared__ float red[4][64];
-    const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
-    const int64_t b = blockIdx.y;
-    const int64_t j = (int64_t)blockIdx.x * 64 + c;
-    float sum = 0.f;
-    if (j < d) {
-        const float *p = part + b * chunks * d + j;
-        int64_t r = g;
-        for (; r + 12 < chunks; r += 16) {
-            const float v0 = p[r * d], v1 = p[(r + 4) * d], v2 = p[(r + 8) * d], v3 = p[(r + 12) * d];
-            sum += v0;
-            sum += v1;
-            sum += v2;
-            sum += v3;
-        }
-        for (; r < chunks; r += 4) sum += p[r * d];
-    }
-    red[g][c] = sum;
-    __syncthreads();
-    if (g == 0 && j < d) s[b * d + j] = __fsqrt_rn(((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
 }
 
 // ------------------------------------------------------------------ block scan
@@ -312,97 +289,150 @@ __global__ __launch_bounds__(BS) void select_big_kernel(const float *__restrict_
     }
 }
 
-// Register-resident exact TopK for d <= BS * E: thread t owns the contiguous
-// scores [t*E, t*E + E).  Three radix passes over 11/11/10-bit digits of the
-// order-preserving key, each: LDS histogram (ping-pong buffers, so the next
-// one is cleared while this one fills), per-thread bin sums from the top, a
-// wave scan plus wave totals to find the digit holding the k-th largest key.
-// The passes stop early once the digit's bin holds exactly the keys still
-// needed.  Compaction in ascending index order keeps every key whose resolved
-// prefix is larger and the lowest-indexed keys whose prefix equals it.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+// ------------------------------------------------------------------ wave helpers (DPP)
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then row broadcasts of lane 15 and lane 31.
+__device__ __forceinline__ int wave_incl_add(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+    return x;
+}
+// Maximum over the wave (same shift pattern; lane 63 holds the result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+template <int BS>
+struct SelectShared {
+    int hist[2][2048];
+    int wsum[4][BS / 64];
+    uint32_t wmax[2][BS / 64];
+    uint32_t wlow[BS / 64];
+    int found[4][3];
+};
+
+// Bitwise OR over the wave (lane 63 holds the result).
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t x) {
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
     return x;
 }
 
+// Exact TopK of the keys held by a workgroup: thread t owns keys
+// [t*E, t*E + nv) (nv <= E, order-preserving keys of the scores).  Keeps the
+// k largest, ties to the lower index, and writes them in ascending order to
+// idx (when given), pad (when given; entries k..ld_pad-1 become -1) and, for
+// a decode row, their activation values to aval.
+//  * min and max of the keys fix the highest bit where keys differ, so the
+//    first 11-bit radix digit starts there and spreads the keys over the 2048
+//    LDS bins (no pile-up of atomics on a few bins);
+//  * each pass: histogram (ping-pong buffers: the next one is cleared while
+//    this one fills), per-thread bin sums from the top, DPP wave scan plus
+//    wave totals locate the bin holding the k-th largest key; passes stop
+//    once that bin holds exactly the keys still needed;
+//  * compaction: one packed block scan of (larger, equal) counts gives each
+//    thread its output position and the number of equal keys before it.
 template <int BS, int E>
-__global__ __launch_bounds__(BS) void select_reg_kernel(const float *__restrict__ s_all, const void *__restrict__ a_all,
-                                                        int a_bf16, int64_t a_stride, int d, int k,
-                                                        int32_t *__restrict__ idx_all, int64_t ld_idx,
-                                                        int32_t *__restrict__ pad_all, int64_t ld_pad,
-                                                        float *__restrict__ aval) {
+__device__ void block_select(SelectShared<BS> &sh, const uint32_t (&key)[E], int nv, int j0, int k,
+                             int32_t *__restrict__ idx, int32_t *__restrict__ pad, int64_t ld_pad,
+                             float *__restrict__ aval, const float (&vals)[E], int32_t *out_idx,
+                             float *out_val) {
     constexpr int NW = BS / 64;
     constexpr int NB = 2048 / BS;
-    __shared__ int hist[2][2048];
-    __shared__ int wsum[5][NW];
-    __shared__ int found[3][3];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t b = blockIdx.x;
 
-    KeySource src;
-    src.s = s_all ? s_all + b * d : nullptr;
-    src.a = a_all ? (a_bf16 ? (const void *)(static_cast<const uint16_t *>(a_all) + b * a_stride)
-                            : (const void *)(static_cast<const float *>(a_all) + b * a_stride))
-                  : nullptr;
-    src.a_bf16 = a_bf16;
-    src.lds = nullptr;
-
-    const int j0 = tid * E;
-    const int nv = max(0, min(E, d - j0));
-    uint32_t key[E];
+    // extent of the keys: max, min, and the lowest bit any key has set (bits
+    // below it are zero in every key and never need resolving; bf16 scores
+    // leave the low 16 bits clear)
+    uint32_t kmax = 0u, kmin = 0xffffffffu, kor = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = e < nv ? score_key(src.score(j0 + e)) : 0u;
-
-    for (int q = tid; q < 2048; q += BS) hist[0][q] = 0;
-    __syncthreads();
-
-    uint32_t prefix = 0, pmask = 0;
-    int rem = k;
-    const int shifts[3] = {21, 10, 0};
-    const uint32_t dmasks[3] = {0x7ffu, 0x7ffu, 0x3ffu};
-#pragma unroll 1
-    for (int p = 0; p < 3; ++p) {
-        int *H = hist[p & 1];
-        if (p < 2)
-            for (int q = tid; q < 2048; q += BS) hist[(p + 1) & 1][q] = 0;
-        const int sh = shifts[p];
-        const uint32_t dm = dmasks[p];
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            if (e < nv && (key[e] & pmask) == prefix) atomicAdd(&H[(key[e] >> sh) & dm], 1);
-        __syncthreads();
-        int c = 0;
-#pragma unroll
-        for (int e = 0; e < NB; ++e) c += H[2047 - (tid * NB + e)];
-        const int incl = wave_incl_scan(c);
-        if (lane == 63) wsum[p][w] = incl;
-        __syncthreads();
-        int before = incl - c;
-        for (int v = 0; v < w; ++v) before += wsum[p][v];
-        if (before < rem && before + c >= rem) {
-            int cum = before;
-            for (int e = 0; e < NB; ++e) {
-                const int bin = 2047 - (tid * NB + e);
-                const int h = H[bin];
-                if (cum + h >= rem) {
-                    found[p][0] = bin;
-                    found[p][1] = rem - cum;
-                    found[p][2] = h;
-                    break;
-                }
-                cum += h;
-            }
+    for (int e = 0; e < E; ++e)
+        if (e < nv) {
+            kmax = max(kmax, key[e]);
+            kmin = min(kmin, key[e]);
+            kor |= key[e];
         }
-        __syncthreads();
-        prefix |= uint32_t(found[p][0]) << sh;
-        pmask |= dm << sh;
-        rem = found[p][1];
-        if (found[p][2] == rem) break;  // every key left in this bin is kept
+    kmax = wave_max_u32(kmax);
+    kmin = ~wave_max_u32(~kmin);
+    if (lane == 0) {
+        sh.wmax[0][w] = kmax;
+        sh.wmax[1][w] = ~kmin;
+        sh.wlow[w] = __builtin_amdgcn_readlane((int)wave_or_u32(kor), 63);
+    }
+    for (int q = tid; q < 2048; q += BS) sh.hist[0][q] = 0;
+    __syncthreads();
+    kmax = 0u;
+    uint32_t nmin = 0u, allor = 0u;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        kmax = max(kmax, sh.wmax[0][v]);
+        nmin = max(nmin, sh.wmax[1][v]);
+        allor |= sh.wlow[v];
+    }
+    kmin = ~nmin;
+    const int zbits = allor ? __builtin_ctz(allor) : 0;  // bits below are zero in every key
+
+    uint32_t prefix = kmax, pmask = 0xffffffffu;
+    int rem = k;
+    if (kmin != kmax) {
+        const int hb = 31 - __builtin_clz(kmin ^ kmax);  // highest differing bit
+        pmask = hb >= 31 ? 0u : (0xffffffffu << (hb + 1));
+        prefix = kmax & pmask;
+        int lo = hb + 1;  // bits below `lo` are still unresolved
+#pragma unroll 1
+        for (int p = 0; lo > zbits; ++p) {
+            const int width = lo - zbits >= 11 ? 11 : lo - zbits;
+            const int sh_ = lo - width;
+            const uint32_t dm = (1u << width) - 1u;
+            int *H = sh.hist[p & 1];
+            for (int q = tid; q < 2048; q += BS) sh.hist[(p + 1) & 1][q] = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (e < nv && (key[e] & pmask) == prefix) atomicAdd(&H[(key[e] >> sh_) & dm], 1);
+            __syncthreads();
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < NB; ++e) c += H[2047 - (tid * NB + e)];
+            const int incl = wave_incl_add(c);
+            if (lane == 63) sh.wsum[p & 1][w] = incl;
+            __syncthreads();
+            int before = incl - c;
+            for (int v = 0; v < w; ++v) before += sh.wsum[p & 1][v];
+            if (before < rem && before + c >= rem) {
+                int cum = before;
+                for (int e = 0; e < NB; ++e) {
+                    const int bin = 2047 - (tid * NB + e);
+                    const int h = H[bin];
+                    if (cum + h >= rem) {
+                        sh.found[p & 3][0] = bin;
+                        sh.found[p & 3][1] = rem - cum;
+                        sh.found[p & 3][2] = h;
+                        break;
+                    }
+                    cum += h;
+                }
+            }
+            __syncthreads();
+            prefix |= uint32_t(sh.found[p & 3][0]) << sh_;
+            pmask |= dm << sh_;
+            rem = sh.found[p & 3][1];
+            lo = sh_;
+            if (sh.found[p & 3][2] == rem) break;  // every key left in this bin is kept
+        }
     }
 
     // compaction: masked key above prefix -> kept; equal -> first `rem` by index
@@ -415,23 +445,17 @@ __global__ __launch_bounds__(BS) void select_reg_kernel(const float *__restrict_
             gt += mk > prefix;
         }
     }
-    int incl = wave_incl_scan(eq);
-    if (lane == 63) wsum[3][w] = incl;
+    const int packed = (gt << 16) | eq;  // counts < 2^16 (d <= 16384 on this path)
+    const int incl = wave_incl_add(packed);
+    if (lane == 63) sh.wsum[2][w] = incl;
     __syncthreads();
-    int eqb = incl - eq;
-    for (int v = 0; v < w; ++v) eqb += wsum[3][v];
-    const int sel = gt + max(0, min(eq, rem - eqb));
-    incl = wave_incl_scan(sel);
-    if (lane == 63) wsum[4][w] = incl;
-    __syncthreads();
-    int pos = incl - sel;
-    for (int v = 0; v < w; ++v) pos += wsum[4][v];
-
-    int32_t *idx = idx_all ? idx_all + b * ld_idx : nullptr;
-    int32_t *pad = pad_all ? pad_all + b * ld_pad : nullptr;
-    if (pad)
-        for (int64_t q = k + tid; q < ld_pad; q += BS) pad[q] = -1;
-    int er = eqb;
+    int exclusive = incl - packed;
+    for (int v = 0; v < w; ++v) exclusive += sh.wsum[2][v];
+    const int gt_before = exclusive >> 16, eq_before = exclusive & 0xffff;
+    int pos = gt_before + min(eq_before, rem);
+    // the kept indices (and values) land in LDS in output order first, then
+    // the whole workgroup copies them out with contiguous stores
+    int er = eq_before;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if (e < nv) {
@@ -442,17 +466,147 @@ __global__ __launch_bounds__(BS) void select_reg_kernel(const float *__restrict_
                 ++er;
             }
             if (take && pos < k) {
-                const int j = j0 + e;
-                if (idx) idx[pos] = j;
-                if (pad) pad[pos] = j;
-                if (aval) {
-                    aval[b * k + pos] = src.a_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(src.a)[j])
-                                                   : static_cast<const float *>(src.a)[j];
-                }
+                out_idx[pos] = j0 + e;
+                if (aval) out_val[pos] = vals[e];
                 ++pos;
             }
         }
     }
+    __syncthreads();
+    for (int q = tid; q < k; q += BS) {
+        const int32_t v = out_idx[q];
+        if (idx) idx[q] = v;
+        if (pad) pad[q] = v;
+        if (aval) aval[q] = out_val[q];
+    }
+    if (pad)
+        for (int64_t q = k + tid; q < ld_pad; q += BS) pad[q] = -1;
+}
+
+// Raw 32-bit / 16-bit buffer loads (out-of-range offsets read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int32_t)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+}
+
+// Selection per batch entry from a score vector (ROW_BF16 = false: fp32
+// scores s) or from a single bf16 activation row (ROW_BF16 = true: score
+// |a_j|, the column norm of a one-row block; the kept values a[I_t] go to
+// aval).  All loads are issued up front, unconditionally, so their
+// latencies overlap.
+template <int BS, int E, bool ROW_BF16, bool VEC>
+__global__ __launch_bounds__(BS) void select_kernel(const void *__restrict__ src_all, int64_t stride, int d, int k,
+                                                    int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                    int32_t *__restrict__ pad_all, int64_t ld_pad,
+                                                    float *__restrict__ aval_all) {
+    __shared__ SelectShared<BS> sh;
+    extern __shared__ int32_t sel_out[];  // k indices, then k values when aval is requested
+    const int64_t b = blockIdx.x;
+    constexpr int ESZ = ROW_BF16 ? 2 : 4;
+    const char *base = static_cast<const char *>(src_all) + b * stride * ESZ;
+    const __amdgpu_buffer_rsrc_t r = sel_rsrc(base, (int64_t)d * ESZ);
+    const int j0 = threadIdx.x * E;
+    const int nv = max(0, min(E, d - j0));
+    float vals[E];
+    if constexpr (VEC) {
+        // E consecutive values per thread in 16-byte pieces (base 16-byte aligned)
+        constexpr int PER = 16 / ESZ;
+        static_assert(E % PER == 0, "");
+#pragma unroll
+        for (int q = 0; q < E / PER; ++q) {
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         r, (uint32_t)(j0 + q * PER) * ESZ, 0, 0));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if constexpr (ROW_BF16) {
+                    vals[q * PER + 2 * h] = __uint_as_float(w[h] << 16);
+                    vals[q * PER + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+                } else {
+                    vals[q * PER + h] = __uint_as_float(w[h]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t off = (uint32_t)(j0 + e) * ESZ;
+            if constexpr (ROW_BF16)
+                vals[e] = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+            else
+                vals[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+        }
+    }
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = score_key(ROW_BF16 ? fabsf(vals[e]) : vals[e]);
+    block_select<BS, E>(sh, key, nv, j0, k, idx_all ? idx_all + b * ld_idx : nullptr,
+                        pad_all ? pad_all + b * ld_pad : nullptr, ld_pad, aval_all ? aval_all + b * k : nullptr, vals,
+                        sel_out, reinterpret_cast<float *>(sel_out + k));
+}
+
+// Final column norms, and (with `counter`) the selection in the same launch.
+// 64 columns per workgroup, 16 row-chunk groups per column: group g sums the
+// chunks g, g+16, ... in ascending order (four loads in flight), the 16 group
+// sums are added in a fixed tree order, then a correctly rounded sqrt.  Each
+// workgroup then publishes its norms and takes a ticket; the last workgroup of
+// a batch entry (all norms visible after the fence) runs the exact TopK over
+// all d scores.  The counter is cleared by the column-norm kernel that runs
+// before this one in the same stream.
+__global__ __launch_bounds__(1024) void finalize_select_kernel(const float *__restrict__ part, int64_t chunks, int d,
+                                                                float *__restrict__ s_all, unsigned *__restrict__ counter,
+                                                                int k, int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                                int32_t *__restrict__ pad_all, int64_t ld_pad) {
+    extern __shared__ int32_t sel_out[];
+    __shared__ float red[16][64];
+    __shared__ SelectShared<1024> sh;
+    __shared__ int last;
+    const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int64_t b = blockIdx.y;
+    const int64_t j = (int64_t)blockIdx.x * 64 + c;
+    float *s = s_all + b * d;
+    float sum = 0.f;
+    if (j < d) {
+        const float *p = part + b * chunks * d + j;
+        int64_t r = g;
+        for (; r + 48 < chunks; r += 64) {
+            const float v0 = p[r * d], v1 = p[(r + 16) * d], v2 = p[(r + 32) * d], v3 = p[(r + 48) * d];
+            sum += v0;
+            sum += v1;
+            sum += v2;
+            sum += v3;
+        }
+        for (; r < chunks; r += 16) sum += p[r * d];
+    }
+    red[g][c] = sum;
+    __syncthreads();
+    if (g == 0 && j < d) {
+        float t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t[q] = red[2 * q][c] + red[2 * q + 1][c];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = t[2 * q] + t[2 * q + 1];
+        s[j] = __fsqrt_rn((t[0] + t[1]) + (t[2] + t[3]));
+    }
+    if (!counter) return;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last = atomicAdd(&counter[b], 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    constexpr int E = 16;  // d <= 16384 on this path
+    const int j0 = threadIdx.x * E;
+    const int nv = max(0, min(E, d - j0));
+    uint32_t key[E];
+    float vals[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        vals[e] = e < nv ? __builtin_nontemporal_load(&s[j0 + e]) : 0.f;
+        key[e] = score_key(vals[e]);
+    }
+    block_select<1024, E>(sh, key, nv, j0, k, idx_all ? idx_all + b * ld_idx : nullptr,
+                          pad_all ? pad_all + b * ld_pad : nullptr, ld_pad, nullptr, vals, sel_out, nullptr);
 }
 
 __global__ void iota_kernel(int32_t *idx, int64_t k, int64_t ld, int64_t total) {
@@ -489,24 +643,27 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch) {
 }
 
 hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda, int64_t batch,
-                                  int64_t strideA, const ColnormPlan &p, float *part, hipStream_t stream) {
+                                  int64_t strideA, const ColnormPlan &p, float *part, unsigned *counter,
+                                  hipStream_t stream) {
     dim3 grid(p.strips, p.chunks, (unsigned)batch);
     const int esz = dt == RMM_BF16 ? 2 : 4;
     const int V = 16 / esz;
     const int vec_ok = ((uintptr_t)A % 16 == 0) && (lda % V == 0) && (batch == 1 || strideA % V == 0);
     if (dt == RMM_BF16)
         colnorm_partial_kernel<uint16_t><<<grid, kNormThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part);
+            static_cast<const uint16_t *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part, counter);
     else
         colnorm_partial_kernel<float><<<grid, kNormThreads, 0, stream>>>(
-            static_cast<const float *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part);
+            static_cast<const float *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part, counter);
     return hipGetLastError();
 }
 
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
-                                   hipStream_t stream) {
+                                   unsigned *counter, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad,
+                                   int64_t ld_pad, hipStream_t stream) {
     dim3 grid((unsigned)((d + 63) / 64), (unsigned)batch);
-    colnorm_finalize_kernel<<<grid, 256, 0, stream>>>(part, chunks, d, s);
+    finalize_select_kernel<<<grid, 1024, counter ? (size_t)k * 4 : 0, stream>>>(part, chunks, (int)d, s, counter, (int)k,
+                                                                                idx, ld_idx, idx_pad, ld_pad);
     return hipGetLastError();
 }
 
@@ -518,28 +675,58 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
                          float *aval, hipStream_t stream) {
     const int a_bf16 = a_dt == RMM_BF16;
     const unsigned g = (unsigned)batch;
-    if (d <= 256) {
-        select_reg_kernel<64, 4><<<g, 64, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
-                                                       idx_pad, ld_pad, aval);
-    } else if (d <= 4096) {
-        select_reg_kernel<256, 16><<<g, 256, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
-                                                          idx_pad, ld_pad, aval);
-    } else if (d <= 8192) {
-        select_reg_kernel<512, 16><<<g, 512, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx, ld_idx,
-                                                          idx_pad, ld_pad, aval);
-    } else if (d <= 16384) {
-        select_reg_kernel<1024, 16><<<g, 1024, 0, stream>>>(s, a_src, a_bf16, a_stride, (int)d, (int)k, idx,
-                                                            ld_idx, idx_pad, ld_pad, aval);
-    } else {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-        if (dev < 32 && !(g_select_attr_done & (1u << dev))) {
-            hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_big_kernel<1024>),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                (int)(kSelectLdsKeys * 4));
-            if (e1 != hipSuccess) return e1;
-            g_select_attr_done |= 1u << dev;
+    // dynamic LDS for the staged outputs (<= 128 KB: d <= 16384)
+    const size_t out_lds = (size_t)k * 4 * (aval ? 2 : 1);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (dev < 32 && !(g_select_attr_done & (1u << dev))) {
+        const void *ks[] = {reinterpret_cast<const void *>(&select_kernel<1024, 16, true, true>),
+                            reinterpret_cast<const void *>(&select_kernel<1024, 16, false, true>),
+                            reinterpret_cast<const void *>(&select_kernel<1024, 16, false, false>),
+                            reinterpret_cast<const void *>(&select_big_kernel<1024>)};
+        for (const void *kf : ks) {
+            hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+            if (e != hipSuccess) return e;
         }
+        g_select_attr_done |= 1u << dev;
+    }
+    if (a_src && a_dt == RMM_BF16) {
+        if ((uintptr_t)a_src % 16 != 0 || a_stride % 8 != 0 || d > 16384) return hipErrorInvalidValue;
+        const void *src = a_src;
+        if (d <= 256)
+            select_kernel<64, 8, true, true><<<g, 64, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx, ld_idx,
+                                                                          idx_pad, ld_pad, aval);
+        else if (d <= 4096)
+            select_kernel<256, 16, true, true><<<g, 256, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx, ld_idx,
+                                                                            idx_pad, ld_pad, aval);
+        else
+            select_kernel<1024, 16, true, true><<<g, 1024, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx,
+                                                                              ld_idx, idx_pad, ld_pad, aval);
+        return hipGetLastError();
+    }
+    const bool vec = ((uintptr_t)s % 16 == 0) && (d % 4 == 0);
+    if (d <= 256) {
+        if (vec)
+            select_kernel<64, 4, false, true><<<g, 64, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx, idx_pad,
+                                                                           ld_pad, aval);
+        else
+            select_kernel<64, 4, false, false><<<g, 64, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx, idx_pad,
+                                                                            ld_pad, aval);
+    } else if (d <= 4096) {
+        if (vec)
+            select_kernel<256, 16, false, true><<<g, 256, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                             idx_pad, ld_pad, aval);
+        else
+            select_kernel<256, 16, false, false><<<g, 256, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                              idx_pad, ld_pad, aval);
+    } else if (d <= 16384) {
+        if (vec)
+            select_kernel<1024, 16, false, true><<<g, 1024, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                               idx_pad, ld_pad, aval);
+        else
+            select_kernel<1024, 16, false, false><<<g, 1024, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                                idx_pad, ld_pad, aval);
+    } else {
         const int use_lds = d <= kSelectLdsKeys;
         const size_t lds = use_lds ? (size_t)d * 4 : 0;
         select_big_kernel<1024><<<g, 1024, lds, stream>>>(s, a_src, a_bf16, a_stride, d, k, idx, ld_idx, idx_pad,

@@ -166,7 +166,7 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     const bool ptr_ok = (!A || aligned16(A)) && (!B || aligned16(B)) && (!Y || aligned16(Y));
     const bool ld_ok = ds->lda % 8 == 0 && ds->ldb % 8 == 0 && ds->ldy % 8 == 0 && ds->m % 8 == 0 &&
                        (ds->batch == 1 || (ds->strideA % 8 == 0 && ds->strideB % 8 == 0 && ds->strideY % 8 == 0));
-    if (bf && ptr_ok && ld_ok && ds->n == 1 && !ds->transB && ds->batch == 1) {
+    if (bf && ptr_ok && ld_ok && ds->n == 1 && !ds->transB && ds->batch == 1 && ds->d <= kFusedSelectMaxD) {
         p.route = ROUTE_DECODE;
         p.shortcut = false;  // the fused |a| selection also produces the kept values
     } else if (bf && ptr_ok && ld_ok && mfma_extents_ok(ds, p.kpad)) {
@@ -271,8 +271,9 @@ rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, in
     const size_t need = (size_t)p.chunks * (size_t)d * 4;
     if (ws_bytes < need || !workspace) return RMM_ERR_WORKSPACE;
     float *part = static_cast<float *>(workspace);
-    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(A, dt, n, d, lda, 1, 0, p, part, stream));
-    RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.chunks, d, 1, s_out, stream));
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(A, dt, n, d, lda, 1, 0, p, part, nullptr, stream));
+    RMM_LAUNCH(RMM_KERNEL_FINALIZE,
+               launch_colnorm_finalize(part, p.chunks, d, 1, s_out, nullptr, 0, nullptr, 0, nullptr, 0, stream));
     return RMM_OK;
 }
 
@@ -339,8 +340,9 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         float *part = reinterpret_cast<float *>(ws + p.off_part);
         float *s = reinterpret_cast<float *>(ws + p.off_s);
         RMM_LAUNCH(RMM_KERNEL_COLNORM,
-                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
-        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, stream));
+                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, nullptr, stream));
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, nullptr, 0, nullptr, 0,
+                                                                nullptr, 0, stream));
         RMM_LAUNCH(RMM_KERNEL_SELECT,
                    launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, pidx, p.kpad, nullptr, stream));
     }

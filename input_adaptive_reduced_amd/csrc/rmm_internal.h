@@ -48,12 +48,20 @@ struct ColnormPlan {
     int64_t rows_per_chunk;
 };
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch);
+// `counter` (batch entries, may be null) is cleared for the finalize step.
 hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
                                   int64_t batch, int64_t strideA, const ColnormPlan &p, float *part,
-                                  hipStream_t stream);
-// s[b][j] = sqrt(sum_r part[b][r][j]) with r ascending.
+                                  unsigned *counter, hipStream_t stream);
+// s[b][j] = sqrt(sum_r part[b][r][j]) in a fixed order.  With `counter`
+// (cleared by launch_colnorm_partial in the same stream) the last workgroup
+// of each batch entry also selects the k largest scores into idx / idx_pad,
+// as launch_select does; d <= 16384 on that path.  (The library runs the
+// selection as its own launch: the device-scope fences this variant needs
+// cost more than the launch they save on MI355X.)
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
-                                   hipStream_t stream);
+                                   unsigned *counter, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad,
+                                   int64_t ld_pad, hipStream_t stream);
+constexpr int64_t kFusedSelectMaxD = 16384;
 
 // Exact TopK by radix select; rows of idx (ld_idx apart) and of idx_pad
 // (ld_pad apart, entries k..ld_pad-1 set to -1) receive the kept indices in
