@@ -236,8 +236,9 @@ def cpu_baseline(runner, rho, budget_s=12.0):
     return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"fp64 oracle: full column norms + full-sort TopK of one {n}x{d} matrix "
                        f"({t_sel:.2f} s) and the reduced product for {rows} of {n} output rows "
-                       f"({t_rows:.2f} s), extrapolated to all rows" +
-                       (f" and {runner.batch} heads" if runner.batch > 1 else "")),
+                       f"({t_rows:.2f} s)" +
+                       (", extrapolated to all rows" if rows < n else " (the whole product)") +
+                       (f"; one of {runner.batch} heads, scaled to all" if runner.batch > 1 else "")),
             "seconds_measured": t_sel + t_rows + t_probe}
 
 
@@ -252,6 +253,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--kernel-steps", type=int, default=50, help="steps for per-kernel event timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB a few times (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -268,6 +272,17 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "launches": 5}), flush=True)
+        return 0
 
     wl = WORKLOADS[args.workload]
     case = synthetic.make_case(wl["case"])
