@@ -9,23 +9,23 @@
 //
 // Operand handling
 //  * A's kept columns are strided 2-byte elements of row-major A, so they are
-//    first packed into a k-contiguous buffer (pack_kernel: each workgroup
-//    stages whole rows of A in LDS with 16-byte loads and gathers from LDS),
-//    padded with zeros to a multiple of the 64-wide K step.
-//  * B's kept rows are contiguous.  With B stored d x m the GEMM reads them in
-//    place through the index list (bmode 0): each thread fetches an 8 x 8
-//    block (8 gathered rows x 8 columns, 16-byte loads), transposes it in
-//    registers and writes eight k-contiguous 16-byte vectors to LDS, the
-//    layout the MFMA B operand wants.  With B stored as B^T (m x d: the keys
-//    of Q K^T) the kept columns are packed like A (bmode 1).
-//  * LDS tiles hold rows of 64 bf16 (eight 16-byte chunks); chunk c of row r
-//    lives at c ^ ((r ^ (r >> 3)) & 7), which keeps both the transposed
-//    stores (rows 8 apart) and the MFMA operand reads (consecutive rows)
-//    free of bank conflicts.
-//  * Tiles are 256x256 (4 waves, 128x128 each) or 128x128, double-buffered in
-//    LDS; workgroup ids are remapped so that each XCD (ids are dealt to the 8
-//    XCDs round-robin) works on a compact block of output tiles and shares
-//    its A rows and B columns in its own L2.
+//    first packed (pack_blocks_kernel) into MFMA operand blocks: for 32 rows
+//    and 16 kept entries, a 1 KB block in the order the lanes of one
+//    32x32x16 MFMA want it, padded with zeros to whole blocks.  The main
+//    kernel (gemm_adirect_kernel) then loads every A fragment straight from
+//    memory into registers with one coalesced 16-byte load per lane, two K
+//    steps ahead; A never passes through LDS.
+//  * B's kept rows are contiguous.  With B stored d x m the kernels read them
+//    in place through the index list: each thread fetches 16-byte pieces of
+//    eight kept rows, stores them into a row-major LDS tile and the waves read
+//    their MFMA operands with ds_read_b64_tr_b16.  With B stored as B^T
+//    (m x d: the keys of Q K^T) the kept columns are packed into rows of kpad
+//    entries (pack_kernel) and staged like a k-contiguous operand (bmode 1 of
+//    gemm_bf16_kernel, which also serves the 128x128 tiles of small shapes).
+//  * Tiles are 256x256 (4 waves, 128x128 each) or 128x128; workgroup ids are
+//    remapped so that each XCD (ids are dealt to the 8 XCDs round-robin) works
+//    on a compact block of output tiles and shares its A rows and B columns in
+//    its own L2.
 //  * Shapes with too few tiles to fill 256 CUs split the K range; fp32
 //    partials are then added in split order by splitk_reduce (deterministic).
 #include "rmm_internal.h"
@@ -367,6 +367,235 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
 }
 
+// Reduced product with A fragments loaded straight from HBM into registers
+// (256x256 output tile, 4 waves in a 2x2 grid, each wave 128x128).
+//
+// A[:, I] arrives packed in MFMA operand order (pack_kernel, layout 1): the
+// operand of one 32x32x16 step for 32 rows and 16 kept indices is a 1 KB
+// block in which lane l's 16 bytes hold row l % 32, entries 8 (l / 32) ..
+// +7.  Block (row block R, 16-entry group G) sits at (R * kpad/16 + G) KB.
+// Every A fragment is therefore one coalesced 16-byte-per-lane load, issued
+// two K steps before its MFMAs into the register slot its previous contents
+// just left; A never passes through LDS.
+//
+// Only the gathered rows of B go through LDS: per K step, each thread loads
+// eight 16-byte pieces (eight kept rows x 8 columns) through the index list
+// two steps ahead, stores the previous step's pieces into the free LDS
+// buffer over sub-steps 0-2 and the waves read their MFMA operands with
+// ds_read_b64_tr_b16 (row-major B tile: chunk c of row k at c ^ 2(k & 3)).
+// The kept row numbers of the workgroup's K range are copied once into LDS
+// as 16-bit values (0xffff marks padding: such rows read as zero), so the
+// gather never waits on a global index load.
+template <bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_adirect_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, NT = 256, WTM = 128, WTN = 128;
+    constexpr int FM = 4, FN = 4;
+    constexpr int CPR = BN / 8;        // 16-byte chunks per B row
+    constexpr int BUF = BK * CPR;      // uint4 per B buffer (32 KB)
+    __shared__ uint4 sL[4 * BUF];      // B buffers 0/1 | kept row numbers (u16, 64 KB) ; epilogue staging
+    uint16_t *sIdx = reinterpret_cast<uint16_t *>(sL + 2 * BUF);
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+    const int tiles_m = (int)((g.n + BM - 1) / BM), tiles_n = (int)((g.m + BN - 1) / BN);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t b = blockIdx.z;
+    const int split = blockIdx.y;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (b / g.group) * g.strideB, g.b_bytes);
+    const int32_t *idx = g.idx + b * g.ld_idx;
+
+    const int KT = (int)(g.kpad / BK);
+    const int per = ((KT + g.splits - 1) / g.splits + 1) & ~1;
+    const int kt0 = split * per;
+    const int kt1 = min(KT, kt0 + per);
+    const int KG = (int)(g.kpad / 16);
+
+    // this wave's A row blocks; blocks past n read as zero
+    uint32_t aoff[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t rb = (m0 + wm * WTM) / 32 + i;
+        aoff[i] = rb * 32 < g.n ? (uint32_t)(rb * KG * 1024 + lane * 16) : kOob;
+    }
+    // B: thread owns kept rows kq*8 .. kq*8+7 of a step, 16-byte column chunk nc
+    const int kq = tid / CPR, nc = tid % CPR;
+    const uint32_t ldb2 = (uint32_t)(g.ldb * 2), bcol2 = (uint32_t)((n0 + nc * 8) * 2);
+
+    auto load_rows = [&](int kt, uint32_t (&o)[4]) {  // eight u16 row numbers, one LDS read
+        const int t0 = (min(kt, kt1 - 1) - kt0) * BK + kq * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(sIdx + t0);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    };
+    auto load_b = [&](int r0, int r1, uint4 (&rb)[8], const uint32_t (&ix)[4]) {
+#pragma unroll
+        for (int r = r0; r < r1; ++r) {
+            const uint32_t row = (r & 1) ? (ix[r >> 1] >> 16) : (ix[r >> 1] & 0xffffu);
+            rb[r] = buf_load16(rB, row == 0xffffu ? kOob : row * ldb2 + bcol2);
+        }
+    };
+    auto load_a = [&](int kt, int ks, bf16x8_t (&fa)[FM]) {
+        const uint32_t ko = (uint32_t)(min(kt, kt1 - 1) * 4 + ks) * 1024u;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = as_bf16x8(buf_load16(rA, aoff[i] + ko));
+    };
+    auto store_b = [&](int buf, const uint4 (&rb)[8], int r0, int r1) {
+#pragma unroll
+        for (int r = r0; r < r1; ++r) {
+            const int k = kq * 8 + r;
+            sL[buf * BUF + k * CPR + (nc ^ ((k & 3) << 1))] = rb[r];
+        }
+    };
+    auto read_b = [&](int buf, int ks, bf16x8_t (&fb)[FN]) {
+        const int gq = lane >> 4, li = lane & 15;
+        const int kbase = ks * 16 + 8 * (gq >> 1) + (li >> 2);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int nn = wn * WTN + j * 32 + 16 * (gq & 1) + 4 * (li & 3);
+            union {
+                v4i16_t h[2];
+                bf16x8_t v;
+            } u;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int k = kbase + 4 * hh;
+                const char *p = reinterpret_cast<const char *>(&sL[buf * BUF + k * CPR + ((nn >> 3) ^ ((k & 3) << 1))]) +
+                                ((nn >> 2) & 1) * 8;
+                u.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
+            }
+            fb[j] = u.v;
+        }
+    };
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    bf16x8_t fa[2][4][FM];  // [step parity][sub-step][row block]
+    bf16x8_t fb[2][FN];
+    uint4 rb0[8], rb1[8];
+    uint32_t ix0[4], ix1[4];
+
+    // one K step on LDS buffer `buf` and A slot set `p`: B rows of step kt+2
+    // are loaded into lb while those of step kt+1 (sb) are stored
+    auto step = [&](int kt, int p, int buf, uint4 (&lb)[8], uint32_t (&lix)[4], const uint4 (&sb)[8]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) read_b(buf, ks + 1, fb[(ks + 1) & 1]);
+            else read_b(buf ^ 1, 0, fb[0]);
+            if (ks < 3) {
+                load_b(ks * 3, min(8, ks * 3 + 3), lb, lix);
+                store_b(buf ^ 1, sb, ks * 3, min(8, ks * 3 + 3));
+            }
+            // operands swapped: each lane ends up holding four consecutive
+            // output columns of one output row
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[p][ks][i], acc[i][j], 0, 0, 0);
+            load_a(kt + 2, ks, fa[p][ks]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == 2) __syncthreads();
+        }
+        load_rows(kt + 4, lix);
+    };
+
+    if (kt0 < kt1) {
+        for (int t = tid; t < (kt1 - kt0) * BK; t += NT) {
+            const int32_t v = idx[kt0 * BK + t];
+            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
+        }
+        __syncthreads();
+        load_rows(kt0, ix0);
+        load_rows(kt0 + 1, ix1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) load_a(kt0, ks, fa[0][ks]);
+        load_b(0, 8, rb0, ix0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) load_a(kt0 + 1, ks, fa[1][ks]);
+        load_b(0, 8, rb1, ix1);
+        load_rows(kt0 + 2, ix0);
+        load_rows(kt0 + 3, ix1);
+        store_b(0, rb0, 0, 8);
+        __syncthreads();
+        read_b(0, 0, fb[0]);
+        for (int kt = kt0; kt < kt1; kt += 2) {
+            step(kt, 0, 0, rb0, ix0, rb1);      // step kt on buffer 0; step kt+1's rows -> buffer 1
+            step(kt + 1, 1, 1, rb1, ix1, rb0);  // step kt+1 on buffer 1; step kt+2's rows -> buffer 0
+        }
+    }
+
+    // epilogue: lane l, registers 4q..4q+3 of block (i, j) hold output row
+    // i*32 + l%32 and columns j*32 + 8q + 4(l/32) + 0..3.
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+            if (row >= g.n) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                    if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
+                    *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m + col) =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                }
+            }
+        }
+    } else {
+        // bf16 results go through LDS (each wave stages its 128 x 128 block,
+        // 16-byte chunk c of row r at c ^ (r % 16)) so every global store is
+        // a full 16-byte piece and each 16-lane group writes 256 contiguous bytes
+        constexpr int CPW = WTN / 8;
+        __syncthreads();  // every wave is done with the operand buffers
+        uint4 *stage = sL + w * WTM * CPW;
+        char *st = reinterpret_cast<char *>(stage);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c4 = j * 8 + q * 2 + (lane >> 5);
+                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q])) |
+                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 1])) << 16);
+                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 2])) |
+                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 3])) << 16);
+                    const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
+                    *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        constexpr int RPI = 64 / CPW;
+#pragma unroll 4
+        for (int it = 0; it < WTM / RPI; ++it) {
+            const int r = it * RPI + lane / CPW;
+            const int c = lane % CPW;
+            const uint4 v = stage[r * CPW + (c ^ (r & (CPW - 1)))];
+            const int64_t row = m0 + wm * WTM + r;
+            const int64_t col = n0 + wn * WTN + c * 8;
+            if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(g.Y + b * g.strideY + row * g.ldy + col) = v;
+        }
+    }
+}
+
 // Y = alpha * sum over splits (ascending) of the fp32 partials; 4 columns per thread.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits, int64_t n,
                                                             int64_t m, int64_t batch, float alpha,
@@ -429,21 +658,124 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
         __syncthreads();
     }
     const int64_t cpr = kpad / 8;  // output chunks per row
+    auto gather = [&](int rr, const int32_t (&j)[8]) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t jj = j[e] >= 0 ? j[e] : 0;
+            const uint16_t v = use_lds ? rowbuf[rr * d + jj] : S[(r0 + rr) * ld_src + jj];
+            h[e] = j[e] >= 0 ? v : 0;
+        }
+        return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    };
     for (int64_t c = tid; c < cpr; c += 256) {
         const int4 p0 = *reinterpret_cast<const int4 *>(idx + c * 8);
         const int4 p1 = *reinterpret_cast<const int4 *>(idx + c * 8 + 4);
         const int32_t j[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        for (int rr = 0; rr < nr; ++rr) {
-            uint32_t h[8];
+        for (int rr = 0; rr < nr; ++rr) *reinterpret_cast<uint4 *>(D + (r0 + rr) * kpad + c * 8) = gather(rr, j);
+    }
+}
+
+// Pack into MFMA operand blocks (layout 1).  One workgroup builds the output
+// of one 32-row block and 128 consecutive kept entries: 8 operand blocks,
+// 8 KB written contiguously (each wave stores whole 1 KB blocks).  The kept
+// source columns of those entries are ascending, so the workgroup stages the
+// source window [I[t0], I[t0+127]] of its 32 rows in LDS (in pieces of at
+// most kPackWin columns, 16-byte loads along the rows) and gathers from it.
+// Rows past `rows` and padding entries (index -1) are written as zero.
+constexpr int kPackWin = 512;             // source columns per staged window
+constexpr int kPackRowStride = kPackWin + 4;  // u16 per staged row (8-byte pad against bank conflicts)
+
+__global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__restrict__ src, int64_t rows, int64_t d,
+                                                          int64_t ld_src, int64_t src_stride, int64_t group,
+                                                          const int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                          int64_t kpad, uint16_t *__restrict__ dst,
+                                                          int64_t dst_stride, int vec_ok) {
+    __shared__ uint16_t win[32 * kPackRowStride];
+    __shared__ int32_t span[2];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t rb = blockIdx.x, t0 = (int64_t)blockIdx.y * 128, b = blockIdx.z;
+    const uint16_t *S = src + (b / group) * src_stride;
+    const int32_t *idx = idx_all + b * ld_idx;
+    const int row = lane & 31;                // row within the block owned by this lane
+    const int64_t grow = rb * 32 + row;
+    const bool row_ok = grow < rows;
+    const int nrows = (int)max((int64_t)0, min((int64_t)32, rows - rb * 32));
+
+    // this thread's two output pieces: block w + 4h, lane -> (row, chunk)
+    int32_t j[2][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t jj = j[e] >= 0 ? j[e] : 0;
-                const uint16_t v = use_lds ? rowbuf[rr * d + jj] : S[(r0 + rr) * ld_src + jj];
-                h[e] = j[e] >= 0 ? v : 0;
+    for (int h = 0; h < 2; ++h) {
+        const int64_t c = 2 * (w + 4 * h) + (lane >> 5);  // chunk of 8 entries within the tile
+        const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8);
+        const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8 + 4);
+        j[h][0] = p0.x; j[h][1] = p0.y; j[h][2] = p0.z; j[h][3] = p0.w;
+        j[h][4] = p1.x; j[h][5] = p1.y; j[h][6] = p1.z; j[h][7] = p1.w;
+    }
+    // kept entries ascend and padding (-1) only trails, so the tile's source
+    // span is [first entry, last valid entry + 1).  Thread 0 holds the first
+    // entry and thread 255 the last; only the tile holding the end of the
+    // list searches for its last valid entry.
+    if (tid == 0) span[0] = j[0][0];
+    if (tid == 255) {
+        int32_t last = j[1][7];
+        if (last < 0 && idx[t0] >= 0) {
+            int a = 0, z = 127;
+            while (a < z) {
+                const int mid = (a + z + 1) >> 1;
+                if (idx[t0 + mid] >= 0) a = mid; else z = mid - 1;
             }
-            *reinterpret_cast<uint4 *>(D + (r0 + rr) * kpad + c * 8) =
-                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            last = idx[t0 + a];
         }
+        span[1] = last + 1;
+    }
+    __syncthreads();
+    const int32_t lo = span[0], hi = span[1];
+
+    uint32_t hv[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[h][e] = 0;
+
+    if (lo >= 0 && nrows > 0) {
+        for (int64_t w0 = lo & ~7; w0 < hi; w0 += kPackWin) {
+            const int64_t wend = min(w0 + (int64_t)kPackWin, (int64_t)hi);
+            if (w0 != (lo & ~7)) __syncthreads();  // previous window fully consumed
+            if (vec_ok) {
+                const int chunks = (int)((wend - w0 + 7) / 8);  // d % 8 == 0: chunks stay inside the row
+                for (int q = tid; q < nrows * chunks; q += 256) {
+                    const int r = q / chunks, c = q - r * chunks;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(S + (rb * 32 + r) * ld_src + w0 + c * 8);
+                    uint16_t *o = win + r * kPackRowStride + c * 8;
+                    *reinterpret_cast<uint2 *>(o) = make_uint2(v.x, v.y);
+                    *reinterpret_cast<uint2 *>(o + 4) = make_uint2(v.z, v.w);
+                }
+            } else {
+                const int cols = (int)(wend - w0);
+                for (int q = tid; q < nrows * cols; q += 256) {
+                    const int r = q / cols, c = q - r * cols;
+                    win[r * kPackRowStride + c] = S[(rb * 32 + r) * ld_src + w0 + c];
+                }
+            }
+            __syncthreads();
+            if (row_ok) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int32_t jj = j[h][e];
+                        if (jj >= w0 && jj < wend) hv[h][e] = win[row * kPackRowStride + (jj - w0)];
+                    }
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t blk = rb * (kpad >> 4) + (t0 >> 4) + (w + 4 * h);
+        *reinterpret_cast<uint4 *>(dst + b * dst_stride + blk * 512 + lane * 8) =
+            make_uint4(hv[h][0] | (hv[h][1] << 16), hv[h][2] | (hv[h][3] << 16), hv[h][4] | (hv[h][5] << 16),
+                       hv[h][6] | (hv[h][7] << 16));
     }
 }
 
@@ -535,7 +867,25 @@ hipError_t allow_big_lds(K kernel) {
 
 }  // namespace
 
-GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch) {
+static GemmConfig gemm_choose_tile(int64_t n, int64_t m, int64_t k, int64_t batch);
+
+// The A-direct kernel needs row-major B (rows gathered through the list),
+// kept row numbers below 0xffff and a per-split K range whose list fits its
+// 64 KB of LDS (32768 entries).
+static bool adirect_ok(int64_t kpad, int splits, int64_t d, int transB) {
+    if (transB || d >= 0xffff) return false;
+    const int64_t KT = kpad / BK;
+    const int64_t per = ((KT + splits - 1) / splits + 1) & ~1LL;
+    return per * BK <= 32768;
+}
+
+GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB) {
+    GemmConfig c = gemm_choose_tile(n, m, k, batch);
+    if (c.tile == 0 && adirect_ok((k + 127) / 128 * 128, c.splits, d, transB)) c.tile = 2;
+    return c;
+}
+
+static GemmConfig gemm_choose_tile(int64_t n, int64_t m, int64_t k, int64_t batch) {
     GemmConfig c;
     const int64_t big = ((n + 255) / 256) * ((m + 255) / 256) * batch;
     const int64_t ksteps = (k + BK - 1) / BK;
@@ -590,6 +940,16 @@ static hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream) {
     GemmArgs a = g;
     a.splits = c.splits;
+    if (c.tile == 2) {
+        if (a.bmode != 0) return hipErrorInvalidValue;
+        const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
+        dim3 grid((unsigned)tiles, (unsigned)a.splits, (unsigned)a.batch);
+        if (a.splits > 1)
+            gemm_adirect_kernel<true><<<grid, 256, 0, stream>>>(a);
+        else
+            gemm_adirect_kernel<false><<<grid, 256, 0, stream>>>(a);
+        return hipGetLastError();
+    }
     if (c.tile == 0) return launch_tile<256, 256, 2, 2>(a, stream);
     return launch_tile<128, 128, 2, 2>(a, stream);
 }
@@ -607,7 +967,7 @@ static constexpr int64_t kPackLdsBytes = 64 * 1024;
 
 hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src, int64_t src_stride,
                        int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad, void *dst,
-                       int64_t dst_stride, int64_t batch, hipStream_t stream) {
+                       int64_t dst_stride, int64_t batch, int layout, hipStream_t stream) {
     if (dt != RMM_BF16) return hipErrorInvalidValue;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
@@ -616,9 +976,18 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
         if (e != hipSuccess) return e;
         g_pack_attr_done |= 1u << dev;
     }
+    if (layout != 0) {
+        if (kpad % 128 != 0) return hipErrorInvalidValue;
+        const int vec = ((uintptr_t)src % 16 == 0) && (ld_src % 8 == 0) && (d % 8 == 0) && (src_stride % 8 == 0);
+        dim3 grid((unsigned)((rows + 31) / 32), (unsigned)(kpad / 128), (unsigned)batch);
+        pack_blocks_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src, src_stride,
+                                                     group, idx, ld_idx, kpad, static_cast<uint16_t *>(dst),
+                                                     dst_stride, vec);
+        return hipGetLastError();
+    }
     const int64_t row_bytes = d * 2;
     int rpw = (int)(kPackLdsBytes / row_bytes);
-    int use_lds = rpw >= 1;
+    const int use_lds = rpw >= 1;
     if (rpw > 8) rpw = 8;
     if (rpw < 1) rpw = 4;
     const int vec_ok = use_lds && ((uintptr_t)src % 16 == 0) && (ld_src % 8 == 0) && (d % 8 == 0) &&

@@ -96,6 +96,7 @@ struct Plan {
     ColnormPlan cp;
     GemmConfig gc;
     int gsplits;
+    int64_t a_rows;  // rows of the packed A buffer per batch entry
     size_t off_part, off_s, off_idx, off_Ap, off_Bp, off_gpart, off_aval, total;
 };
 
@@ -149,7 +150,7 @@ int64_t b_extent_bytes(const rmm_desc_t *ds) {
 }
 bool mfma_extents_ok(const rmm_desc_t *ds, int64_t kpad) {
     return a_extent_bytes(ds) < kMaxBufferBytes && b_extent_bytes(ds) < kMaxBufferBytes &&
-           ds->n * kpad * 2 < kMaxBufferBytes && ds->m * kpad * 2 < kMaxBufferBytes;
+           (ds->n + 31) / 32 * 32 * kpad * 2 < kMaxBufferBytes && ds->m * kpad * 2 < kMaxBufferBytes;
 }
 
 // Alignment-based part of the route choice; pointers may be null when only
@@ -190,10 +191,11 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     }
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
     if (p.route == ROUTE_MFMA) {
-        p.directA = p.shortcut && d % 128 == 0;
-        if (!p.directA) p.off_Ap = take((size_t)batch * n * p.kpad * 2);
+        p.gc = gemm_choose(n, m, k, batch, d, ds->transB);
+        p.directA = p.shortcut && d % 128 == 0 && p.gc.tile != 2;
+        p.a_rows = p.gc.tile == 2 ? (n + 31) / 32 * 32 : n;  // operand blocks cover whole 32-row groups
+        if (!p.directA) p.off_Ap = take((size_t)batch * p.a_rows * p.kpad * 2);
         if (ds->transB) p.off_Bp = take((size_t)batch * m * p.kpad * 2);
-        p.gc = gemm_choose(n, m, k, batch);
         if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * batch * n * m * 4);
     } else if (p.route == ROUTE_DECODE) {
         p.gsplits = gemv_splits(m, k);
@@ -387,10 +389,10 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
             gemm_idx = pidx;
         }
         RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(A, RMM_BF16, n, d, ds.lda, ds.strideA, 1, pidx, p.kpad, p.kpad, Ap,
-                                                n * p.kpad, batch, stream));
+                                                p.a_rows * p.kpad, batch, p.gc.tile == 2 ? 1 : 0, stream));
         g.A = Ap;
         g.lda = p.kpad;
-        g.strideA = n * p.kpad;
+        g.strideA = p.a_rows * p.kpad;
     }
     if (ds.transB) {
         uint16_t *Bp = reinterpret_cast<uint16_t *>(ws + p.off_Bp);
@@ -399,7 +401,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
             gemm_idx = pidx;
         }
         RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(B, RMM_BF16, m, d, ds.ldb, ds.strideB, ds.b_group, pidx, p.kpad,
-                                                p.kpad, Bp, m * p.kpad, batch, stream));
+                                                p.kpad, Bp, m * p.kpad, batch, 0, stream));
         g.B = Bp;
         g.ldb = p.kpad;
         g.strideB = m * p.kpad;
@@ -426,7 +428,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     g.m = m;
     g.k = k;
     g.kpad = p.directA ? d : p.kpad;
-    g.a_bytes = p.directA ? a_extent_bytes(desc) : n * p.kpad * 2;
+    g.a_bytes = p.directA ? a_extent_bytes(desc) : p.a_rows * p.kpad * 2;
     g.b_bytes = ds.transB ? m * p.kpad * 2 : b_extent_bytes(desc);
     g.batch = batch;
     g.alpha = ds.alpha;

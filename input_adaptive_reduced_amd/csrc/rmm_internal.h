@@ -74,9 +74,13 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
 
 // dst[b][r][t] = src[b / group][r][idx[b][t]] for t < kpad, 0 where idx[b][t]
 // is -1.  idx rows are ld_idx apart (a multiple of 64, 256-byte aligned).
+// layout 0: dst rows of kpad entries (row r at dst + r * kpad).
+// layout 1: MFMA operand blocks for the A-direct GEMM: rows padded to a
+// multiple of 32; the 16-byte piece (row r, entries 8c..8c+7) sits at element
+// ((r / 32) * (kpad / 16) + c / 2) * 512 + ((c % 2) * 32 + r % 32) * 8.
 hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src,
                        int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad,
-                       void *dst, int64_t dst_stride, int64_t batch, hipStream_t stream);
+                       void *dst, int64_t dst_stride, int64_t batch, int layout, hipStream_t stream);
 
 // Index rows 0..k-1 then -1 up to ld, per batch entry (rho = 1 shortcut).
 hipError_t launch_iota(int32_t *idx, int64_t k, int64_t ld, int64_t batch, hipStream_t stream);
@@ -101,10 +105,10 @@ struct GemmArgs {
     float alpha;
 };
 struct GemmConfig {
-    int tile;    // 0: 256x256, 1: 128x128, 2: 256x128
+    int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct)
     int splits;  // >= 1
 };
-GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch);
+GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream);
 // Y = alpha * sum_s part[s] (s ascending), rounded to bf16.
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,
