@@ -30,6 +30,8 @@
 //    partials are then added in split order by splitk_reduce (deterministic).
 #include "rmm_internal.h"
 
+#include <algorithm>
+
 namespace rmm {
 
 namespace {
@@ -343,10 +345,8 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c4 = j * 8 + q * 2 + (lane >> 5);  // 4-column group within the wave row
-                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q])) |
-                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 1])) << 16);
-                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 2])) |
-                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 3])) << 16);
+                    const uint32_t lo = pack_bf16x2(g.alpha * acc[i][j][4 * q], g.alpha * acc[i][j][4 * q + 1]);
+                    const uint32_t hi = pack_bf16x2(g.alpha * acc[i][j][4 * q + 2], g.alpha * acc[i][j][4 * q + 3]);
                     const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
                     *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
                 }
@@ -572,10 +572,8 @@ __global__ __launch_bounds__(256, 1) void gemm_adirect_kernel(GemmArgs g) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c4 = j * 8 + q * 2 + (lane >> 5);
-                    const uint32_t lo = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q])) |
-                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 1])) << 16);
-                    const uint32_t hi = uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 2])) |
-                                        (uint32_t(f32_to_bf16(g.alpha * acc[i][j][4 * q + 3])) << 16);
+                    const uint32_t lo = pack_bf16x2(g.alpha * acc[i][j][4 * q], g.alpha * acc[i][j][4 * q + 1]);
+                    const uint32_t hi = pack_bf16x2(g.alpha * acc[i][j][4 * q + 2], g.alpha * acc[i][j][4 * q + 3]);
                     const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
                     *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
                 }
@@ -593,6 +591,151 @@ __global__ __launch_bounds__(256, 1) void gemm_adirect_kernel(GemmArgs g) {
             const int64_t col = n0 + wn * WTN + c * 8;
             if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(g.Y + b * g.strideY + row * g.ldy + col) = v;
         }
+    }
+}
+
+// Reduced product for a single 64-entry K step (kpad = 64), both operands
+// in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I], i.e. the
+// kept columns of the keys for Q K^T).  Such products are bound by writing
+// Y (62 flop per output byte at k = 64), so the kernel is persistent and
+// splits each workgroup into two roles:
+//  * waves 0-3 compute: each owns 128 rows x 64 columns of a 256x128 output
+//    tile, rounds its results to bf16 and writes them into one of two LDS
+//    stage buffers;
+//  * waves 4-7 store: one workgroup barrier per tile later they copy the
+//    staged tile to Y, 16 lanes writing 256 contiguous bytes of a row.
+// A workgroup walks whole row panels (one batch entry, 256 rows, every
+// column tile), so a compute wave loads its A fragments once per panel and
+// only its 8 B fragments per tile, issued right after the MFMAs that
+// consumed the previous ones.  Loads share the CU's memory pipeline with the
+// stores, which run at HBM speed; keeping them few is what keeps the compute
+// waves ahead of the stores.  Panels are dealt to workgroups in contiguous
+// runs, and runs to XCDs in order, so each XCD's L2 serves few batch entries.
+// Stage layout: 256 rows x 16 chunks of 16 bytes, chunk c of row r at
+// c ^ (r & 15).
+__global__ __launch_bounds__(512, 1) void gemm_stream_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 128, WTM = 128, WTN = 64, FM = 4, FN = 2, KS = 4, CPR = BN / 8;
+    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool compute = w < 4;
+    const int wm = (w & 3) >> 1, wn = w & 1;
+    const int64_t tiles_m = (g.n + BM - 1) / BM, tiles_n = (g.m + BN - 1) / BN;
+    const int64_t panels = tiles_m * g.batch;
+    const int G = gridDim.x;
+    const int chunk = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int64_t per = (panels + G - 1) / G;
+    const int64_t p0 = chunk * per, p1 = min(panels, p0 + per);
+    const int64_t count = p1 > p0 ? (p1 - p0) * tiles_n : 0;  // tiles of this workgroup
+    // (all counts fit in 32 bits: n, m < 2^30, batch <= 65535)
+    const int tiles_n32 = (int)tiles_n, tiles_m32 = (int)tiles_m, p032 = (int)p0;
+    auto coords = [&](int64_t q64, int64_t &b, int64_t &tm, int64_t &tn) {
+        const int q = (int)q64;
+        const int qp = q / tiles_n32;
+        const int p = p032 + qp;
+        tn = q - qp * tiles_n32;
+        b = p / tiles_m32;
+        tm = p - (int)b * tiles_m32;
+    };
+
+    bf16x8_t fa[KS][FM], fb[KS][FN];
+    auto load_a = [&](int64_t q) {
+        int64_t b, tm, tn;
+        coords(q, b, tm, tn);
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t rb = tm * (BM / 32) + wm * (WTM / 32) + i;
+            const uint32_t off = rb * 32 < g.n ? (uint32_t)(rb * KS * 1024 + lane * 16) : kOob;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) fa[ks][i] = as_bf16x8(buf_load16(rA, off + ks * 1024));
+        }
+    };
+    auto load_b = [&](int64_t q) {
+        int64_t b, tm, tn;
+        coords(q, b, tm, tn);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + b * g.strideB, g.b_bytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t cb = tn * (BN / 32) + wn * (WTN / 32) + j;
+            const uint32_t off = cb * 32 < g.m ? (uint32_t)(cb * KS * 1024 + lane * 16) : kOob;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) fb[ks][j] = as_bf16x8(buf_load16(rB, off + ks * 1024));
+        }
+    };
+
+    if (compute && count > 0) {
+        load_a(0);
+        load_b(0);
+    }
+    // iteration q computes this workgroup's tile q and stores tile q - 1
+    for (int64_t q = 0; q <= count; ++q) {
+        if (compute) {
+            if (q < count) {
+                f32x16_t acc[FM][FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] =
+                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+                // round to bf16 first (frees the accumulators), then fetch the
+                // next tile's operands, then stage
+                uint2 pk[FM][FN][4];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq)
+                            pk[i][j][qq] =
+                                make_uint2(pack_bf16x2(g.alpha * acc[i][j][4 * qq], g.alpha * acc[i][j][4 * qq + 1]),
+                                           pack_bf16x2(g.alpha * acc[i][j][4 * qq + 2], g.alpha * acc[i][j][4 * qq + 3]));
+                if (q + 1 < count) {
+                    if ((int)(q + 1) % tiles_n32 == 0) load_a(q + 1);  // next panel
+                    load_b(q + 1);
+                }
+                char *st = reinterpret_cast<char *>(stageL[q & 1]);
+                // lane l, registers 4qq..4qq+3 of block (i, j): row i*32 + l%32,
+                // columns j*32 + 8qq + 4(l/32) + 0..3 of this wave's block
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                        for (int qq = 0; qq < 4; ++qq) {
+                            const int c = wn * (WTN / 8) + j * 4 + qq;  // 16-byte chunk of the tile row
+                            *reinterpret_cast<uint2 *>(st + (r * CPR + (c ^ (r & 15))) * 16 + (lane >> 5) * 8) =
+                                pk[i][j][qq];
+                        }
+                    }
+                }
+            }
+        } else if (q > 0) {
+            int64_t b, tm, tn;
+            coords(q - 1, b, tm, tn);
+            const int64_t m0 = tm * BM, n0 = tn * BN;
+            const uint4 *stg = stageL[(q - 1) & 1];
+            uint16_t *Yb = g.Y + b * g.strideY;
+            const int sw = w - 4;  // rows 64 sw .. 64 sw + 63 of the tile
+#pragma unroll 4
+            for (int it = 0; it < 16; ++it) {
+                const int r = sw * 64 + it * 4 + (lane >> 4);
+                const int c = lane & 15;
+                const uint4 v = stg[r * CPR + (c ^ (r & 15))];
+                const int64_t row = m0 + r, col = n0 + c * 8;
+                if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(Yb + row * g.ldy + col) = v;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -616,8 +759,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         s.w += v.w;
     }
     uint16_t *y = Y + b * strideY + row * ldy + col;
-    uint32_t lo = uint32_t(f32_to_bf16(alpha * s.x)) | (uint32_t(f32_to_bf16(alpha * s.y)) << 16);
-    uint32_t hi = uint32_t(f32_to_bf16(alpha * s.z)) | (uint32_t(f32_to_bf16(alpha * s.w)) << 16);
+    uint32_t lo = pack_bf16x2(alpha * s.x, alpha * s.y);
+    uint32_t hi = pack_bf16x2(alpha * s.z, alpha * s.w);
     *reinterpret_cast<uint2 *>(y) = make_uint2(lo, hi);
 }
 
@@ -677,8 +820,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 }
 
 // Pack into MFMA operand blocks (layout 1).  One workgroup builds the output
-// of one 32-row block and 128 consecutive kept entries: 8 operand blocks,
-// 8 KB written contiguously (each wave stores whole 1 KB blocks).  The kept
+// of one 32-row block and TT (128, or 64 for short lists) consecutive kept
+// entries: TT/16 operand blocks written contiguously (each wave stores whole
+// 1 KB blocks).  The kept
 // source columns of those entries are ascending, so the workgroup stages the
 // source window [I[t0], I[t0+127]] of its 32 rows in LDS (in pieces of at
 // most kPackWin columns, 16-byte loads along the rows) and gathers from it.
@@ -686,6 +830,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
 constexpr int kPackWin = 512;             // source columns per staged window
 constexpr int kPackRowStride = kPackWin + 4;  // u16 per staged row (8-byte pad against bank conflicts)
 
+template <int TT>
 __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__restrict__ src, int64_t rows, int64_t d,
                                                           int64_t ld_src, int64_t src_stride, int64_t group,
                                                           const int32_t *__restrict__ idx_all, int64_t ld_idx,
@@ -694,7 +839,8 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
     __shared__ uint16_t win[32 * kPackRowStride];
     __shared__ int32_t span[2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t rb = blockIdx.x, t0 = (int64_t)blockIdx.y * 128, b = blockIdx.z;
+    constexpr int PP = TT / 64;  // output pieces per thread
+    const int64_t rb = blockIdx.x, t0 = (int64_t)blockIdx.y * TT, b = blockIdx.z;
     const uint16_t *S = src + (b / group) * src_stride;
     const int32_t *idx = idx_all + b * ld_idx;
     const int row = lane & 31;                // row within the block owned by this lane
@@ -702,10 +848,10 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
     const bool row_ok = grow < rows;
     const int nrows = (int)max((int64_t)0, min((int64_t)32, rows - rb * 32));
 
-    // this thread's two output pieces: block w + 4h, lane -> (row, chunk)
-    int32_t j[2][8];
+    // this thread's output pieces: block w + 4h, lane -> (row, chunk)
+    int32_t j[PP][8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < PP; ++h) {
         const int64_t c = 2 * (w + 4 * h) + (lane >> 5);  // chunk of 8 entries within the tile
         const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8);
         const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8 + 4);
@@ -718,9 +864,9 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
     // list searches for its last valid entry.
     if (tid == 0) span[0] = j[0][0];
     if (tid == 255) {
-        int32_t last = j[1][7];
+        int32_t last = j[PP - 1][7];
         if (last < 0 && idx[t0] >= 0) {
-            int a = 0, z = 127;
+            int a = 0, z = TT - 1;
             while (a < z) {
                 const int mid = (a + z + 1) >> 1;
                 if (idx[t0 + mid] >= 0) a = mid; else z = mid - 1;
@@ -732,9 +878,9 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
     __syncthreads();
     const int32_t lo = span[0], hi = span[1];
 
-    uint32_t hv[2][8];
+    uint32_t hv[PP][8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < PP; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[h][e] = 0;
 
@@ -761,7 +907,7 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
             __syncthreads();
             if (row_ok) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < PP; ++h)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int32_t jj = j[h][e];
@@ -771,7 +917,7 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
         }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < PP; ++h) {
         const int64_t blk = rb * (kpad >> 4) + (t0 >> 4) + (w + 4 * h);
         *reinterpret_cast<uint4 *>(dst + b * dst_stride + blk * 512 + lane * 8) =
             make_uint4(hv[h][0] | (hv[h][1] << 16), hv[h][2] | (hv[h][3] << 16), hv[h][4] | (hv[h][5] << 16),
@@ -880,6 +1026,13 @@ static bool adirect_ok(int64_t kpad, int splits, int64_t d, int transB) {
 }
 
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB) {
+    if (transB && k <= BK && ((n + 255) / 256) * ((m + 255) / 256) * batch >= 512) {
+        // one K step, many tiles (scores Q K^T): write-bound streaming kernel
+        GemmConfig c;
+        c.tile = 3;
+        c.splits = 1;
+        return c;
+    }
     GemmConfig c = gemm_choose_tile(n, m, k, batch);
     if (c.tile == 0 && adirect_ok((k + 127) / 128 * 128, c.splits, d, transB)) c.tile = 2;
     return c;
@@ -940,6 +1093,17 @@ static hipError_t launch_tile(const GemmArgs &g, hipStream_t stream) {
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream) {
     GemmArgs a = g;
     a.splits = c.splits;
+    if (c.tile == 3) {
+        if (a.kpad != BK || a.splits != 1) return hipErrorInvalidValue;
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+        const int64_t panels = ((a.n + 255) / 256) * a.batch;
+        const unsigned grid = (unsigned)std::min<int64_t>(panels, (int64_t)cus);
+        gemm_stream_kernel<<<grid, 512, 0, stream>>>(a);
+        return hipGetLastError();
+    }
     if (c.tile == 2) {
         if (a.bmode != 0) return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
@@ -977,12 +1141,18 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
         g_pack_attr_done |= 1u << dev;
     }
     if (layout != 0) {
-        if (kpad % 128 != 0) return hipErrorInvalidValue;
+        if (kpad % 64 != 0) return hipErrorInvalidValue;
         const int vec = ((uintptr_t)src % 16 == 0) && (ld_src % 8 == 0) && (d % 8 == 0) && (src_stride % 8 == 0);
-        dim3 grid((unsigned)((rows + 31) / 32), (unsigned)(kpad / 128), (unsigned)batch);
-        pack_blocks_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src, src_stride,
-                                                     group, idx, ld_idx, kpad, static_cast<uint16_t *>(dst),
-                                                     dst_stride, vec);
+        const int tt = kpad % 128 == 0 ? 128 : 64;
+        dim3 grid((unsigned)((rows + 31) / 32), (unsigned)(kpad / tt), (unsigned)batch);
+        if (tt == 128)
+            pack_blocks_kernel<128><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src,
+                                                              src_stride, group, idx, ld_idx, kpad,
+                                                              static_cast<uint16_t *>(dst), dst_stride, vec);
+        else
+            pack_blocks_kernel<64><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src,
+                                                             src_stride, group, idx, ld_idx, kpad,
+                                                             static_cast<uint16_t *>(dst), dst_stride, vec);
         return hipGetLastError();
     }
     const int64_t row_bytes = d * 2;

@@ -97,6 +97,7 @@ struct Plan {
     GemmConfig gc;
     int gsplits;
     int64_t a_rows;  // rows of the packed A buffer per batch entry
+    int64_t b_rows;  // rows of the packed B^T buffer per batch entry
     size_t off_part, off_s, off_idx, off_Ap, off_Bp, off_gpart, off_aval, total;
 };
 
@@ -189,13 +190,17 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
         p.off_part = take((size_t)p.cp.chunks * d * batch * 4);
         p.off_s = take((size_t)d * batch * 4);
     }
+    if (p.route == ROUTE_MFMA && gemm_choose(n, m, k, batch, d, ds->transB).tile == 3) p.kpad = 64;
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
     if (p.route == ROUTE_MFMA) {
         p.gc = gemm_choose(n, m, k, batch, d, ds->transB);
-        p.directA = p.shortcut && d % 128 == 0 && p.gc.tile != 2;
-        p.a_rows = p.gc.tile == 2 ? (n + 31) / 32 * 32 : n;  // operand blocks cover whole 32-row groups
+        const bool blocks = p.gc.tile >= 2;  // operands in MFMA operand blocks
+        if (p.gc.tile == 3) p.kpad = 64;     // single K step
+        p.directA = p.shortcut && d % 128 == 0 && !blocks;
+        p.a_rows = blocks ? (n + 31) / 32 * 32 : n;  // operand blocks cover whole 32-row groups
+        p.b_rows = p.gc.tile == 3 ? (m + 31) / 32 * 32 : m;
         if (!p.directA) p.off_Ap = take((size_t)batch * p.a_rows * p.kpad * 2);
-        if (ds->transB) p.off_Bp = take((size_t)batch * m * p.kpad * 2);
+        if (ds->transB) p.off_Bp = take((size_t)batch * p.b_rows * p.kpad * 2);
         if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * batch * n * m * 4);
     } else if (p.route == ROUTE_DECODE) {
         p.gsplits = gemv_splits(m, k);
@@ -389,7 +394,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
             gemm_idx = pidx;
         }
         RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(A, RMM_BF16, n, d, ds.lda, ds.strideA, 1, pidx, p.kpad, p.kpad, Ap,
-                                                p.a_rows * p.kpad, batch, p.gc.tile == 2 ? 1 : 0, stream));
+                                                p.a_rows * p.kpad, batch, p.gc.tile >= 2 ? 1 : 0, stream));
         g.A = Ap;
         g.lda = p.kpad;
         g.strideA = p.a_rows * p.kpad;
@@ -401,10 +406,11 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
             gemm_idx = pidx;
         }
         RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(B, RMM_BF16, m, d, ds.ldb, ds.strideB, ds.b_group, pidx, p.kpad,
-                                                p.kpad, Bp, m * p.kpad, batch, 0, stream));
+                                                p.kpad, Bp, p.b_rows * p.kpad, batch, p.gc.tile == 3 ? 1 : 0,
+                                                stream));
         g.B = Bp;
         g.ldb = p.kpad;
-        g.strideB = m * p.kpad;
+        g.strideB = p.b_rows * p.kpad;
         g.group = 1;
         g.bmode = 1;
         g.idx = nullptr;
@@ -429,7 +435,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     g.k = k;
     g.kpad = p.directA ? d : p.kpad;
     g.a_bytes = p.directA ? a_extent_bytes(desc) : p.a_rows * p.kpad * 2;
-    g.b_bytes = ds.transB ? m * p.kpad * 2 : b_extent_bytes(desc);
+    g.b_bytes = ds.transB ? p.b_rows * p.kpad * 2 : b_extent_bytes(desc);
     g.batch = batch;
     g.alpha = ds.alpha;
     g.splits = p.gc.splits;

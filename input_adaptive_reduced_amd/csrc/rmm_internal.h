@@ -21,6 +21,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return uint16_t(u >> 16);
 }
 
+// Two floats rounded to bf16 (nearest-even) and packed low/high into one
+// word with the hardware conversion: one v_cvt_pk_bf16_f32, bit-identical
+// to f32_to_bf16 for every finite input (NaN stays NaN).
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 rmm_bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float rmm_f32x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const rmm_f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, rmm_bf16x2_t));
+}
+
 // Order-preserving map from an fp32 score to an unsigned key (larger score ->
 // larger key).  -0 is folded onto +0 and every NaN onto +qNaN, which ranks
 // above +Inf.
@@ -105,7 +115,8 @@ struct GemmArgs {
     float alpha;
 };
 struct GemmConfig {
-    int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct)
+    int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
+                 // 3: persistent single-K-step kernel, both operands in operand blocks
     int splits;  // >= 1
 };
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);

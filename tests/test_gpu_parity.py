@@ -129,6 +129,14 @@ def test_small_attention(rmm):
         check_attention(rmm, case, Q, rho, heads=range(8), rows=None)
 
 
+def test_many_heads_ragged_attention(rmm):
+    # 128 query heads of 300 tokens: enough 256x256 tiles (512) for the
+    # persistent single-K-step kernel at rho = 0.5, with ragged tile edges
+    case, Q = attention_case(dict(heads=128, kv_heads=32, L=300))
+    for rho in case.rhos:
+        check_attention(rmm, case, Q, rho, heads=range(0, 128, 7), rows=None)
+
+
 def test_full_size_attention(rmm):
     case, Q = attention_case()
     rows = sample_rows(Q.shape[1], 6, seed=3)
