@@ -819,53 +819,54 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
     }
 }
 
-// Pack into MFMA operand blocks (layout 1).  One workgroup builds the output
-// of one 32-row block and TT (128, or 64 for short lists) consecutive kept
-// entries: TT/16 operand blocks written contiguously (each wave stores whole
-// 1 KB blocks).  The kept
-// source columns of those entries are ascending, so the workgroup stages the
-// source window [I[t0], I[t0+127]] of its 32 rows in LDS (in pieces of at
-// most kPackWin columns, 16-byte loads along the rows) and gathers from it.
-// Rows past `rows` and padding entries (index -1) are written as zero.
-constexpr int kPackWin = 512;             // source columns per staged window
-constexpr int kPackRowStride = kPackWin + 4;  // u16 per staged row (8-byte pad against bank conflicts)
+// Pack into MFMA operand blocks (layout 1).  The output of one 32-row block
+// and TT consecutive kept entries (a "tile": TT/16 operand blocks) is 2*TT
+// bytes per row, written contiguously (each wave stores whole 1 KB blocks).
+// Kept entries ascend, so a tile's source columns lie in the window
+// [first entry, last valid entry + 1) of its 32 rows.  A workgroup owns one
+// row block and a run of consecutive tiles and streams through them: while
+// it gathers tile i out of one LDS window buffer and writes it, the 16-byte
+// loads of tile i+1's window (and its index pieces) are already in flight
+// into registers, then land in the other buffer.  Loads are issued before
+// the stores of the same iteration, so waiting for them never waits for the
+// stores.  A tile whose window is wider than the buffer (kPackWinChunks
+// 16-byte chunks), or any tile when rows are not 16-byte aligned, gathers
+// straight from memory instead.  Rows past `rows` and padding entries
+// (index -1) are written as zero.
+constexpr int kPackWinChunks = 40;                      // window capacity: 320 source columns
+constexpr int kPackRowStride = kPackWinChunks * 8 + 8;  // u16 per staged row (16-byte pad)
+constexpr int kPackMaxTiles = 64;                       // tiles per workgroup
 
 template <int TT>
 __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__restrict__ src, int64_t rows, int64_t d,
                                                           int64_t ld_src, int64_t src_stride, int64_t group,
                                                           const int32_t *__restrict__ idx_all, int64_t ld_idx,
                                                           int64_t kpad, uint16_t *__restrict__ dst,
-                                                          int64_t dst_stride, int vec_ok) {
-    __shared__ uint16_t win[32 * kPackRowStride];
-    __shared__ int32_t span[2];
+                                                          int64_t dst_stride, int vec_ok, int tiles_per_wg) {
+    constexpr int PP = TT / 64;                        // output pieces per thread per tile
+    constexpr int WPT = (32 * kPackWinChunks + 255) / 256;  // window chunks per thread
+    __shared__ uint16_t win[2][32 * kPackRowStride];
+    __shared__ int32_t span_lo[kPackMaxTiles], span_hi[kPackMaxTiles];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    constexpr int PP = TT / 64;  // output pieces per thread
-    const int64_t rb = blockIdx.x, t0 = (int64_t)blockIdx.y * TT, b = blockIdx.z;
+    const int64_t rb = blockIdx.x, b = blockIdx.z;
+    const int ntiles_all = (int)(kpad / TT);
+    const int tt0 = (int)blockIdx.y * tiles_per_wg;
+    const int nt = min(tiles_per_wg, ntiles_all - tt0);
+    if (nt <= 0) return;
     const uint16_t *S = src + (b / group) * src_stride;
     const int32_t *idx = idx_all + b * ld_idx;
-    const int row = lane & 31;                // row within the block owned by this lane
+    uint16_t *D = dst + b * dst_stride;
+    const int row = lane & 31;  // row within the block owned by this lane
     const int64_t grow = rb * 32 + row;
     const bool row_ok = grow < rows;
     const int nrows = (int)max((int64_t)0, min((int64_t)32, rows - rb * 32));
 
-    // this thread's output pieces: block w + 4h, lane -> (row, chunk)
-    int32_t j[PP][8];
-#pragma unroll
-    for (int h = 0; h < PP; ++h) {
-        const int64_t c = 2 * (w + 4 * h) + (lane >> 5);  // chunk of 8 entries within the tile
-        const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8);
-        const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8 + 4);
-        j[h][0] = p0.x; j[h][1] = p0.y; j[h][2] = p0.z; j[h][3] = p0.w;
-        j[h][4] = p1.x; j[h][5] = p1.y; j[h][6] = p1.z; j[h][7] = p1.w;
-    }
-    // kept entries ascend and padding (-1) only trails, so the tile's source
-    // span is [first entry, last valid entry + 1).  Thread 0 holds the first
-    // entry and thread 255 the last; only the tile holding the end of the
-    // list searches for its last valid entry.
-    if (tid == 0) span[0] = j[0][0];
-    if (tid == 255) {
-        int32_t last = j[PP - 1][7];
-        if (last < 0 && idx[t0] >= 0) {
+    // source span of every tile of this run: [first entry, last valid + 1)
+    for (int q = tid; q < nt; q += 256) {
+        const int64_t t0 = (int64_t)(tt0 + q) * TT;
+        const int32_t lo = idx[t0];
+        int32_t last = idx[t0 + TT - 1];
+        if (last < 0 && lo >= 0) {
             int a = 0, z = TT - 1;
             while (a < z) {
                 const int mid = (a + z + 1) >> 1;
@@ -873,55 +874,96 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
             }
             last = idx[t0 + a];
         }
-        span[1] = last + 1;
+        span_lo[q] = lo;
+        span_hi[q] = lo >= 0 ? last + 1 : -1;
     }
     __syncthreads();
-    const int32_t lo = span[0], hi = span[1];
 
-    uint32_t hv[PP][8];
+    auto fits = [&](int q) {
+        const int32_t lo = span_lo[q];
+        return vec_ok && lo >= 0 && (span_hi[q] - (lo & ~7) + 7) / 8 <= kPackWinChunks;
+    };
+    // 16-byte loads of tile q's window (rows x chunks); chunk c of row r
+    // goes to register slot (r * chunks + c - tid) / 256
+    auto load_window = [&](int q, uint4 (&wr)[WPT]) {
+        if (!fits(q)) return;
+        const int32_t w0 = span_lo[q] & ~7;
+        const int chunks = (span_hi[q] - w0 + 7) / 8;  // d % 8 == 0: chunks stay inside the row
 #pragma unroll
-    for (int h = 0; h < PP; ++h)
+        for (int u = 0; u < WPT; ++u) {
+            const int e = tid + u * 256;
+            const int r = e / kPackWinChunks, c = e - r * kPackWinChunks;
+            if (r < nrows && c < chunks)
+                wr[u] = *reinterpret_cast<const uint4 *>(S + (rb * 32 + r) * ld_src + w0 + c * 8);
+        }
+    };
+    auto store_window = [&](int q, const uint4 (&wr)[WPT], uint16_t *buf) {
+        if (!fits(q)) return;
+        const int chunks = (span_hi[q] - (span_lo[q] & ~7) + 7) / 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hv[h][e] = 0;
-
-    if (lo >= 0 && nrows > 0) {
-        for (int64_t w0 = lo & ~7; w0 < hi; w0 += kPackWin) {
-            const int64_t wend = min(w0 + (int64_t)kPackWin, (int64_t)hi);
-            if (w0 != (lo & ~7)) __syncthreads();  // previous window fully consumed
-            if (vec_ok) {
-                const int chunks = (int)((wend - w0 + 7) / 8);  // d % 8 == 0: chunks stay inside the row
-                for (int q = tid; q < nrows * chunks; q += 256) {
-                    const int r = q / chunks, c = q - r * chunks;
-                    const uint4 v = *reinterpret_cast<const uint4 *>(S + (rb * 32 + r) * ld_src + w0 + c * 8);
-                    uint16_t *o = win + r * kPackRowStride + c * 8;
-                    *reinterpret_cast<uint2 *>(o) = make_uint2(v.x, v.y);
-                    *reinterpret_cast<uint2 *>(o + 4) = make_uint2(v.z, v.w);
-                }
-            } else {
-                const int cols = (int)(wend - w0);
-                for (int q = tid; q < nrows * cols; q += 256) {
-                    const int r = q / cols, c = q - r * cols;
-                    win[r * kPackRowStride + c] = S[(rb * 32 + r) * ld_src + w0 + c];
-                }
-            }
-            __syncthreads();
-            if (row_ok) {
-#pragma unroll
-                for (int h = 0; h < PP; ++h)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int32_t jj = j[h][e];
-                        if (jj >= w0 && jj < wend) hv[h][e] = win[row * kPackRowStride + (jj - w0)];
-                    }
+        for (int u = 0; u < WPT; ++u) {
+            const int e = tid + u * 256;
+            const int r = e / kPackWinChunks, c = e - r * kPackWinChunks;
+            if (r < nrows && c < chunks) {
+                uint16_t *o = buf + r * kPackRowStride + c * 8;
+                *reinterpret_cast<uint2 *>(o) = make_uint2(wr[u].x, wr[u].y);
+                *reinterpret_cast<uint2 *>(o + 4) = make_uint2(wr[u].z, wr[u].w);
             }
         }
-    }
+    };
+    // this thread's index pieces of tile q: block w + 4h, lane -> (row, chunk)
+    auto load_j = [&](int q, int32_t (&j)[PP][8]) {
+        const int64_t t0 = (int64_t)(tt0 + q) * TT;
 #pragma unroll
-    for (int h = 0; h < PP; ++h) {
-        const int64_t blk = rb * (kpad >> 4) + (t0 >> 4) + (w + 4 * h);
-        *reinterpret_cast<uint4 *>(dst + b * dst_stride + blk * 512 + lane * 8) =
-            make_uint4(hv[h][0] | (hv[h][1] << 16), hv[h][2] | (hv[h][3] << 16), hv[h][4] | (hv[h][5] << 16),
-                       hv[h][6] | (hv[h][7] << 16));
+        for (int h = 0; h < PP; ++h) {
+            const int64_t c = 2 * (w + 4 * h) + (lane >> 5);
+            const int4 p0 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8);
+            const int4 p1 = *reinterpret_cast<const int4 *>(idx + t0 + c * 8 + 4);
+            j[h][0] = p0.x; j[h][1] = p0.y; j[h][2] = p0.z; j[h][3] = p0.w;
+            j[h][4] = p1.x; j[h][5] = p1.y; j[h][6] = p1.z; j[h][7] = p1.w;
+        }
+    };
+
+    uint4 wr[WPT];
+    int32_t jc[PP][8], jn[PP][8];
+    load_window(0, wr);
+    load_j(0, jc);
+    store_window(0, wr, win[0]);
+    __syncthreads();
+    for (int q = 0; q < nt; ++q) {
+        if (q + 1 < nt) {
+            load_window(q + 1, wr);
+            load_j(q + 1, jn);
+        }
+        const uint16_t *buf = win[q & 1];
+        const bool fast = fits(q);
+        const int32_t w0 = span_lo[q] & ~7;
+        uint32_t hv[PP][8];
+#pragma unroll
+        for (int h = 0; h < PP; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int32_t jj = jc[h][e];
+                uint32_t v = 0;
+                if (row_ok && jj >= 0) v = fast ? buf[row * kPackRowStride + (jj - w0)] : S[grow * ld_src + jj];
+                hv[h][e] = v;
+            }
+        const int64_t t0 = (int64_t)(tt0 + q) * TT;
+#pragma unroll
+        for (int h = 0; h < PP; ++h) {
+            const int64_t blk = rb * (kpad >> 4) + (t0 >> 4) + (w + 4 * h);
+            *reinterpret_cast<uint4 *>(D + blk * 512 + lane * 8) =
+                make_uint4(hv[h][0] | (hv[h][1] << 16), hv[h][2] | (hv[h][3] << 16), hv[h][4] | (hv[h][5] << 16),
+                           hv[h][6] | (hv[h][7] << 16));
+        }
+        if (q + 1 < nt) {
+            store_window(q + 1, wr, win[(q + 1) & 1]);
+#pragma unroll
+            for (int h = 0; h < PP; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) jc[h][e] = jn[h][e];
+        }
+        __syncthreads();
     }
 }
 
@@ -1144,15 +1186,20 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
         if (kpad % 64 != 0) return hipErrorInvalidValue;
         const int vec = ((uintptr_t)src % 16 == 0) && (ld_src % 8 == 0) && (d % 8 == 0) && (src_stride % 8 == 0);
         const int tt = kpad % 128 == 0 ? 128 : 64;
-        dim3 grid((unsigned)((rows + 31) / 32), (unsigned)(kpad / tt), (unsigned)batch);
+        const int64_t ntiles = kpad / tt, rblocks = (rows + 31) / 32;
+        // runs of consecutive tiles per workgroup: about 768 workgroups in all
+        int64_t per = (ntiles * rblocks * batch + 767) / 768;
+        per = std::max<int64_t>(1, std::min<int64_t>(per, kPackMaxTiles));
+        if ((ntiles + per - 1) / per > 65535) per = std::min<int64_t>(kPackMaxTiles, (ntiles + 65534) / 65535);
+        dim3 grid((unsigned)rblocks, (unsigned)((ntiles + per - 1) / per), (unsigned)batch);
         if (tt == 128)
             pack_blocks_kernel<128><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src,
                                                               src_stride, group, idx, ld_idx, kpad,
-                                                              static_cast<uint16_t *>(dst), dst_stride, vec);
+                                                              static_cast<uint16_t *>(dst), dst_stride, vec, (int)per);
         else
             pack_blocks_kernel<64><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, d, ld_src,
                                                              src_stride, group, idx, ld_idx, kpad,
-                                                             static_cast<uint16_t *>(dst), dst_stride, vec);
+                                                             static_cast<uint16_t *>(dst), dst_stride, vec, (int)per);
         return hipGetLastError();
     }
     const int64_t row_bytes = d * 2;
