@@ -751,7 +751,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     const int64_t rc = q - b * plane;
     const int64_t row = rc / m, col = rc - row * m;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < splits; ++sp) {
+    int sp = 0;
+    // eight partial rows in flight, still added in ascending split order
+    for (; sp + 8 <= splits; sp += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4 *>(part + (int64_t)(sp + u) * total + q);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s.x += v[u].x;
+            s.y += v[u].y;
+            s.z += v[u].z;
+            s.w += v[u].w;
+        }
+    }
+    for (; sp < splits; ++sp) {
         const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * total + q);
         s.x += v.x;
         s.y += v.y;
@@ -762,6 +776,60 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     uint32_t lo = pack_bf16x2(alpha * s.x, alpha * s.y);
     uint32_t hi = pack_bf16x2(alpha * s.z, alpha * s.w);
     *reinterpret_cast<uint2 *>(y) = make_uint2(lo, hi);
+}
+
+// Same sum for many splits: 64 four-column groups x 4 split groups per
+// workgroup; split group g adds splits g, g+4, g+8, ... (ascending) with all
+// its loads in flight, then the four group sums are added in the order
+// 0, 1, 2, 3 (a fixed order, so results are bit-reproducible).
+__global__ __launch_bounds__(256) void splitk_reduce_wide_kernel(const float *__restrict__ part, int splits, int64_t n,
+                                                                 int64_t m, int64_t batch, float alpha,
+                                                                 uint16_t *__restrict__ Y, int64_t ldy,
+                                                                 int64_t strideY) {
+    __shared__ float4 red[4][64];
+    const int cq = threadIdx.x & 63, sg = threadIdx.x >> 6;
+    const int64_t q = ((int64_t)blockIdx.x * 64 + cq) * 4;
+    const int64_t plane = n * m;
+    const int64_t total = plane * batch;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < total) {
+        int sp = sg;
+        for (; sp + 12 < splits; sp += 16) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4 *>(part + (int64_t)(sp + 4 * u) * total + q);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
+        for (; sp < splits; sp += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)sp * total + q);
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+    }
+    red[sg][cq] = s;
+    __syncthreads();
+    if (sg != 0 || q >= total) return;
+    float4 t = red[0][cq];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) {
+        t.x += red[g][cq].x;
+        t.y += red[g][cq].y;
+        t.z += red[g][cq].z;
+        t.w += red[g][cq].w;
+    }
+    const int64_t b = q / plane;
+    const int64_t rc = q - b * plane;
+    const int64_t row = rc / m, col = rc - row * m;
+    uint16_t *y = Y + b * strideY + row * ldy + col;
+    *reinterpret_cast<uint2 *>(y) = make_uint2(pack_bf16x2(alpha * t.x, alpha * t.y), pack_bf16x2(alpha * t.z, alpha * t.w));
 }
 
 // ------------------------------------------------------------------ pack
@@ -1163,8 +1231,15 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,
                                 uint16_t *Y, int64_t ldy, int64_t strideY, hipStream_t stream) {
     const int64_t quads = n * m * batch / 4;
-    splitk_reduce_kernel<<<(unsigned)((quads + 255) / 256), 256, 0, stream>>>(part, splits, n, m, batch, alpha, Y,
-                                                                            ldy, strideY);
+    if (splits >= 16 && quads < (1 << 20)) {
+        splitk_reduce_wide_kernel<<<(unsigned)((quads + 63) / 64), 256, 0, stream>>>(part, splits, n, m, batch, alpha,
+                                                                                   Y, ldy, strideY);
+        return hipGetLastError();
+    }
+    // small outputs (decode rows) use 64-thread workgroups to spread over more CUs
+    const int bs = quads < 65536 ? 64 : 256;
+    splitk_reduce_kernel<<<(unsigned)((quads + bs - 1) / bs), bs, 0, stream>>>(part, splits, n, m, batch, alpha, Y,
+                                                                              ldy, strideY);
     return hipGetLastError();
 }
 
