@@ -79,6 +79,19 @@ def test_small_linear_all_rho(rmm, name, scale):
     check_linear(rmm, case, A, B64, 1.0, full_path=True)
 
 
+@pytest.mark.parametrize("scale", [dict(n=3100, d=1504, m=4000), dict(n=2050, d=4200, m=3080)],
+                         ids=["adirect", "adirect-splitk"])
+def test_ragged_large_tiles(rmm, scale):
+    # shapes that take the 256x256 operand-block kernel (the second with split
+    # K) with n not a multiple of 32 and m not a multiple of 256; sampled rows
+    # include the last rows of the ragged final row block
+    case, A, B64 = linear_case("c2", scale)
+    n = A.shape[0]
+    rows = sorted(set(sample_rows(n, 12, seed=5)) | {n - 1, n - 2, n - 17, n - 33})
+    for rho in (0.5, 0.8):
+        check_linear(rmm, case, A, B64, rho, rows=rows)
+
+
 @pytest.mark.parametrize("name", ["c2", "c3", "c5"])
 def test_full_size_linear(rmm, name):
     case, A, B64 = linear_case(name)
