@@ -124,6 +124,64 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
     }
 }
 
+// bf16 column sums of squares with every load of a thread issued up front:
+// thread (tx, ty) of a 256-thread workgroup owns eight columns and RPT rows
+// (ty, ty + tr, ...) of its strip x chunk; all RPT 16-byte loads are in
+// flight before the first multiply, so one memory round trip covers the
+// whole workgroup.  Rows past the chunk or past n read as zero (raw buffer
+// loads with an out-of-range offset).  Each column's sum still runs in row
+// order within a thread, then over row lanes in order through LDS.
+template <int RPT>
+__global__ __launch_bounds__(kNormThreads) void colnorm_rows_kernel(const uint16_t *__restrict__ A, int64_t n,
+                                                                    int64_t d, int64_t lda, int64_t strideA, int tc,
+                                                                    int64_t rows_per_chunk, int64_t a_bytes,
+                                                                    float *__restrict__ part,
+                                                                    unsigned *__restrict__ counter) {
+    __shared__ float red[kNormThreads * 8];
+    const int tid = threadIdx.x;
+    const int tx = tid % tc, ty = tid / tc, tr = kNormThreads / tc;
+    const int64_t b = blockIdx.z;
+    const int64_t j0 = (int64_t)blockIdx.x * tc * 8 + (int64_t)tx * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+    const int64_t r1 = min(n, r0 + rows_per_chunk);
+    if (counter && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) counter[b] = 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A + b * strideA), (short)0, (int)a_bytes, 0x00020000);
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (j0 + 8 <= d) {  // d % 8 == 0 on this path
+        uint4 v[RPT];
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const int64_t i = r0 + ty + (int64_t)q * tr;
+            const uint32_t off = i < r1 ? (uint32_t)((i * lda + j0) * 2) : 0x80000000u;
+            v[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        }
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float lo = __uint_as_float(w[h] << 16), hi = __uint_as_float(w[h] & 0xffff0000u);
+                acc[2 * h] = fmaf(lo, lo, acc[2 * h]);
+                acc[2 * h + 1] = fmaf(hi, hi, acc[2 * h + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[ty * tc * 8 + tx * 8 + e] = acc[e];
+    __syncthreads();
+    const int cols = tc * 8;
+    for (int c = tid; c < cols; c += kNormThreads) {
+        float sum = 0.f;
+        for (int y = 0; y < tr; ++y) sum += red[y * cols + c];
+        const int64_t j = (int64_t)blockIdx.x * cols + c;
+        if (j < d) part[(b * gridDim.y + blockIdx.y) * d + j] = sum;
+    }
+}
+
 // ------------------------------------------------------------------ block scan
 template <int BS>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sm, int &total) {
@@ -627,11 +685,28 @@ unsigned g_select_attr_done = 0;  // bit per device
 // activation block (7.4 us, 4.6 TB/s, against 13-15 us for 512-column strips).
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch) {
     const int V = dt == RMM_BF16 ? 8 : 4;
+    ColnormPlan p;
+    if (dt == RMM_BF16) {
+        // 128- or 256-column strips; rows per thread 8, 16 or 32, whichever
+        // first brings the grid to at most ~768 workgroups
+        int tc = d <= 4096 ? 16 : 32;
+        while (tc > 1 && (int64_t)tc * V / 2 >= d) tc /= 2;
+        const int tr = kNormThreads / tc;
+        p.tc = tc;
+        p.strips = (int)((d + (int64_t)tc * V - 1) / ((int64_t)tc * V));
+        int rpt = 8;
+        while (rpt < 32 && (int64_t)p.strips * batch * ((n + (int64_t)tr * rpt - 1) / ((int64_t)tr * rpt)) > 768)
+            rpt *= 2;
+        p.rpt = rpt;
+        p.rows_per_chunk = (int64_t)tr * rpt;
+        p.chunks = (int)((n + p.rows_per_chunk - 1) / p.rows_per_chunk);
+        return p;
+    }
     int tc = 16;
     while (tc > 1 && (int64_t)tc * V / 2 >= d) tc /= 2;
     const int tr = kNormThreads / tc;
-    ColnormPlan p;
     p.tc = tc;
+    p.rpt = 0;
     p.strips = (int)((d + (int64_t)tc * V - 1) / ((int64_t)tc * V));
     int64_t want = (1024 + (int64_t)p.strips * batch - 1) / ((int64_t)p.strips * batch);
     int64_t max_chunks = (n + 8 * tr - 1) / (8 * tr);
@@ -649,6 +724,22 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
     const int esz = dt == RMM_BF16 ? 2 : 4;
     const int V = 16 / esz;
     const int vec_ok = ((uintptr_t)A % 16 == 0) && (lda % V == 0) && (batch == 1 || strideA % V == 0);
+    const int64_t a_bytes = ((n - 1) * lda + d) * 2;  // one batch entry
+    if (dt == RMM_BF16 && p.rpt > 0 && vec_ok && d % 8 == 0 && a_bytes < 0x7fffffff) {
+        if (p.rpt == 8)
+            colnorm_rows_kernel<8><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
+                                                                       strideA, p.tc, p.rows_per_chunk, a_bytes, part,
+                                                                       counter);
+        else if (p.rpt == 16)
+            colnorm_rows_kernel<16><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
+                                                                        strideA, p.tc, p.rows_per_chunk, a_bytes, part,
+                                                                        counter);
+        else
+            colnorm_rows_kernel<32><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
+                                                                        strideA, p.tc, p.rows_per_chunk, a_bytes, part,
+                                                                        counter);
+        return hipGetLastError();
+    }
     if (dt == RMM_BF16)
         colnorm_partial_kernel<uint16_t><<<grid, kNormThreads, 0, stream>>>(
             static_cast<const uint16_t *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part, counter);

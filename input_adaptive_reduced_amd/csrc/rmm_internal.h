@@ -56,6 +56,7 @@ struct ColnormPlan {
     int strips;      // column strips
     int chunks;      // row chunks R
     int64_t rows_per_chunk;
+    int rpt;         // bf16: rows per thread with every load issued up front (0: looped kernel)
 };
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch);
 // `counter` (batch entries, may be null) is cleared for the finalize step.
