@@ -138,6 +138,10 @@ class Runner:
         rmm.matmul(self.A[i], self.B[i], rho, transB=self.transB, b_group=self.group, alpha=self.alpha,
                    out=self.Y[i], idx_out=self.idx[key], workspace=self.ws[key], full_path=full_path)
 
+    def plan(self, rho):
+        """Kernels the library picks for this workload (host-side query)."""
+        return self.rmm.plan_info(self.A[0], self.B[0], rho, transB=self.transB, b_group=self.group)
+
     def dense(self, i):
         """Dense bf16 product of the same shape (hipBLASLt through torch)."""
         torch = self.torch
@@ -317,7 +321,7 @@ def main(argv=None):
 
     kt = kernel_times(torch, rmm, runner, rho, args.kernel_steps, runner.copies)
     log("per-kernel mean us: " + ", ".join(f"{kk}={v[0] * 1e3:.1f}" for kk, v in kt.items() if v[1]))
-    stream = runner.transB and k <= 64 and runner.batch * ((runner.n + 255) // 256) * ((runner.m + 255) // 256) >= 512
+    stream = runner.plan(rho)["gemm"] == "stream"
     if runner.n == 1:
         dom, bound = "gemv", "hbm"
         gemv_ms = kt["gemv"][0]
@@ -340,7 +344,8 @@ def main(argv=None):
         dom = "gemm"
         gemm_ms = kt["gemm"][0]
         achieved = runner.flops(rho) / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "gemm_adirect", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "kernel": "gemm_" + runner.plan(rho)["gemm"], "achieved": achieved,
+                "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                 "algorithmic_flops": runner.flops(rho), "kernel_ms": gemm_ms}
     roof["traffic"] = load_traffic(dom, args.workload)

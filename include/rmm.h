@@ -145,6 +145,30 @@ void rmm_desc_init(rmm_desc_t *desc, rmm_dtype_t dtype, int64_t n, int64_t d, in
 size_t rmm_workspace_size(const rmm_desc_t *desc, double rho);
 
 /*
+ * Which kernels rmm_matmul would run for (desc, rho), decided on the host
+ * from sizes alone (alignment of the eventual pointers is assumed).  Writes
+ * info[0] = route (RMM_ROUTE_*), info[1] = reduced-product kernel
+ * (RMM_GEMM_*, -1 unless the route is RMM_ROUTE_MFMA), info[2] = number of
+ * K splits (1 = none; for the decode route, the GEMV's row splits).  For
+ * measurement tools and tests that want to know which kernel a shape takes;
+ * no GPU call.  Errors: RMM_ERR_INVALID_ARG for an invalid descriptor or rho
+ * or a NULL info.
+ */
+enum {
+    RMM_ROUTE_GENERIC = 0, /* fp32 or unaligned operands: FMA tile kernel */
+    RMM_ROUTE_MFMA = 1,    /* bf16 matrix-core product */
+    RMM_ROUTE_DECODE = 2   /* bf16 single row (n = 1): gathered GEMV */
+};
+enum {
+    RMM_GEMM_TILE256 = 0, /* 256x256 tiles, both operands staged in LDS */
+    RMM_GEMM_TILE128 = 1, /* 128x128 tiles (small or short products) */
+    RMM_GEMM_ADIRECT = 2, /* 256x256, A in operand blocks straight to registers */
+    RMM_GEMM_STREAM = 3,  /* persistent single-K-step kernel (scores Q K^T) */
+    RMM_GEMM_BDMA = 4     /* as ADIRECT, B rows staged by LDS-DMA loads */
+};
+rmm_status_t rmm_plan_info(const rmm_desc_t *desc, double rho, int32_t *info);
+
+/*
  * The whole reduced product  (Sec. 3.2, 3.3):
  *   1. s_j = ||A_b[:, j]||_2 for every batch entry b,
  *   2. I_b = TopK(s, k) with k = rmm_k(rho, d),

@@ -107,6 +107,8 @@ def load():
     L.rmm_workspace_size.restype = sz
     L.rmm_matmul.argtypes = [ctypes.POINTER(Desc), vp, vp, ctypes.c_double, vp, vp, vp, sz, vp]
     L.rmm_matmul.restype = ctypes.c_int
+    L.rmm_plan_info.argtypes = [ctypes.POINTER(Desc), ctypes.c_double, ctypes.POINTER(i32)]
+    L.rmm_plan_info.restype = ctypes.c_int
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
     L.rmm_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.rmm_timing_collect.restype = ctypes.c_int
@@ -242,6 +244,20 @@ def workspace_size(A, B, rho: float, transB: bool = False, b_group: int = 1, ful
     if w == ctypes.c_size_t(-1).value:
         raise RMMError(1, "rmm_workspace_size")
     return int(w)
+
+
+ROUTES = ("generic", "mfma", "decode")
+GEMM_KERNELS = ("tile256", "tile128", "adirect", "stream", "bdma")
+
+
+def plan_info(A, B, rho: float, transB: bool = False, b_group: int = 1, full_path: bool = False) -> dict:
+    """The kernels ``matmul`` would run for these operands (host-side, from
+    shapes, strides and dtype only: tensors on the ``meta`` device will do)."""
+    ds, _ = _desc_for(A, B, transB, b_group, 1.0, full_path)
+    info = (ctypes.c_int32 * 3)()
+    _check(load().rmm_plan_info(ctypes.byref(ds), float(rho), info), "rmm_plan_info")
+    return {"route": ROUTES[info[0]], "gemm": GEMM_KERNELS[info[1]] if info[1] >= 0 else None,
+            "splits": int(info[2])}
 
 
 def matmul(A, B, rho: float, *, transB: bool = False, b_group: int = 1, alpha: float = 1.0,

@@ -603,6 +603,65 @@ __global__ __launch_bounds__(BS) void select_kernel(const void *__restrict__ src
                         sel_out, reinterpret_cast<float *>(sel_out + k));
 }
 
+// Norms and selection in one workgroup per batch entry, straight from the
+// row-chunk partials: thread t owns columns [t*E, t*E + E), issues every
+// partial load of its columns up front (16-byte buffer loads; columns past d
+// and chunks past the last read as zero), adds the chunks in ascending order,
+// takes the correctly rounded square root and runs block_select on the
+// register-resident keys.  This replaces a finalize launch plus a select
+// launch when the partials are few (norm_select_ok).
+template <int E>
+__global__ __launch_bounds__(1024) void norm_select_kernel(const float *__restrict__ part_all, int chunks, int d,
+                                                           int k, int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                           int32_t *__restrict__ pad_all, int64_t ld_pad) {
+    constexpr int BS = 1024, Q = E / 4, U = 8 / Q;  // 8 loads in flight per thread
+    __shared__ SelectShared<BS> sh;
+    extern __shared__ int32_t sel_out[];
+    const int64_t b = blockIdx.x;
+    const float *part = part_all + b * (int64_t)chunks * d;
+    const __amdgpu_buffer_rsrc_t r = sel_rsrc(part, (int64_t)chunks * d * 4);
+    const int j0 = threadIdx.x * E;
+    const int nv = max(0, min(E, d - j0));
+    // offsets past the buffer (at most 4 MB here) read as zero; columns past d
+    // must not read the next chunk's row, so they and chunks past the last
+    // get 2^30 added (both: 2^31), which is out of range
+    constexpr uint32_t kFar = 0x40000000u;
+    uint32_t base[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) base[q] = j0 + 4 * q < d ? (uint32_t)(j0 + 4 * q) * 4u : kFar;
+    float sum[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) sum[e] = 0.f;
+    for (int c0 = 0; c0 < chunks; c0 += U) {
+        uint4 v[U][Q];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t co = c0 + u < chunks ? (uint32_t)(c0 + u) * (uint32_t)d * 4u : kFar;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+                v[u][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, base[q] + co, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                sum[4 * q] += __uint_as_float(v[u][q].x);
+                sum[4 * q + 1] += __uint_as_float(v[u][q].y);
+                sum[4 * q + 2] += __uint_as_float(v[u][q].z);
+                sum[4 * q + 3] += __uint_as_float(v[u][q].w);
+            }
+    }
+    float vals[E];
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        vals[e] = __fsqrt_rn(sum[e]);
+        key[e] = score_key(vals[e]);
+    }
+    block_select<BS, E>(sh, key, nv, j0, k, idx_all ? idx_all + b * ld_idx : nullptr,
+                        pad_all ? pad_all + b * ld_pad : nullptr, ld_pad, nullptr, vals, sel_out, nullptr);
+}
+
 // Final column norms, and (with `counter`) the selection in the same launch.
 // 64 columns per workgroup, 16 row-chunk groups per column: group g sums the
 // chunks g, g+16, ... in ascending order (four loads in flight), the 16 group
@@ -676,6 +735,7 @@ __global__ void iota_kernel(int32_t *idx, int64_t k, int64_t ld, int64_t total) 
 }
 
 unsigned g_select_attr_done = 0;  // bit per device
+unsigned g_norm_select_attr_done = 0;
 
 }  // namespace
 
@@ -755,6 +815,22 @@ hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d,
     dim3 grid((unsigned)((d + 63) / 64), (unsigned)batch);
     finalize_select_kernel<<<grid, 1024, counter ? (size_t)k * 4 : 0, stream>>>(part, chunks, (int)d, s, counter, (int)k,
                                                                                 idx, ld_idx, idx_pad, ld_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_select(const float *part, int64_t chunks, int64_t d, int64_t batch, int64_t k, int32_t *idx,
+                              int64_t ld_idx, int32_t *idx_pad, int64_t ld_pad, hipStream_t stream) {
+    if (!norm_select_ok(chunks, d) || ((uintptr_t)part & 15)) return hipErrorInvalidValue;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (dev < 32 && !(g_norm_select_attr_done & (1u << dev))) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&norm_select_kernel<4>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+        if (e != hipSuccess) return e;
+        g_norm_select_attr_done |= 1u << dev;
+    }
+    norm_select_kernel<4><<<(unsigned)batch, 1024, (size_t)k * 4, stream>>>(part, (int)chunks, (int)d, (int)k, idx,
+                                                                            ld_idx, idx_pad, ld_pad);
     return hipGetLastError();
 }
 

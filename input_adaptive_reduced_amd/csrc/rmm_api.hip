@@ -300,6 +300,18 @@ size_t rmm_workspace_size(const rmm_desc_t *desc, double rho) {
     return make_plan(desc, k, nullptr, nullptr, nullptr).total;
 }
 
+rmm_status_t rmm_plan_info(const rmm_desc_t *desc, double rho, int32_t *info) {
+    int64_t ea, eb, ey;
+    if (!info || check_desc(desc, ea, eb, ey) != RMM_OK) return RMM_ERR_INVALID_ARG;
+    const int64_t k = k_of(rho, desc->d);
+    if (k < 1) return RMM_ERR_INVALID_ARG;
+    const Plan p = make_plan(desc, k, nullptr, nullptr, nullptr);
+    info[0] = p.route;
+    info[1] = p.route == ROUTE_MFMA ? p.gc.tile : -1;
+    info[2] = p.route == ROUTE_MFMA ? p.gc.splits : p.route == ROUTE_DECODE ? p.gsplits : 1;
+    return RMM_OK;
+}
+
 rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,
                         int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream) {
     int64_t extA, extB, extY;
@@ -348,10 +360,15 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         float *s = reinterpret_cast<float *>(ws + p.off_s);
         RMM_LAUNCH(RMM_KERNEL_COLNORM,
                    launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, nullptr, stream));
-        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, nullptr, 0, nullptr, 0,
-                                                                nullptr, 0, stream));
-        RMM_LAUNCH(RMM_KERNEL_SELECT,
-                   launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, pidx, p.kpad, nullptr, stream));
+        if (norm_select_ok(p.cp.chunks, d)) {
+            RMM_LAUNCH(RMM_KERNEL_SELECT, launch_norm_select(part, p.cp.chunks, d, batch, k, idx_out, k, pidx, p.kpad,
+                                                             stream));
+        } else {
+            RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, nullptr, 0, nullptr,
+                                                                    0, nullptr, 0, stream));
+            RMM_LAUNCH(RMM_KERNEL_SELECT,
+                       launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, pidx, p.kpad, nullptr, stream));
+        }
     }
 
     if (p.route == ROUTE_GENERIC) {

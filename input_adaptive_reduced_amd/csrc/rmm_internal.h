@@ -73,6 +73,17 @@ hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d,
                                    unsigned *counter, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad,
                                    int64_t ld_pad, hipStream_t stream);
 constexpr int64_t kFusedSelectMaxD = 16384;
+// Norms from the row-chunk partials and the selection in one launch (one
+// workgroup per batch entry, every partial load in flight at once).  One
+// workgroup reads all chunks x d partials, so this pays only while they are
+// few: d <= 4096 and at most 256 KB of partials (beyond that, on MI355X, a
+// wide finalize launch plus the selection launch is faster).  d % 4 == 0,
+// part 16-byte aligned.
+inline bool norm_select_ok(int64_t chunks, int64_t d) {
+    return d <= 4096 && d % 4 == 0 && chunks * d <= 65536;
+}
+hipError_t launch_norm_select(const float *part, int64_t chunks, int64_t d, int64_t batch, int64_t k, int32_t *idx,
+                              int64_t ld_idx, int32_t *idx_pad, int64_t ld_pad, hipStream_t stream);
 
 // Exact TopK by radix select; rows of idx (ld_idx apart) and of idx_pad
 // (ld_pad apart, entries k..ld_pad-1 set to -1) receive the kept indices in
@@ -117,7 +128,8 @@ struct GemmArgs {
 };
 struct GemmConfig {
     int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
-                 // 3: persistent single-K-step kernel, both operands in operand blocks
+                 // 3: persistent single-K-step kernel, both operands in operand blocks,
+                 // 4: as 2 with B rows staged by LDS-DMA loads (gemm_bdma_kernel)
     int splits;  // >= 1
 };
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);

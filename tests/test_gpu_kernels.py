@@ -107,6 +107,10 @@ ODD = [
     (64, 4096, 64, "bf16", 1 / 4096, "k = 1"),
     (33, 65, 72, "bf16", 0.999, "k = d - 0 (ceil)"),
     (2, 100, 8, "bf16", 0.07, "rho*d just above an integer"),
+    # norms finalized in their own launch before the selection: d above the
+    # one-workgroup norm+select kernel, and more row chunks than it takes
+    (64, 20480, 64, "bf16", 0.5, "d above the fused selection"),
+    (65536, 256, 64, "bf16", 0.5, "many row chunks"),
 ]
 
 

@@ -32,12 +32,12 @@ def rmm():
 _CACHE = {}
 
 
-def linear_case(name, scale=None):
-    key = (name, tuple(sorted((scale or {}).items())))
+def linear_case(name, scale=None, rhos=None):
+    key = (name, tuple(sorted((scale or {}).items())), rhos)
     if key not in _CACHE:
         case = synthetic.make_case(name, scale)
         d = case.A.shape[1]
-        ks = [oracle.k_of(r, d) for r in case.rhos]
+        ks = [oracle.k_of(r, d) for r in (rhos or case.rhos)]
         A, _ = enforce_gap(case.A, ks, case.dtype)
         _CACHE[key] = (case, A, np.ascontiguousarray(case.B, dtype=np.float64))
     return _CACHE[key]
@@ -79,17 +79,34 @@ def test_small_linear_all_rho(rmm, name, scale):
     check_linear(rmm, case, A, B64, 1.0, full_path=True)
 
 
-@pytest.mark.parametrize("scale", [dict(n=3100, d=1504, m=4000), dict(n=2050, d=4200, m=3080)],
-                         ids=["adirect", "adirect-splitk"])
-def test_ragged_large_tiles(rmm, scale):
-    # shapes that take the 256x256 operand-block kernel (the second with split
-    # K) with n not a multiple of 32 and m not a multiple of 256; sampled rows
-    # include the last rows of the ragged final row block
-    case, A, B64 = linear_case("c2", scale)
+RAGGED = [
+    # (scale, rho, kernel, split K): the 256x256 operand-block kernels with n
+    # not a multiple of 32 and m not a multiple of 256.  bdma rounds each
+    # split's K steps up to a multiple of three with zero steps: 104 -> 105
+    # steps at d = 8200, and 16 -> 18 in the last of two splits at d = 4200,
+    # rho = 0.5.
+    (dict(n=3100, d=1504, m=4000), 0.5, "bdma", False),
+    (dict(n=3100, d=8200, m=4000), 0.8, "bdma", False),
+    (dict(n=2050, d=4200, m=3080), 0.5, "bdma", True),
+    (dict(n=2050, d=4200, m=3080), 0.8, "bdma", True),
+    (dict(n=3100, d=1504, m=4000), 0.8, "adirect", False),
+    (dict(n=2050, d=4200, m=3080), 0.48, "adirect", True),
+]
+
+
+@pytest.mark.parametrize("scale,rho,kernel,split", RAGGED,
+                         ids=[f"{k}{'-splitk' if s else ''}-d{c['d']}-rho{r}" for c, r, k, s in RAGGED])
+def test_ragged_large_tiles(rmm, scale, rho, kernel, split):
+    # sampled rows include the last rows of the ragged final row block
+    torch = pytest.importorskip("torch")
+    case, A, B64 = linear_case("c2", scale, rhos=(rho,))
     n = A.shape[0]
     rows = sorted(set(sample_rows(n, 12, seed=5)) | {n - 1, n - 2, n - 17, n - 33})
-    for rho in (0.5, 0.8):
-        check_linear(rmm, case, A, B64, rho, rows=rows)
+    Am = torch.empty(A.shape, dtype=torch.bfloat16, device="meta")
+    Bm = torch.empty(case.B.shape, dtype=torch.bfloat16, device="meta")
+    info = rmm.plan_info(Am, Bm, rho)
+    assert info["gemm"] == kernel and (info["splits"] > 1) == split, info
+    check_linear(rmm, case, A, B64, rho, rows=rows)
 
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c5"])

@@ -1,0 +1,79 @@
+"""Host-side check of an ordering argument the LDS-DMA product kernel relies on.
+
+gemm_bdma_kernel waits for its own LDS-DMA loads of the next K step with
+``s_waitcnt vmcnt(28)``: vector-memory loads retire in issue order, so the
+wait covers those loads only if at least 28 loads are issued after the last
+of them and before the wait.  The kernel fences its sub-steps with scheduling
+barriers so that this holds by construction; this test compiles the kernel
+to gfx950 assembly and checks it in every loop that contains the wait.  No
+GPU is used.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "input_adaptive_reduced_amd", "csrc")
+
+
+def loop_sequences(asm: str, kernel: str):
+    lines = asm.split("\n")
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*" + kernel + r"\S*:", l))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    body = lines[start:end]
+    for h, l in enumerate(body):
+        if "Loop Header" not in l:
+            continue
+        stop = next((i for i in range(h + 1, len(body))
+                     if body[i].startswith(".LBB") and "in Loop" not in body[i]), len(body))
+        seq = []
+        for x in body[h:stop]:
+            x = x.strip()
+            if x.startswith(("buffer_load", "global_load")):
+                seq.append("D" if " lds" in x else "A")
+            elif x.startswith("s_waitcnt") and "vmcnt(28)" in x:
+                seq.append("W")
+        if "W" in seq:
+            yield seq
+
+
+def min_younger(seq):
+    """Fewest loads issued after the previous step's last DMA load and before
+    each wait, around the loop (the sequence repeats)."""
+    s2 = seq * 2
+    waits = [i for i, c in enumerate(s2) if c == "W"]
+    worst = None
+    for a, b in zip(waits, waits[1:]):
+        dma = [i for i in range(a) if s2[i] == "D"]
+        if not dma:
+            continue
+        n = sum(1 for i in range(dma[-1] + 1, b) if s2[i] in "AD")
+        worst = n if worst is None else min(worst, n)
+    return worst
+
+
+def test_min_younger_counts_loads_after_the_previous_steps_dma():
+    # each wait needs the DMA loads issued before the previous wait: after
+    # the last of them come 3 A loads, 2 DMA loads and 3 A loads
+    assert min_younger(list("DDAAAWDDAAAW")) == 8
+    # DMA right before each wait: only the next step's two DMA loads follow
+    assert min_younger(list("DDWDDW")) == 2
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
+def test_bdma_wait_covers_its_dma(tmp_path):
+    out = tmp_path / "gemm.s"
+    cmd = ["hipcc", "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(CSRC, "gemm.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    asm = out.read_text()
+    for split in ("0", "1"):
+        seqs = list(loop_sequences(asm, "gemm_bdma_kernelILb" + split))
+        assert seqs, "no loop with the DMA wait found"
+        for seq in seqs:
+            assert seq.count("W") % 3 == 0
+            assert min_younger(seq) >= 28, "".join(seq)
