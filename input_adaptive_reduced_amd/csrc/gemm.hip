@@ -1250,6 +1250,63 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
     }
 }
 
+// Pack of short rows (d <= 128: attention head dimensions) into MFMA
+// operand blocks.  A workgroup takes 256 consecutive rows; its 256 threads
+// read them with coalesced 16-byte loads (all issued up front) into LDS rows
+// padded to an odd number of 8-byte words, then thread r gathers the kept
+// entries of row r (the same columns for every row, so a wave's 64 reads of
+// one entry hit 64 rows: at most two lanes per bank) and writes its 16-byte
+// pieces; for one piece the 32 rows of a block are 512 contiguous bytes.
+// Rows past `rows` and padding entries (index -1) are written as zero.
+template <int D>
+__global__ __launch_bounds__(256) void pack_short_rows_kernel(const uint16_t *__restrict__ src, int64_t rows,
+                                                              int64_t ld_src, int64_t src_stride, int64_t group,
+                                                              const int32_t *__restrict__ idx_all, int64_t ld_idx,
+                                                              int64_t kpad, uint16_t *__restrict__ dst,
+                                                              int64_t dst_stride) {
+    constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int STRIDE = D / 4 + 1;    // 8-byte words per LDS row (odd)
+    constexpr int PER = CPR;             // chunk loads per thread (256 rows x CPR chunks / 256)
+    __shared__ uint2 rowl[256 * STRIDE];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t r0 = (int64_t)blockIdx.x * 256;
+    const uint16_t *S = src + (b / group) * src_stride;
+    const int32_t *idx = idx_all + b * ld_idx;
+    uint16_t *Dp = dst + b * dst_stride;
+    const int nr = (int)min((int64_t)256, rows - r0);
+
+    uint4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = u * 256 + tid;  // chunk e: row e / CPR, chunk e % CPR
+        const int r = e / CPR, c = e % CPR;
+        v[u] = r < nr ? *reinterpret_cast<const uint4 *>(S + (r0 + r) * ld_src + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = u * 256 + tid;
+        const int r = e / CPR, c = e % CPR;
+        rowl[r * STRIDE + 2 * c] = make_uint2(v[u].x, v[u].y);
+        rowl[r * STRIDE + 2 * c + 1] = make_uint2(v[u].z, v[u].w);
+    }
+    __syncthreads();
+    const uint16_t *mine = reinterpret_cast<const uint16_t *>(rowl + tid * STRIDE);
+    const int64_t row = r0 + tid;
+    const int64_t blk = row >> 5;
+    if (row >= ((rows + 31) & ~(int64_t)31)) return;  // past the last 32-row block of the output
+    for (int c = 0; c < (int)(kpad / 8); ++c) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int32_t j = idx[c * 8 + e];  // uniform: scalar load
+            h[e] = (j >= 0 && tid < nr) ? mine[j] : 0u;
+        }
+        *reinterpret_cast<uint4 *>(Dp + ((blk * (kpad >> 4) + (c >> 1)) * 64 + (c & 1) * 32 + (row & 31)) * 8) =
+            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+}
+
 // ------------------------------------------------------------------ generic SIMT path
 template <typename T>
 struct Elem;
@@ -1499,6 +1556,19 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
     if (layout != 0) {
         if (kpad % 64 != 0) return hipErrorInvalidValue;
         const int vec = ((uintptr_t)src % 16 == 0) && (ld_src % 8 == 0) && (d % 8 == 0) && (src_stride % 8 == 0);
+        if (vec && (d == 64 || d == 128) && (uintptr_t)dst % 16 == 0) {
+            // padded output rows: whole 32-row blocks, written by the 256-row workgroups
+            dim3 grid((unsigned)((rows + 255) / 256), (unsigned)batch);
+            if (d == 64)
+                pack_short_rows_kernel<64><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, ld_src,
+                                                                     src_stride, group, idx, ld_idx, kpad,
+                                                                     static_cast<uint16_t *>(dst), dst_stride);
+            else
+                pack_short_rows_kernel<128><<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(src), rows, ld_src,
+                                                                      src_stride, group, idx, ld_idx, kpad,
+                                                                      static_cast<uint16_t *>(dst), dst_stride);
+            return hipGetLastError();
+        }
         const int tt = kpad % 128 == 0 ? 128 : 64;
         const int64_t ntiles = kpad / tt, rblocks = (rows + 31) / 32;
         // runs of consecutive tiles per workgroup: about 768 workgroups in all
