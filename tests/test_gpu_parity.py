@@ -209,3 +209,44 @@ def test_decode_exact_ties(rmm):
         B64 = B.astype(np.float64)
         assert_close(to_host(Y), oracle.reduced_product(a, B64, ref_idx),
                      oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx), k, "bf16", f"ties k={k}")
+
+
+BATCHED = [
+    # (batch, n, d, m, group, rhos, rows sampled per entry or None for all)
+    (8, 300, 520, 136, 4, (0.5, 0.8), None),
+    (8, 1024, 2048, 1536, 2, (0.5, 0.8), 6),
+]
+
+
+@pytest.mark.parametrize("batch,n,d,m,group,rhos,nrows", BATCHED, ids=["small", "large-tiles"])
+def test_batched_grouped_linear(rmm, batch, n, d, m, group, rhos, nrows):
+    """Batched products with B shared by `group` consecutive entries and not
+    transposed: one selection per entry (the token-axis shape P V of Sec. 3.3,
+    with P as A and the GQA value head as B)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(batch * 1000 + d)
+    A = np.stack([synthetic.lognormal_outlier_activations(rng, n, d, "bf16", n_outliers=3)[0]
+                  for _ in range(batch)])
+    B = np.stack([synthetic.gaussian_weights(rng, d, m, "bf16") for _ in range(batch // group)])
+    A, _ = enforce_gap_batched(A, [oracle.k_of(r, d) for r in rhos], "bf16")
+    Ad, Bd = to_device(A, "bf16"), to_device(B, "bf16")
+    for rho in rhos:
+        k = oracle.k_of(rho, d)
+        info = rmm.plan_info(Ad, Bd, rho, b_group=group)
+        assert info["route"] == "mfma", info
+        if nrows is not None:
+            assert info["gemm"] in ("adirect", "bdma"), info
+        Y, idx = rmm.matmul(Ad, Bd, rho, b_group=group)
+        torch.cuda.synchronize()
+        got_idx = idx.cpu().numpy()
+        for b in range(batch):
+            ref_idx = oracle.topk(oracle.colnorm(A[b]), k)
+            assert np.array_equal(got_idx[b], ref_idx), f"entry {b} rho={rho}: index sets differ"
+            rows = None if nrows is None else sample_rows(n, nrows, seed=b)
+            B64 = B[b // group].astype(np.float64)
+            Yh = to_host(Y[b])
+            if rows is not None:
+                Yh = Yh[rows]
+            assert_close(Yh, oracle.reduced_product(A[b], B64, ref_idx, 1.0, rows),
+                         oracle.reduced_product(np.abs(A[b]), np.abs(B64), ref_idx, 1.0, rows), k, "bf16",
+                         f"batched entry {b} rho={rho}")
