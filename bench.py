@@ -49,7 +49,7 @@ WORKLOADS = {
                label="Llama-3.1-70B-shaped MLP up projection: A 4096x8192 bf16 x B 8192x28672 bf16"),
     "c5-decode": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), decode=True,
                       label="70B up projection decode: a 1x8192 bf16 x B 8192x28672 bf16"),
-    "c4": dict(case="c4", rho=0.5, sweep=(0.5, 1.0),
+    "c4": dict(case="c4", rho=0.5, sweep=(0.5, 0.8, 1.0),
                label="QK^T with head-dim selection: Q 32x4096x128, K 8 GQA heads x4096x128 bf16"),
 }
 

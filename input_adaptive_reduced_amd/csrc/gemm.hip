@@ -809,14 +809,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
     store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
-// Reduced product for a single 64-entry K step (kpad = 64), both operands
-// in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I], i.e. the
-// kept columns of the keys for Q K^T).  Such products are bound by writing
-// Y (62 flop per output byte at k = 64), so the kernel is persistent and
+// Reduced product for one or two 64-entry K steps (kpad = 64 or 128), both
+// operands in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I],
+// i.e. the kept columns of the keys for Q K^T).  Such products are bound by
+// writing Y (62 or 124 flop per output byte), so the kernel is persistent and
 // splits each workgroup into two roles:
-//  * waves 0-3 compute: each owns 128 rows x 64 columns of a 256x128 output
-//    tile, rounds its results to bf16 and writes them into one of two LDS
-//    stage buffers;
+//  * waves 0-3 compute: each owns WTM rows x 64 columns of a BM x 128 output
+//    tile (KS = kpad / 16 sub-steps: BM = 256 for kpad 64, 128 for kpad 128,
+//    so the operand registers of a panel fit), rounds its results to bf16
+//    and writes them into one of two LDS stage buffers;
 //  * waves 4-7 store: one workgroup barrier per tile later they copy the
 //    staged tile to Y, 16 lanes writing 256 contiguous bytes of a row.
 // A workgroup walks whole row panels (one batch entry, 256 rows, every
@@ -826,11 +827,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
 // stores, which run at HBM speed; keeping them few is what keeps the compute
 // waves ahead of the stores.  Panels are dealt to workgroups in contiguous
 // runs, and runs to XCDs in order, so each XCD's L2 serves few batch entries.
-// Stage layout: 256 rows x 16 chunks of 16 bytes, chunk c of row r at
+// Stage layout: BM rows x 16 chunks of 16 bytes, chunk c of row r at
 // c ^ (r & 15).
+template <int KS>
 __global__ __launch_bounds__(512, 1) void gemm_stream_kernel(GemmArgs g) {
-    constexpr int BM = 256, BN = 128, WTM = 128, WTN = 64, FM = 4, FN = 2, KS = 4, CPR = BN / 8;
-    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB
+    constexpr int BM = KS == 4 ? 256 : 128, BN = 128, WTM = BM / 2, WTN = 64, FM = WTM / 32, FN = 2, CPR = BN / 8;
+    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB (kpad 64) or 2 x 32 KB (kpad 128)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const bool compute = w < 4;
     const int wm = (w & 3) >> 1, wn = w & 1;
@@ -940,10 +942,10 @@ __global__ __launch_bounds__(512, 1) void gemm_stream_kernel(GemmArgs g) {
             const int64_t m0 = tm * BM, n0 = tn * BN;
             const uint4 *stg = stageL[(q - 1) & 1];
             uint16_t *Yb = g.Y + b * g.strideY;
-            const int sw = w - 4;  // rows 64 sw .. 64 sw + 63 of the tile
+            const int sw = w - 4;  // rows (BM/4) sw .. (BM/4) sw + BM/4 - 1 of the tile
 #pragma unroll 4
-            for (int it = 0; it < 16; ++it) {
-                const int r = sw * 64 + it * 4 + (lane >> 4);
+            for (int it = 0; it < BM / 16; ++it) {
+                const int r = sw * (BM / 4) + it * 4 + (lane >> 4);
                 const int c = lane & 15;
                 const uint4 v = stg[r * CPR + (c ^ (r & 15))];
                 const int64_t row = m0 + r, col = n0 + c * 8;
@@ -1421,8 +1423,8 @@ static bool bdma_ok(int64_t kpad, int splits, int64_t d, int transB) {
 }
 
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB) {
-    if (transB && k <= BK && ((n + 255) / 256) * ((m + 255) / 256) * batch >= 512) {
-        // one K step, many tiles (scores Q K^T): write-bound streaming kernel
+    if (transB && k <= 2 * BK && ((n + 255) / 256) * ((m + 255) / 256) * batch >= 512) {
+        // one or two K steps, many tiles (scores Q K^T): write-bound streaming kernel
         GemmConfig c;
         c.tile = 3;
         c.splits = 1;
@@ -1493,14 +1495,18 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
     GemmArgs a = g;
     a.splits = c.splits;
     if (c.tile == 3) {
-        if (a.kpad != BK || a.splits != 1) return hipErrorInvalidValue;
+        if ((a.kpad != BK && a.kpad != 2 * BK) || a.splits != 1) return hipErrorInvalidValue;
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 256;
-        const int64_t panels = ((a.n + 255) / 256) * a.batch;
+        const int bm = a.kpad == BK ? 256 : 128;
+        const int64_t panels = ((a.n + bm - 1) / bm) * a.batch;
         const unsigned grid = (unsigned)std::min<int64_t>(panels, (int64_t)cus);
-        gemm_stream_kernel<<<grid, 512, 0, stream>>>(a);
+        if (a.kpad == BK)
+            gemm_stream_kernel<4><<<grid, 512, 0, stream>>>(a);
+        else
+            gemm_stream_kernel<8><<<grid, 512, 0, stream>>>(a);
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {

@@ -190,12 +190,13 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
         p.off_part = take((size_t)p.cp.chunks * d * batch * 4);
         p.off_s = take((size_t)d * batch * 4);
     }
-    if (p.route == ROUTE_MFMA && gemm_choose(n, m, k, batch, d, ds->transB).tile == 3) p.kpad = 64;
+    // the streaming kernel runs one or two whole 64-entry K steps
+    if (p.route == ROUTE_MFMA && gemm_choose(n, m, k, batch, d, ds->transB).tile == 3) p.kpad = k <= 64 ? 64 : 128;
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
     if (p.route == ROUTE_MFMA) {
         p.gc = gemm_choose(n, m, k, batch, d, ds->transB);
         const bool blocks = p.gc.tile >= 2;  // operands in MFMA operand blocks
-        if (p.gc.tile == 3) p.kpad = 64;     // single K step
+        if (p.gc.tile == 3) p.kpad = k <= 64 ? 64 : 128;
         p.directA = p.shortcut && d % 128 == 0 && !blocks;
         p.a_rows = blocks ? (n + 31) / 32 * 32 : n;  // operand blocks cover whole 32-row groups
         p.b_rows = p.gc.tile == 3 ? (m + 31) / 32 * 32 : m;

@@ -117,12 +117,12 @@ def test_full_size_linear(rmm, name):
         check_linear(rmm, case, A, B64, rho, rows=rows)
 
 
-def attention_case(scale=None):
-    key = ("c4", tuple(sorted((scale or {}).items())))
+def attention_case(scale=None, rhos=None):
+    key = ("c4", tuple(sorted((scale or {}).items())), rhos)
     if key not in _CACHE:
         case = synthetic.make_case("c4", scale)
         dh = case.A.shape[2]
-        Q, _ = enforce_gap_batched(case.A, [oracle.k_of(r, dh) for r in case.rhos], "bf16")
+        Q, _ = enforce_gap_batched(case.A, [oracle.k_of(r, dh) for r in (rhos or case.rhos)], "bf16")
         _CACHE[key] = (case, Q)
     return _CACHE[key]
 
@@ -159,12 +159,32 @@ def test_small_attention(rmm):
         check_attention(rmm, case, Q, rho, heads=range(8), rows=None)
 
 
+def stream_plan(rmm, case, Q, rho):
+    torch = pytest.importorskip("torch")
+    Qm = torch.empty(Q.shape, dtype=torch.bfloat16, device="meta")
+    Km = torch.empty(case.B.shape, dtype=torch.bfloat16, device="meta")
+    return rmm.plan_info(Qm, Km, rho, transB=True, b_group=case.A.shape[0] // case.B.shape[0])
+
+
 def test_many_heads_ragged_attention(rmm):
-    # 128 query heads of 300 tokens: enough 256x256 tiles (512) for the
-    # persistent single-K-step kernel at rho = 0.5, with ragged tile edges
-    case, Q = attention_case(dict(heads=128, kv_heads=32, L=300))
+    # 128 query heads of 296 tokens (a multiple of 8, so the MFMA route is
+    # taken): enough 256x256 tiles (512) for the persistent streaming kernel,
+    # with ragged tile edges in both rows and columns
+    case, Q = attention_case(dict(heads=128, kv_heads=32, L=296))
     for rho in case.rhos:
+        info = stream_plan(rmm, case, Q, rho)
+        assert info["gemm"] == "stream", info
         check_attention(rmm, case, Q, rho, heads=range(0, 128, 7), rows=None)
+
+
+@pytest.mark.parametrize("rho", [0.8, 1.0])
+def test_many_heads_two_k_steps(rmm, rho):
+    # k = 103 (rho = 0.8, the pages' attention setting) and k = 128 fill two
+    # 64-entry K steps: the streaming kernel's 128-row tiles, ragged at L = 296
+    case, Q = attention_case(dict(heads=128, kv_heads=32, L=296), rhos=(rho,))
+    info = stream_plan(rmm, case, Q, rho)
+    assert info["gemm"] == "stream", info
+    check_attention(rmm, case, Q, rho, heads=range(0, 128, 9), rows=None)
 
 
 def test_full_size_attention(rmm):
