@@ -270,3 +270,48 @@ def test_batched_grouped_linear(rmm, batch, n, d, m, group, rhos, nrows):
             assert_close(Yh, oracle.reduced_product(A[b], B64, ref_idx, 1.0, rows),
                          oracle.reduced_product(np.abs(A[b]), np.abs(B64), ref_idx, 1.0, rows), k, "bf16",
                          f"batched entry {b} rho={rho}")
+
+
+TRANSPOSED = [
+    # (n, d, m, rhos, kernel, rows sampled or None): B given as m x d (the
+    # nn.Linear weight layout); its kept columns are packed like the keys of
+    # Q K^T and contracted with 128x128 or 256x256 tiles
+    (300, 520, 264, (0.5, 0.8), "tile128", None),
+    (4096, 1024, 3072, (0.5, 0.8), "tile256", 10),
+]
+
+
+@pytest.mark.parametrize("n,d,m,rhos,kernel,nrows", TRANSPOSED, ids=["tile128", "tile256"])
+def test_transposed_weights(rmm, n, d, m, rhos, kernel, nrows):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(n + m)
+    A, _ = synthetic.lognormal_outlier_activations(rng, n, d, "bf16", n_outliers=3)
+    W = synthetic.gaussian_weights(rng, m, d, "bf16")  # m x d: B = W^T
+    A, _ = enforce_gap(A, [oracle.k_of(r, d) for r in rhos], "bf16")
+    Ad, Wd = to_device(A, "bf16"), to_device(W, "bf16")
+    B64 = np.ascontiguousarray(W.astype(np.float64).T)
+    rows = None if nrows is None else sample_rows(n, nrows, seed=11)
+    for rho in rhos:
+        k = oracle.k_of(rho, d)
+        info = rmm.plan_info(Ad, Wd, rho, transB=True)
+        assert info["gemm"] == kernel, info
+        Y, idx = rmm.matmul(Ad, Wd, rho, transB=True)
+        torch.cuda.synchronize()
+        ref_idx = oracle.topk(oracle.colnorm(A), k)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx)
+        Yh = to_host(Y)
+        if rows is not None:
+            Yh = Yh[rows]
+        assert_close(Yh, oracle.reduced_product(A, B64, ref_idx, 1.0, rows),
+                     oracle.reduced_product(np.abs(A), np.abs(B64), ref_idx, 1.0, rows), k, "bf16",
+                     f"transposed rho={rho}")
+
+
+def test_small_attention_mfma_route(rmm):
+    # 296-token heads (a multiple of 8): the MFMA route with 128x128 tiles
+    # (too few tiles for the streaming kernel), packed keys
+    case, Q = attention_case(dict(heads=8, kv_heads=2, L=296))
+    for rho in case.rhos:
+        info = stream_plan(rmm, case, Q, rho)
+        assert info["route"] == "mfma" and info["gemm"] == "tile128", info
+        check_attention(rmm, case, Q, rho, heads=range(8), rows=None)
