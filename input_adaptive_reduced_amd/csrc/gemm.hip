@@ -809,164 +809,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
     store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
-// Reduced product for a single 64-entry K step (kpad = 64), both operands
-// in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I], i.e. the
-// kept columns of the keys for Q K^T).  Such products are bound by writing
-// Y (62 flop per output byte at k = 64), so the kernel is persistent and
-// splits each workgroup into two roles:
-//  * waves 0-3 compute: each owns 128 rows x 64 columns of a 256x128 output
-//    tile, rounds its results to bf16 and writes them into one of two LDS
-//    stage buffers;
-//  * waves 4-7 store: one workgroup barrier per tile later they copy the
-//    staged tile to Y, 16 lanes writing 256 contiguous bytes of a row.
-// A workgroup walks whole row panels (one batch entry, 256 rows, every
-// column tile), so a compute wave loads its A fragments once per panel and
-// only its 8 B fragments per tile, issued right after the MFMAs that
-// consumed the previous ones.  Loads share the CU's memory pipeline with the
-// stores, which run at HBM speed; keeping them few is what keeps the compute
-// waves ahead of the stores.  Panels are dealt to workgroups in contiguous
-// runs, and runs to XCDs in order, so each XCD's L2 serves few batch entries.
-// Stage layout: 256 rows x 16 chunks of 16 bytes, chunk c of row r at
-// c ^ (r & 15).
+// Reduced product for one or two 64-entry K steps (kpad = 64 or 128), both
+// operands in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I],
+// i.e. the kept columns of the keys for Q K^T).  Such products are bound by
+// writing Y (62 or 124 flop per output byte), so the kernel is persistent and
+// built to keep the store stream at HBM speed.  A workgroup walks whole row
+// panels (one batch entry, 256 rows, every 128-column tile); its four waves
+// each compute 128 rows x 64 columns of a tile, with the panel's A fragments
+// (KS = kpad / 16 sub-steps x 4 row blocks) held in registers for the whole
+// panel and only the tile's B fragments loaded per tile, right after the
+// MFMAs that consumed the previous ones.  A wave rounds its results to bf16,
+// stages them in one of two LDS tile buffers and, after the workgroup
+// barrier, reads back 64 whole tile rows and stores them (16 lanes per
+// 256-byte row run); the stores drain while the next tile's MFMAs run.  Two
+// stage buffers make one barrier per tile enough: a buffer is rewritten only
+// after the barrier that follows every wave's reads of it.  Panels are dealt
+// to workgroups in contiguous runs, and runs to XCDs in order, so each XCD's
+// L2 serves few batch entries.  Stage layout: 256 rows x 16 chunks of 16
+// bytes, chunk c of row r at c ^ (r & 15).
 template <int KS>
-__global__ __launch_bounds__(512, 1) void gemm_stream_kernel(GemmArgs g) {
-    static_assert(KS == 4, "one K step");
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 128, WTM = 128, WTN = 64, FM = 4, FN = 2, CPR = BN / 8;
-    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const bool compute = w < 4;
-    const int wm = (w & 3) >> 1, wn = w & 1;
-    const int64_t tiles_m = (g.n + BM - 1) / BM, tiles_n = (g.m + BN - 1) / BN;
-    const int64_t panels = tiles_m * g.batch;
-    const int G = gridDim.x;
-    const int chunk = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int64_t per = (panels + G - 1) / G;
-    const int64_t p0 = chunk * per, p1 = min(panels, p0 + per);
-    const int64_t count = p1 > p0 ? (p1 - p0) * tiles_n : 0;  // tiles of this workgroup
-    // (all counts fit in 32 bits: n, m < 2^30, batch <= 65535)
-    const int tiles_n32 = (int)tiles_n, tiles_m32 = (int)tiles_m, p032 = (int)p0;
-    auto coords = [&](int64_t q64, int64_t &b, int64_t &tm, int64_t &tn) {
-        const int q = (int)q64;
-        const int qp = q / tiles_n32;
-        const int p = p032 + qp;
-        tn = q - qp * tiles_n32;
-        b = p / tiles_m32;
-        tm = p - (int)b * tiles_m32;
-    };
-
-    bf16x8_t fa[KS][FM], fb[KS][FN];
-    auto load_a = [&](int64_t q) {
-        int64_t b, tm, tn;
-        coords(q, b, tm, tn);
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t rb = tm * (BM / 32) + wm * (WTM / 32) + i;
-            const uint32_t off = rb * 32 < g.n ? (uint32_t)(rb * KS * 1024 + lane * 16) : kOob;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) fa[ks][i] = as_bf16x8(buf_load16(rA, off + ks * 1024));
-        }
-    };
-    auto load_b = [&](int64_t q) {
-        int64_t b, tm, tn;
-        coords(q, b, tm, tn);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + b * g.strideB, g.b_bytes);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t cb = tn * (BN / 32) + wn * (WTN / 32) + j;
-            const uint32_t off = cb * 32 < g.m ? (uint32_t)(cb * KS * 1024 + lane * 16) : kOob;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) fb[ks][j] = as_bf16x8(buf_load16(rB, off + ks * 1024));
-        }
-    };
-
-    if (compute && count > 0) {
-        load_a(0);
-        load_b(0);
-    }
-    // iteration q computes this workgroup's tile q and stores tile q - 1
-    for (int64_t q = 0; q <= count; ++q) {
-        if (compute) {
-            if (q < count) {
-                f32x16_t acc[FM][FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] =
-                                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
-                // round to bf16 first (frees the accumulators), then fetch the
-                // next tile's operands, then stage
-                uint2 pk[FM][FN][4];
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-#pragma unroll
-                        for (int qq = 0; qq < 4; ++qq)
-                            pk[i][j][qq] =
-                                make_uint2(pack_bf16x2(g.alpha * acc[i][j][4 * qq], g.alpha * acc[i][j][4 * qq + 1]),
-                                           pack_bf16x2(g.alpha * acc[i][j][4 * qq + 2], g.alpha * acc[i][j][4 * qq + 3]));
-                if (q + 1 < count) {
-                    if ((int)(q + 1) % tiles_n32 == 0) load_a(q + 1);  // next panel
-                    load_b(q + 1);
-                }
-                char *st = reinterpret_cast<char *>(stageL[q & 1]);
-                // lane l, registers 4qq..4qq+3 of block (i, j): row i*32 + l%32,
-                // columns j*32 + 8qq + 4(l/32) + 0..3 of this wave's block
-#pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const int r = wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                        for (int qq = 0; qq < 4; ++qq) {
-                            const int c = wn * (WTN / 8) + j * 4 + qq;  // 16-byte chunk of the tile row
-                            *reinterpret_cast<uint2 *>(st + (r * CPR + (c ^ (r & 15))) * 16 + (lane >> 5) * 8) =
-                                pk[i][j][qq];
-                        }
-                    }
-                }
-            }
-        } else if (q > 0) {
-            int64_t b, tm, tn;
-            coords(q - 1, b, tm, tn);
-            const int64_t m0 = tm * BM, n0 = tn * BN;
-            const uint4 *stg = stageL[(q - 1) & 1];
-            uint16_t *Yb = g.Y + b * g.strideY;
-            const int sw = w - 4;  // rows 64 sw .. 64 sw + 63 of the tile
-#pragma unroll 4
-            for (int it = 0; it < BM / 16; ++it) {
-                const int r = sw * (BM / 4) + it * 4 + (lane >> 4);
-                const int c = lane & 15;
-                const uint4 v = stg[r * CPR + (c ^ (r & 15))];
-                const int64_t row = m0 + r, col = n0 + c * 8;
-                if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(Yb + row * g.ldy + col) = v;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// Two-K-step (kpad = 128) variant for wide heads, without the role split:
-// four waves, each computing 128 rows x 64 columns of a 256 x 128 tile with
-// its panel's A fragments (8 sub-steps x 4 row blocks) held in registers for
-// the whole row panel, which needs one wave per SIMD.  After the MFMAs a
-// wave rounds its results, stages them in one of two LDS tile buffers, and
-// after the workgroup barrier reads back 64 whole tile rows and stores them
-// (16 lanes per 256-byte row run); the stores drain while the next tile's
-// MFMAs run.  Two stage buffers make one barrier per tile enough: a buffer
-// is rewritten only after the barrier that follows every wave's reads of it.
-__global__ __launch_bounds__(256, 1) void gemm_stream8_kernel(GemmArgs g) {
-    constexpr int BM = 256, BN = 128, WTM = 128, WTN = 64, FM = 4, FN = 2, KS = 8, CPR = BN / 8;
     __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
@@ -1622,9 +1485,9 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         const int64_t panels = ((a.n + 255) / 256) * a.batch;
         const unsigned grid = (unsigned)std::min<int64_t>(panels, (int64_t)cus);
         if (a.kpad == BK)
-            gemm_stream_kernel<4><<<grid, 512, 0, stream>>>(a);
+            gemm_stream_kernel<4><<<grid, 256, 0, stream>>>(a);
         else
-            gemm_stream8_kernel<<<grid, 256, 0, stream>>>(a);
+            gemm_stream_kernel<8><<<grid, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {
