@@ -813,40 +813,45 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
 // operands in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I],
 // i.e. the kept columns of the keys for Q K^T).  Such products are bound by
 // writing Y (62 or 124 flop per output byte), so the kernel is persistent and
-// built to keep the store stream at HBM speed.  A workgroup walks whole row
-// panels (one batch entry, 256 rows, every 128-column tile); its four waves
-// each compute 128 rows x 64 columns of a tile, with the panel's A fragments
-// (KS = kpad / 16 sub-steps x 4 row blocks) held in registers for the whole
-// panel and only the tile's B fragments loaded per tile, right after the
-// MFMAs that consumed the previous ones.  A wave rounds its results to bf16,
-// stages them in one of two LDS tile buffers and, after the workgroup
-// barrier, reads back 64 whole tile rows and stores them (16 lanes per
-// 256-byte row run); the stores drain while the next tile's MFMAs run.  Two
-// stage buffers make one barrier per tile enough: a buffer is rewritten only
-// after the barrier that follows every wave's reads of it.  Panels are dealt
-// to workgroups in contiguous runs, and runs to XCDs in order, so each XCD's
-// L2 serves few batch entries.  Stage layout: 256 rows x 16 chunks of 16
-// bytes, chunk c of row r at c ^ (r & 15).
+// built to keep the store stream at HBM speed.  A workgroup owns column
+// strips (one batch entry, 512 columns) and walks down them in 64-row tiles.
+// Its four waves (one per SIMD) each compute 64 rows x 128 columns of a
+// tile, keep their strip's B fragments (KS = kpad / 16 sub-steps x 4 column
+// blocks) in registers for the whole strip and load only the tile's A
+// fragments per tile, right after the MFMAs that consumed the previous ones.
+// A wave rounds its results to bf16, stages them in one of two LDS tile
+// buffers and, after the workgroup barrier, stores 16 whole tile rows, one
+// 1 KB row segment per store instruction; the stores drain while the next
+// tile's MFMAs run.  1 KB row segments are the store pattern HBM absorbs
+// fastest on MI355X (6.3 TB/s measured for runs of 64 x 1 KB tiles, against
+// 5.3 TB/s for 256-byte segments).  Two stage buffers make one barrier per
+// tile enough: a buffer is rewritten only after the barrier that follows
+// every wave's reads of it.  Strips are dealt to workgroups in contiguous
+// runs and runs to XCDs in order, so the strips of a batch entry share an
+// XCD and its L2 copy of A.  Stage layout: 64 rows of 64 16-byte chunks,
+// rows 65 chunks apart (the pad chunk spreads a column's rows over the LDS
+// banks and keeps every staging address a lane base plus a constant).
+constexpr int kStreamBM = 64, kStreamBN = 512;
+
 template <int KS>
 __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
-    constexpr int BM = 256, BN = 128, WTM = 128, WTN = 64, FM = 4, FN = 2, CPR = BN / 8;
-    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 64 KB
+    constexpr int BM = kStreamBM, BN = kStreamBN, WTN = 128, FM = 2, FN = 4, CPR = BN / 8 + 1;
+    __shared__ uint4 stageL[2][BM * CPR];  // 2 x 65 KB
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
     const int64_t tiles_m = (g.n + BM - 1) / BM, tiles_n = (g.m + BN - 1) / BN;
-    const int64_t panels = tiles_m * g.batch;
+    const int64_t strips = tiles_n * g.batch;
     const int G = gridDim.x;
     const int chunk = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int64_t per = (panels + G - 1) / G;
-    const int64_t p0 = chunk * per, p1 = min(panels, p0 + per);
-    const int count = p1 > p0 ? (int)((p1 - p0) * tiles_n) : 0;  // tiles of this workgroup
-    const int tiles_n32 = (int)tiles_n, tiles_m32 = (int)tiles_m, p032 = (int)p0;
+    const int64_t per = (strips + G - 1) / G;
+    const int64_t s0 = chunk * per, s1 = min(strips, s0 + per);
+    const int count = s1 > s0 ? (int)((s1 - s0) * tiles_m) : 0;  // tiles of this workgroup
+    const int tiles_n32 = (int)tiles_n, tiles_m32 = (int)tiles_m, s032 = (int)s0;
     auto coords = [&](int q, int &b, int &tm, int &tn) {
-        const int qp = q / tiles_n32;
-        const int p = p032 + qp;
-        tn = q - qp * tiles_n32;
-        b = p / tiles_m32;
-        tm = p - b * tiles_m32;
+        const int qs = q / tiles_m32;
+        const int s = s032 + qs;
+        tm = q - qs * tiles_m32;
+        b = s / tiles_n32;
+        tn = s - b * tiles_n32;
     };
 
     bf16x8_t fa[KS][FM], fb[KS][FN];
@@ -856,7 +861,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + (int64_t)b * g.strideA, g.a_bytes);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int64_t rb = (int64_t)tm * (BM / 32) + wm * (WTM / 32) + i;
+            const int64_t rb = (int64_t)tm * (BM / 32) + i;
             const uint32_t off = rb * 32 < g.n ? (uint32_t)(rb * KS * 1024 + lane * 16) : kOob;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) fa[ks][i] = as_bf16x8(buf_load16(rA, off + ks * 1024));
@@ -868,7 +873,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (int64_t)b * g.strideB, g.b_bytes);
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t cb = (int64_t)tn * (BN / 32) + wn * (WTN / 32) + j;
+            const int64_t cb = (int64_t)tn * (BN / 32) + w * (WTN / 32) + j;
             const uint32_t off = cb * 32 < g.m ? (uint32_t)(cb * KS * 1024 + lane * 16) : kOob;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) fb[ks][j] = as_bf16x8(buf_load16(rB, off + ks * 1024));
@@ -879,6 +884,8 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
         load_a(0);
         load_b(0);
     }
+    // staging base of this lane's 8-byte pieces: row l%32 (+ 32 i), wave's 8 chunks, half l/32
+    const int sbase = ((lane & 31) * CPR + w * (WTN / 8)) * 16 + (lane >> 5) * 8;
     for (int q = 0; q < count; ++q) {
         f32x16_t acc[FM][FN];
 #pragma unroll
@@ -904,35 +911,31 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g) {
                     pk[i][j][qq] = make_uint2(pack_bf16x2(g.alpha * acc[i][j][4 * qq], g.alpha * acc[i][j][4 * qq + 1]),
                                               pack_bf16x2(g.alpha * acc[i][j][4 * qq + 2], g.alpha * acc[i][j][4 * qq + 3]));
         if (q + 1 < count) {
-            if ((q + 1) % tiles_n32 == 0) load_a(q + 1);  // next panel
-            load_b(q + 1);
+            if ((q + 1) % tiles_m32 == 0) load_b(q + 1);  // next strip
+            load_a(q + 1);
         }
-        char *st = reinterpret_cast<char *>(stageL[q & 1]);
+        // lane l, registers 4qq..4qq+3 of block (i, j): row i*32 + l%32,
+        // columns j*32 + 8qq + 4(l/32) + 0..3 of this wave's 128 columns
+        char *st = reinterpret_cast<char *>(stageL[q & 1]) + sbase;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int r = wm * WTM + i * 32 + (lane & 31);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int c = wn * (WTN / 8) + j * 4 + qq;
-                    *reinterpret_cast<uint2 *>(st + (r * CPR + (c ^ (r & 15))) * 16 + (lane >> 5) * 8) = pk[i][j][qq];
-                }
-            }
-        }
+                for (int qq = 0; qq < 4; ++qq)
+                    *reinterpret_cast<uint2 *>(st + (i * 32 * CPR + j * 4 + qq) * 16) = pk[i][j][qq];
         __syncthreads();
-        // wave w stores tile rows 64 w .. 64 w + 63
+        // wave w stores tile rows 16 w .. 16 w + 15, one 1 KB row segment per instruction
         int b, tm, tn;
         coords(q, b, tm, tn);
-        const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+        const int64_t m0 = (int64_t)tm * BM, col = (int64_t)tn * BN + lane * 8;
         const uint4 *stg = stageL[q & 1];
         uint16_t *Yb = g.Y + (int64_t)b * g.strideY;
 #pragma unroll 4
         for (int it = 0; it < 16; ++it) {
-            const int r = w * 64 + it * 4 + (lane >> 4);
-            const int c = lane & 15;
-            const uint4 v = stg[r * CPR + (c ^ (r & 15))];
-            const int64_t row = m0 + r, col = n0 + c * 8;
+            const int r = w * 16 + it;
+            const uint4 v = stg[r * CPR + lane];
+            const int64_t row = m0 + r;
             if (row < g.n && col < g.m) *reinterpret_cast<uint4 *>(Yb + row * g.ldy + col) = v;
         }
     }
@@ -1482,8 +1485,8 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 256;
-        const int64_t panels = ((a.n + 255) / 256) * a.batch;
-        const unsigned grid = (unsigned)std::min<int64_t>(panels, (int64_t)cus);
+        const int64_t strips = ((a.m + kStreamBN - 1) / kStreamBN) * a.batch;
+        const unsigned grid = (unsigned)std::min<int64_t>(strips, (int64_t)cus);
         if (a.kpad == BK)
             gemm_stream_kernel<4><<<grid, 256, 0, stream>>>(a);
         else
