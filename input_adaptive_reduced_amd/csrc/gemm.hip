@@ -1071,13 +1071,16 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t *__restrict__ 
         __syncthreads();
     }
     const int64_t cpr = kpad / 8;  // output chunks per row
+    // separate LDS and global reads (use_lds is uniform): one pointer that
+    // could be either would make every read a flat load
     auto gather = [&](int rr, const int32_t (&j)[8]) {
         uint32_t h[8];
+        if (use_lds) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t jj = j[e] >= 0 ? j[e] : 0;
-            const uint16_t v = use_lds ? rowbuf[rr * d + jj] : S[(r0 + rr) * ld_src + jj];
-            h[e] = j[e] >= 0 ? v : 0;
+            for (int e = 0; e < 8; ++e) h[e] = j[e] >= 0 ? (uint32_t)rowbuf[rr * d + j[e]] : 0u;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = j[e] >= 0 ? (uint32_t)S[(r0 + rr) * ld_src + j[e]] : 0u;
         }
         return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     };
@@ -1209,15 +1212,26 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
         const bool fast = fits(q);
         const int32_t w0 = span_lo[q] & ~7;
         uint32_t hv[PP][8];
+        // two separate loops (fast is uniform): one pointer that could be
+        // either LDS or global memory would make every read a flat load
+        if (fast) {
+            const uint16_t *mine = buf + row * kPackRowStride - w0;
 #pragma unroll
-        for (int h = 0; h < PP; ++h)
+            for (int h = 0; h < PP; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int32_t jj = jc[h][e];
-                uint32_t v = 0;
-                if (row_ok && jj >= 0) v = fast ? buf[row * kPackRowStride + (jj - w0)] : S[grow * ld_src + jj];
-                hv[h][e] = v;
-            }
+                for (int e = 0; e < 8; ++e) {
+                    const int32_t jj = jc[h][e];
+                    hv[h][e] = (row_ok && jj >= 0) ? (uint32_t)mine[jj] : 0u;
+                }
+        } else {
+#pragma unroll
+            for (int h = 0; h < PP; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int32_t jj = jc[h][e];
+                    hv[h][e] = (row_ok && jj >= 0) ? (uint32_t)S[grow * ld_src + jj] : 0u;
+                }
+        }
         const int64_t t0 = (int64_t)(tt0 + q) * TT;
 #pragma unroll
         for (int h = 0; h < PP; ++h) {

@@ -1,4 +1,10 @@
-"""Host-side check of an ordering argument the LDS-DMA product kernel relies on.
+"""Host-side checks of the compiled gfx950 kernels (no GPU is used).
+
+1. No kernel uses flat (generic-address) loads or stores: a pointer that may
+   point to either LDS or global memory compiles to flat accesses, which wait
+   on both counters and serialise a gather (this once cost the A pack a fifth
+   of its time).
+2. An ordering argument the LDS-DMA product kernel relies on.
 
 gemm_bdma_kernel waits for its own LDS-DMA loads of the next K step with
 ``s_waitcnt vmcnt(28)``: vector-memory loads retire in issue order, so the
@@ -63,14 +69,35 @@ def test_min_younger_counts_loads_after_the_previous_steps_dma():
     assert min_younger(list("DDWDDW")) == 2
 
 
-@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
-def test_bdma_wait_covers_its_dma(tmp_path):
-    out = tmp_path / "gemm.s"
+def compile_to_asm(src, out):
     cmd = ["hipcc", "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
-           os.path.join(CSRC, "gemm.hip"), "-o", str(out)]
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
-    asm = out.read_text()
+    return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    if shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    return compile_to_asm("gemm.hip", tmp_path_factory.mktemp("asm") / "gemm.s")
+
+
+@pytest.mark.parametrize("src", ["norm_select.hip", "gemv.hip", "rmm_api.hip"])
+def test_no_flat_memory_access(src, tmp_path):
+    if shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    asm = compile_to_asm(src, tmp_path / "k.s")
+    assert not re.search(r"\bflat_(load|store|atomic)", asm)
+
+
+def test_no_flat_memory_access_in_gemm(gemm_asm):
+    assert not re.search(r"\bflat_(load|store|atomic)", gemm_asm)
+
+
+def test_bdma_wait_covers_its_dma(gemm_asm):
+    asm = gemm_asm
     for split in ("0", "1"):
         seqs = list(loop_sequences(asm, "gemm_bdma_kernelILb" + split))
         assert seqs, "no loop with the DMA wait found"
