@@ -1215,13 +1215,15 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
         // two separate loops (fast is uniform): one pointer that could be
         // either LDS or global memory would make every read a flat load
         if (fast) {
+            // branch-free: padding entries read a valid slot and are zeroed after
             const uint16_t *mine = buf + row * kPackRowStride - w0;
 #pragma unroll
             for (int h = 0; h < PP; ++h)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int32_t jj = jc[h][e];
-                    hv[h][e] = (row_ok && jj >= 0) ? (uint32_t)mine[jj] : 0u;
+                    const uint32_t v = mine[jj >= 0 ? jj : w0];
+                    hv[h][e] = (row_ok && jj >= 0) ? v : 0u;
                 }
         } else {
 #pragma unroll
@@ -1231,6 +1233,9 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t *__rest
                     const int32_t jj = jc[h][e];
                     hv[h][e] = (row_ok && jj >= 0) ? (uint32_t)S[grow * ld_src + jj] : 0u;
                 }
+            // rare path: let its loads land here, so the LDS reads of the fast
+            // path never wait for outstanding loads (those of the next window)
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         }
         const int64_t t0 = (int64_t)(tt0 + q) * TT;
 #pragma unroll
