@@ -57,14 +57,11 @@ struct Vec16<float> {
 };
 
 // grid: (strips, chunks, batch); block: kNormThreads = tc column-lanes x tr row-lanes.
-// `counter` (one per batch entry, may be null) is cleared here for the
-// finalize kernel that follows in the same stream.
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *__restrict__ A, int64_t n, int64_t d,
                                                                        int64_t lda, int64_t strideA, int tc,
                                                                        int64_t rows_per_chunk, int vec_ok,
-                                                                       float *__restrict__ part,
-                                                                       unsigned *__restrict__ counter) {
+                                                                       float *__restrict__ part) {
     constexpr int V = Vec16<T>::N;
     __shared__ float red[kNormThreads * V];
     const int tid = threadIdx.x;
@@ -74,7 +71,6 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_partial_kernel(const T *
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r1 = min(n, r0 + rows_per_chunk);
     const T *Ab = A + b * strideA;
-    if (counter && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) counter[b] = 0u;
 
     float acc[V];
 #pragma unroll
@@ -135,8 +131,7 @@ template <int RPT>
 __global__ __launch_bounds__(kNormThreads) void colnorm_rows_kernel(const uint16_t *__restrict__ A, int64_t n,
                                                                     int64_t d, int64_t lda, int64_t strideA, int tc,
                                                                     int64_t rows_per_chunk, int64_t a_bytes,
-                                                                    float *__restrict__ part,
-                                                                    unsigned *__restrict__ counter) {
+                                                                    float *__restrict__ part) {
     __shared__ float red[kNormThreads * 8];
     const int tid = threadIdx.x;
     const int tx = tid % tc, ty = tid / tc, tr = kNormThreads / tc;
@@ -144,7 +139,6 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_rows_kernel(const uint16
     const int64_t j0 = (int64_t)blockIdx.x * tc * 8 + (int64_t)tx * 8;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r1 = min(n, r0 + rows_per_chunk);
-    if (counter && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) counter[b] = 0u;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A + b * strideA), (short)0, (int)a_bytes, 0x00020000);
 
@@ -662,22 +656,13 @@ __global__ __launch_bounds__(1024) void norm_select_kernel(const float *__restri
                         pad_all ? pad_all + b * ld_pad : nullptr, ld_pad, nullptr, vals, sel_out, nullptr);
 }
 
-// Final column norms, and (with `counter`) the selection in the same launch.
-// 64 columns per workgroup, 16 row-chunk groups per column: group g sums the
-// chunks g, g+16, ... in ascending order (four loads in flight), the 16 group
-// sums are added in a fixed tree order, then a correctly rounded sqrt.  Each
-// workgroup then publishes its norms and takes a ticket; the last workgroup of
-// a batch entry (all norms visible after the fence) runs the exact TopK over
-// all d scores.  The counter is cleared by the column-norm kernel that runs
-// before this one in the same stream.
-__global__ __launch_bounds__(1024) void finalize_select_kernel(const float *__restrict__ part, int64_t chunks, int d,
-                                                                float *__restrict__ s_all, unsigned *__restrict__ counter,
-                                                                int k, int32_t *__restrict__ idx_all, int64_t ld_idx,
-                                                                int32_t *__restrict__ pad_all, int64_t ld_pad) {
-    extern __shared__ int32_t sel_out[];
+// Final column norms: 64 columns per workgroup, 16 row-chunk groups per
+// column; group g sums the chunks g, g+16, ... in ascending order (four loads
+// in flight), the 16 group sums are added in a fixed tree order, then a
+// correctly rounded sqrt.
+__global__ __launch_bounds__(1024) void finalize_kernel(const float *__restrict__ part, int64_t chunks, int d,
+                                                        float *__restrict__ s_all) {
     __shared__ float red[16][64];
-    __shared__ SelectShared<1024> sh;
-    __shared__ int last;
     const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
     const int64_t j = (int64_t)blockIdx.x * 64 + c;
@@ -705,25 +690,6 @@ __global__ __launch_bounds__(1024) void finalize_select_kernel(const float *__re
         for (int q = 0; q < 4; ++q) t[q] = t[2 * q] + t[2 * q + 1];
         s[j] = __fsqrt_rn((t[0] + t[1]) + (t[2] + t[3]));
     }
-    if (!counter) return;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(&counter[b], 1u) == gridDim.x - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    constexpr int E = 16;  // d <= 16384 on this path
-    const int j0 = threadIdx.x * E;
-    const int nv = max(0, min(E, d - j0));
-    uint32_t key[E];
-    float vals[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        vals[e] = e < nv ? __builtin_nontemporal_load(&s[j0 + e]) : 0.f;
-        key[e] = score_key(vals[e]);
-    }
-    block_select<1024, E>(sh, key, nv, j0, k, idx_all ? idx_all + b * ld_idx : nullptr,
-                          pad_all ? pad_all + b * ld_pad : nullptr, ld_pad, nullptr, vals, sel_out, nullptr);
 }
 
 __global__ void iota_kernel(int32_t *idx, int64_t k, int64_t ld, int64_t total) {
@@ -778,43 +744,38 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch) {
 }
 
 hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda, int64_t batch,
-                                  int64_t strideA, const ColnormPlan &p, float *part, unsigned *counter,
-                                  hipStream_t stream) {
+                                  int64_t strideA, const ColnormPlan &p, float *part, hipStream_t stream) {
     dim3 grid(p.strips, p.chunks, (unsigned)batch);
     const int esz = dt == RMM_BF16 ? 2 : 4;
     const int V = 16 / esz;
     const int vec_ok = ((uintptr_t)A % 16 == 0) && (lda % V == 0) && (batch == 1 || strideA % V == 0);
     const int64_t a_bytes = ((n - 1) * lda + d) * 2;  // one batch entry
     if (dt == RMM_BF16 && p.rpt > 0 && vec_ok && d % 8 == 0 && a_bytes < 0x7fffffff) {
+        const uint16_t *Ab = static_cast<const uint16_t *>(A);
         if (p.rpt == 8)
-            colnorm_rows_kernel<8><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
-                                                                       strideA, p.tc, p.rows_per_chunk, a_bytes, part,
-                                                                       counter);
+            colnorm_rows_kernel<8><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, strideA, p.tc, p.rows_per_chunk,
+                                                                       a_bytes, part);
         else if (p.rpt == 16)
-            colnorm_rows_kernel<16><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
-                                                                        strideA, p.tc, p.rows_per_chunk, a_bytes, part,
-                                                                        counter);
+            colnorm_rows_kernel<16><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, strideA, p.tc, p.rows_per_chunk,
+                                                                        a_bytes, part);
         else
-            colnorm_rows_kernel<32><<<grid, kNormThreads, 0, stream>>>(static_cast<const uint16_t *>(A), n, d, lda,
-                                                                        strideA, p.tc, p.rows_per_chunk, a_bytes, part,
-                                                                        counter);
+            colnorm_rows_kernel<32><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, strideA, p.tc, p.rows_per_chunk,
+                                                                        a_bytes, part);
         return hipGetLastError();
     }
     if (dt == RMM_BF16)
         colnorm_partial_kernel<uint16_t><<<grid, kNormThreads, 0, stream>>>(
-            static_cast<const uint16_t *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part, counter);
+            static_cast<const uint16_t *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part);
     else
         colnorm_partial_kernel<float><<<grid, kNormThreads, 0, stream>>>(
-            static_cast<const float *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part, counter);
+            static_cast<const float *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part);
     return hipGetLastError();
 }
 
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
-                                   unsigned *counter, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad,
-                                   int64_t ld_pad, hipStream_t stream) {
+                                   hipStream_t stream) {
     dim3 grid((unsigned)((d + 63) / 64), (unsigned)batch);
-    finalize_select_kernel<<<grid, 1024, counter ? (size_t)k * 4 : 0, stream>>>(part, chunks, (int)d, s, counter, (int)k,
-                                                                                idx, ld_idx, idx_pad, ld_pad);
+    finalize_kernel<<<grid, 1024, 0, stream>>>(part, chunks, (int)d, s);
     return hipGetLastError();
 }
 

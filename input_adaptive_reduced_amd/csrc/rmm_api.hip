@@ -279,9 +279,9 @@ rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, in
     const size_t need = (size_t)p.chunks * (size_t)d * 4;
     if (ws_bytes < need || !workspace) return RMM_ERR_WORKSPACE;
     float *part = static_cast<float *>(workspace);
-    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(A, dt, n, d, lda, 1, 0, p, part, nullptr, stream));
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(A, dt, n, d, lda, 1, 0, p, part, stream));
     RMM_LAUNCH(RMM_KERNEL_FINALIZE,
-               launch_colnorm_finalize(part, p.chunks, d, 1, s_out, nullptr, 0, nullptr, 0, nullptr, 0, stream));
+               launch_colnorm_finalize(part, p.chunks, d, 1, s_out, stream));
     return RMM_OK;
 }
 
@@ -360,13 +360,12 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
         float *part = reinterpret_cast<float *>(ws + p.off_part);
         float *s = reinterpret_cast<float *>(ws + p.off_s);
         RMM_LAUNCH(RMM_KERNEL_COLNORM,
-                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, nullptr, stream));
+                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
         if (norm_select_ok(p.cp.chunks, d)) {
             RMM_LAUNCH(RMM_KERNEL_SELECT, launch_norm_select(part, p.cp.chunks, d, batch, k, idx_out, k, pidx, p.kpad,
                                                              stream));
         } else {
-            RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, nullptr, 0, nullptr,
-                                                                    0, nullptr, 0, stream));
+            RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, batch, s, stream));
             RMM_LAUNCH(RMM_KERNEL_SELECT,
                        launch_select(s, nullptr, RMM_F32, 0, batch, d, k, idx_out, k, pidx, p.kpad, nullptr, stream));
         }

@@ -59,19 +59,15 @@ struct ColnormPlan {
     int rpt;         // bf16: rows per thread with every load issued up front (0: looped kernel)
 };
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch);
-// `counter` (batch entries, may be null) is cleared for the finalize step.
 hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
                                   int64_t batch, int64_t strideA, const ColnormPlan &p, float *part,
-                                  unsigned *counter, hipStream_t stream);
-// s[b][j] = sqrt(sum_r part[b][r][j]) in a fixed order.  With `counter`
-// (cleared by launch_colnorm_partial in the same stream) the last workgroup
-// of each batch entry also selects the k largest scores into idx / idx_pad,
-// as launch_select does; d <= 16384 on that path.  (The library runs the
-// selection as its own launch: the device-scope fences this variant needs
-// cost more than the launch they save on MI355X.)
+                                  hipStream_t stream);
+// s[b][j] = sqrt(sum_r part[b][r][j]) in a fixed order.
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
-                                   unsigned *counter, int64_t k, int32_t *idx, int64_t ld_idx, int32_t *idx_pad,
-                                   int64_t ld_pad, hipStream_t stream);
+                                   hipStream_t stream);
+// Longest score vector the register-resident selection (select_kernel,
+// norm_select_kernel, the decode |a| selection) handles; longer ones use
+// select_big_kernel.
 constexpr int64_t kFusedSelectMaxD = 16384;
 // Norms from the row-chunk partials and the selection in one launch (one
 // workgroup per batch entry, every partial load in flight at once).  One
