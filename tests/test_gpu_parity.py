@@ -91,6 +91,9 @@ RAGGED = [
     (dict(n=2050, d=4200, m=3080), 0.8, "bdma", True),
     (dict(n=3100, d=1504, m=4000), 0.8, "adirect", False),
     (dict(n=2050, d=4200, m=3080), 0.48, "adirect", True),
+    # rho = 1 (the identity set, A packed through the index list 0..d-1)
+    (dict(n=3100, d=1536, m=4000), 1.0, "bdma", False),
+    (dict(n=2050, d=4224, m=3080), 1.0, "adirect", True),
 ]
 
 
