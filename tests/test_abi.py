@@ -68,3 +68,34 @@ def test_workspace_sizing_and_validation_on_host(lib):
     assert lib.rmm_matmul(None, 1, 1, 0.5, 1, None, None, 0, None) == 1
     assert lib.rmm_select(None, 1, 10, 3, None, None) == 1
     assert lib.rmm_colnorm(None, 1, 2, 2, 2, None, None, 0, None) == 1
+
+
+def test_plan_info_on_host(lib):
+    """rmm_plan_info is host-only: the route and kernel each workload shape
+    takes, and its argument checks."""
+    import input_adaptive_reduced_amd as r
+
+    def info(dtype, n, d, m, rho, transB=0, batch=1, group=1):
+        ds = r.Desc()
+        lib.rmm_desc_init(ctypes.byref(ds), dtype, n, d, m)
+        ds.transB = transB
+        if transB:
+            ds.ldb = d
+        ds.batch, ds.b_group = batch, group
+        if batch > 1:
+            ds.strideA, ds.strideB, ds.strideY = n * d, (m * d if transB else d * m), n * m
+        out = (ctypes.c_int32 * 3)()
+        st = lib.rmm_plan_info(ctypes.byref(ds), rho, out)
+        return st, tuple(out)
+
+    assert info(r.BF16, 4096, 4096, 4096, 0.8) == (0, (1, 2, 1))       # c2: MFMA route, A-direct kernel
+    assert info(r.BF16, 2048, 14336, 4096, 0.8) == (0, (1, 4, 2))      # c3: LDS-DMA kernel, two K splits
+    st, (route, gemm, splits) = info(r.BF16, 1, 8192, 28672, 0.8)     # decode: gathered GEMV
+    assert st == 0 and route == 2 and gemm == -1 and splits > 1
+    assert info(r.BF16, 4096, 128, 4096, 0.5, transB=1, batch=32, group=4) == (0, (1, 3, 1))  # c4 scores
+    assert info(r.F32, 64, 256, 128, 0.5)[1][:2] == (0, -1)             # fp32: generic route
+    assert info(r.BF16, 300, 520, 300, 0.5)[1][:2] == (0, -1)           # m % 8 != 0: generic route
+    assert info(r.BF16, 64, 256, 128, 0.0)[0] == 1                      # invalid rho
+    ds = r.Desc()
+    lib.rmm_desc_init(ctypes.byref(ds), r.BF16, 64, 256, 128)
+    assert lib.rmm_plan_info(ctypes.byref(ds), 0.5, None) == 1          # NULL output
