@@ -706,23 +706,31 @@ unsigned g_norm_select_attr_done = 0;
 }  // namespace
 
 // Strips of 16 threads x one 16-byte load (128 bf16 / 64 fp32 columns: one
-// 256-byte segment per row) and about 1024 workgroups, each thread summing at
-// least 8 rows: the fastest shape measured on MI355X for the 4096 x 4096 bf16
-// activation block (7.4 us, 4.6 TB/s, against 13-15 us for 512-column strips).
+// 256-byte segment per row) and a few hundred workgroups, each thread summing
+// at least 8 rows: the fastest shape measured on MI355X for the 4096 x 4096
+// bf16 activation block (7.4 us, 4.6 TB/s, against 13-15 us for 512-column
+// strips).
 ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch) {
     const int V = dt == RMM_BF16 ? 8 : 4;
     ColnormPlan p;
     if (dt == RMM_BF16) {
         // 128- or 256-column strips; rows per thread 8, 16 or 32, whichever
-        // first brings the grid to at most ~768 workgroups
+        // first brings the grid to at most ~768 workgroups and, for d <= 4096
+        // (where one workgroup per batch entry reads every partial before its
+        // selection), the row chunks to at most 8: one round of loads there.
+        // On the 4096 x 4096 block, 8 chunks instead of 16 cost the partial
+        // pass 0.2 us and save the selection 1 us.
         int tc = d <= 4096 ? 16 : 32;
         while (tc > 1 && (int64_t)tc * V / 2 >= d) tc /= 2;
         const int tr = kNormThreads / tc;
         p.tc = tc;
         p.strips = (int)((d + (int64_t)tc * V - 1) / ((int64_t)tc * V));
         int rpt = 8;
-        while (rpt < 32 && (int64_t)p.strips * batch * ((n + (int64_t)tr * rpt - 1) / ((int64_t)tr * rpt)) > 768)
+        for (;;) {
+            const int64_t chunks = (n + (int64_t)tr * rpt - 1) / ((int64_t)tr * rpt);
+            if (rpt == 32 || ((int64_t)p.strips * batch * chunks <= 768 && (d > 4096 || chunks <= 8))) break;
             rpt *= 2;
+        }
         p.rpt = rpt;
         p.rows_per_chunk = (int64_t)tr * rpt;
         p.chunks = (int)((n + p.rows_per_chunk - 1) / p.rows_per_chunk);
@@ -811,6 +819,9 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
         const void *ks[] = {reinterpret_cast<const void *>(&select_kernel<1024, 16, true, true>),
                             reinterpret_cast<const void *>(&select_kernel<1024, 16, false, true>),
                             reinterpret_cast<const void *>(&select_kernel<1024, 16, false, false>),
+                            reinterpret_cast<const void *>(&select_kernel<1024, 8, true, true>),
+                            reinterpret_cast<const void *>(&select_kernel<1024, 8, false, true>),
+                            reinterpret_cast<const void *>(&select_kernel<1024, 8, false, false>),
                             reinterpret_cast<const void *>(&select_big_kernel<1024>)};
         for (const void *kf : ks) {
             hipError_t e = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
@@ -827,6 +838,9 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
         else if (d <= 4096)
             select_kernel<256, 16, true, true><<<g, 256, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx, ld_idx,
                                                                             idx_pad, ld_pad, aval);
+        else if (d <= 8192)
+            select_kernel<1024, 8, true, true><<<g, 1024, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx,
+                                                                             ld_idx, idx_pad, ld_pad, aval);
         else
             select_kernel<1024, 16, true, true><<<g, 1024, out_lds, stream>>>(src, a_stride, (int)d, (int)k, idx,
                                                                               ld_idx, idx_pad, ld_pad, aval);
@@ -847,6 +861,13 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
         else
             select_kernel<256, 16, false, false><<<g, 256, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
                                                                               idx_pad, ld_pad, aval);
+    } else if (d <= 8192) {
+        if (vec)
+            select_kernel<1024, 8, false, true><<<g, 1024, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                              idx_pad, ld_pad, aval);
+        else
+            select_kernel<1024, 8, false, false><<<g, 1024, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,
+                                                                               idx_pad, ld_pad, aval);
     } else if (d <= 16384) {
         if (vec)
             select_kernel<1024, 16, false, true><<<g, 1024, out_lds, stream>>>(s, d, (int)d, (int)k, idx, ld_idx,

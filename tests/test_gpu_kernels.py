@@ -108,10 +108,12 @@ ODD = [
     (33, 65, 72, "bf16", 0.999, "k = d - 0 (ceil)"),
     (2, 100, 8, "bf16", 0.07, "rho*d just above an integer"),
     # norms finalized in their own launch before the selection: d above the
-    # one-workgroup norm+select kernel, and more row chunks than it takes
+    # one-workgroup norm+select kernel, and more row chunks (65 x 1024
+    # partials) than it takes
     (64, 20480, 64, "bf16", 0.5, "d above the fused selection"),
-    (65536, 256, 64, "bf16", 0.5, "many row chunks"),
+    (33000, 1024, 64, "bf16", 0.5, "many row chunks"),
 ]
+SEPARATE_FINALIZE = {"d above the fused selection", "many row chunks"}
 
 
 @pytest.mark.parametrize("n,d,m,dtype,rho,note", ODD, ids=[o[-1] for o in ODD])
@@ -125,8 +127,16 @@ def test_odd_shapes(rmm, torch, n, d, m, dtype, rho, note):
     if n > 1 and k < d:
         A, _ = enforce_gap_2d(A, k, dtype)
     ref_idx = oracle.topk(oracle.colnorm(A), k)
-    Y, idx = rmm.matmul(to_device(A, dtype), to_device(B, dtype), rho)
-    torch.cuda.synchronize()
+    Ad, Bd = to_device(A, dtype), to_device(B, dtype)
+    rmm.timing_enable(True)
+    try:
+        Y, idx = rmm.matmul(Ad, Bd, rho)
+        torch.cuda.synchronize()
+        launches = {kind: cnt for kind, (_, cnt) in rmm.timing_collect().items()}
+    finally:
+        rmm.timing_enable(False)
+    if note in SEPARATE_FINALIZE:  # the case reaches the path it is meant to cover
+        assert launches["finalize"] == 1, launches
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
     B64 = B.astype(np.float64)
     assert_close(to_host(Y), oracle.reduced_product(A, B64, ref_idx),
