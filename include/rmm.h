@@ -164,7 +164,9 @@ enum {
     RMM_GEMM_TILE128 = 1, /* 128x128 tiles (small or short products) */
     RMM_GEMM_ADIRECT = 2, /* 256x256, A in operand blocks straight to registers */
     RMM_GEMM_STREAM = 3,  /* persistent single-K-step kernel (scores Q K^T) */
-    RMM_GEMM_BDMA = 4     /* as ADIRECT, B rows staged by LDS-DMA loads */
+    RMM_GEMM_BDMA = 4,    /* as ADIRECT, B rows staged by LDS-DMA loads */
+    RMM_GEMM_TDMA = 5     /* 256x256, rows of A^T (written by the norm pass in
+                             place of a pack) and of B staged by LDS-DMA loads */
 };
 rmm_status_t rmm_plan_info(const rmm_desc_t *desc, double rho, int32_t *info);
 
@@ -176,13 +178,15 @@ rmm_status_t rmm_plan_info(const rmm_desc_t *desc, double rho, int32_t *info);
  *   4. Y_b = alpha * A_b[:, I_b] B_g[I_b, :].
  *   A, B, Y   device pointers laid out as the descriptor says
  *   idx_out   device, batch x k int32 (row b at idx_out + b*k), or NULL
- *   workspace device scratch of rmm_workspace_size(desc, rho) bytes; any
- *             contents on entry
+ *   workspace device scratch of rmm_workspace_size(desc, rho) bytes,
+ *             256-byte aligned (as every hipMalloc block is); any contents
+ *             on entry
  * Precision: bf16 inputs are contracted on bf16 MFMA with fp32 accumulation
  * (decode, n = 1: fp32 FMA); fp32 inputs with fp32 FMA.  Each output sums
  * its k terms in a fixed order, so repeated calls are bit-identical.
- * Errors: RMM_ERR_INVALID_ARG for an invalid descriptor, rho, or NULL
- * A, B, Y; RMM_ERR_WORKSPACE when ws_bytes is too small; RMM_ERR_HIP when a
+ * Errors: RMM_ERR_INVALID_ARG for an invalid descriptor, rho, NULL A, B,
+ * Y, or a workspace that is not 256-byte aligned; RMM_ERR_WORKSPACE when
+ * ws_bytes is too small; RMM_ERR_HIP when a
  * launch fails (outputs may then be partly written).
  */
 rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,

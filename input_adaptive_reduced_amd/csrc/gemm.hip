@@ -42,6 +42,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int BK = 64;  // K step: 64 bf16 = eight 16-byte chunks per LDS row
 constexpr int kBdmaListRows = 16384;  // u16 list entries gemm_bdma_kernel keeps in LDS
+constexpr int kTdmaListRows = 8192;   // u16 list entries gemm_tdma_kernel keeps in LDS
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
@@ -809,6 +810,196 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
     store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
+// Reduced product with both operands gathered by rows through LDS: A^T
+// (the activation block transposed, d x n, written by the column-norm pass)
+// supplies rows A^T[I_t, :] exactly as B supplies rows B[I_t, :], so neither
+// operand needs a separate pack pass.
+//
+// Tile and waves are those of gemm_bdma_kernel (256x256, four waves of
+// 128x128).  Each K step's 64 x 256 tiles of both operands sit in one of two
+// LDS stages per operand (4 x 32 KB), filled by LDS-DMA buffer loads in the
+// layout ds_read_b64_tr_b16 reads conflict-free (chunk c of row k at
+// c ^ 2(k & 3)); the transposed reads give the A fragments the same
+// per-lane layout as the B fragments (eight consecutive k of one row), the
+// layout the operand blocks of gemm_adirect_kernel hold.  One barrier per
+// step, after sub-step 2: every wave waits for its own loads of step kt+1
+// (vmcnt(0): the LDS-DMA loads are its only vector-memory loads), and the
+// barrier both publishes stage kt+1 and certifies that every wave has read
+// its last operands of stage kt (sub-step 3's fragments were read during
+// sub-step 2).  Sub-step 3 then refills stage kt with step kt+2 (16 loads
+// per wave, interleaved with its MFMAs) and reads sub-step 0 of step kt+1,
+// so a step's loads have a step and a quarter to land.  The kept row list
+// lives in LDS as 16-bit numbers (kTdmaListRows entries per split, 0xffff
+// for padding: such rows read as zero).  Measured on MI355X at the shape of
+// a 4096 x 4096 x 4096 projection: 2-5% slower per step than the A-direct
+// kernel, which is less than the pack pass it makes unnecessary.
+template <bool SPLIT>
+__global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128;
+    constexpr int FM = 4, FN = 4;
+    constexpr int CPR = 32;
+    constexpr int BUF = BK * CPR;  // uint4 per stage (32 KB)
+    __shared__ uint4 sA0[BUF];
+    __shared__ uint4 sA1[BUF];
+    __shared__ uint4 sB0[BUF];
+    __shared__ uint4 sB1[BUF];
+    __shared__ __align__(16) uint16_t sIdx[kTdmaListRows];
+    typedef __attribute__((address_space(3))) void lds_t;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+    const int tiles_m = (int)((g.n + BM - 1) / BM), tiles_n = (int)((g.m + BN - 1) / BN);
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t b = blockIdx.z;
+    const int split = blockIdx.y;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (b / g.group) * g.strideB, g.b_bytes);
+    const int32_t *idx = g.idx + b * g.ld_idx;
+
+    const int KT = (int)(g.kpad / BK);
+    const int per = ((KT + g.splits - 1) / g.splits + 1) & ~1;
+    const int kt0 = split * per;
+    const int kt1 = min(KT, kt0 + per);
+    const int kte = kt0 + (max(kt1 - kt0, 0) + 1) / 2 * 2;
+    const uint32_t lda2 = (uint32_t)(g.lda * 2), ma2 = (uint32_t)(m0 * 2);
+    const uint32_t ldb2 = (uint32_t)(g.ldb * 2), nb2 = (uint32_t)(n0 * 2);
+    const int hsel = lane >> 5, pos = lane & 31;
+
+    auto load_rows = [&](int kt, uint32_t (&o)[8]) {
+        const int t0 = (kt - kt0) * BK + 16 * w;
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(sIdx + t0);
+        const uint4 v1 = *reinterpret_cast<const uint4 *>(sIdx + t0 + 8);
+        const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = hsel ? (wd[i] >> 16) : (wd[i] & 0xffffu);
+    };
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, uint32_t ld2, uint32_t c2, uint4 *dst, int i0, int i1,
+                   const uint32_t (&rows)[8]) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+            const int kr = 16 * w + 2 * i + hsel;
+            const uint32_t c = (uint32_t)(pos ^ ((kr & 3) << 1));
+            const uint32_t row = rows[i];
+            const uint32_t off = (row * ld2 + c2 + c * 16u) | (row == 0xffffu ? kOob : 0u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_t *)&dst[(16 * w + 2 * i) * CPR], 16, off, 0, 0, 0);
+        }
+    };
+    auto read_tr = [&](const uint4 *stg, int ks, int base, bf16x8_t (&f)[4]) {
+        const int gq = lane >> 4, li = lane & 15;
+        const int kbase = ks * 16 + 8 * (gq >> 1) + (li >> 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int nn = base + j * 32 + 16 * (gq & 1) + 4 * (li & 3);
+            union {
+                v4i16_t h[2];
+                bf16x8_t v;
+            } u;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int k = kbase + 4 * hh;
+                const char *p = reinterpret_cast<const char *>(&stg[k * CPR + ((nn >> 3) ^ ((k & 3) << 1))]) +
+                                ((nn >> 2) & 1) * 8;
+                u.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
+            }
+            f[j] = u.v;
+        }
+    };
+    auto stA = [&](auto Sc) -> uint4 * {
+        if constexpr (decltype(Sc)::value % 2 == 0) return sA0; else return sA1;
+    };
+    auto stB = [&](auto Sc) -> uint4 * {
+        if constexpr (decltype(Sc)::value % 2 == 0) return sB0; else return sB1;
+    };
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    bf16x8_t fa[2][FM], fb[2][FN];
+    uint32_t rows[8];
+
+    auto step = [&](int kt, auto Sc) {
+        constexpr int S = decltype(Sc)::value;
+        const uint4 *cA = stA(std::integral_constant<int, S>{});
+        const uint4 *cB = stB(std::integral_constant<int, S>{});
+        const uint4 *oA = stA(std::integral_constant<int, S + 1>{});
+        const uint4 *oB = stB(std::integral_constant<int, S + 1>{});
+        uint4 *dA = stA(std::integral_constant<int, S>{});
+        uint4 *dB = stB(std::integral_constant<int, S>{});
+        load_rows(kt + 2, rows);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) {
+                read_tr(cB, ks + 1, wn * WTN, fb[(ks + 1) & 1]);
+                read_tr(cA, ks + 1, wm * WTM, fa[(ks + 1) & 1]);
+            } else {
+                read_tr(oB, 0, wn * WTN, fb[0]);
+                read_tr(oA, 0, wm * WTM, fa[0]);
+                dma(rA, lda2, ma2, dA, 0, 8, rows);
+                dma(rB, ldb2, nb2, dB, 0, 8, rows);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+            if (ks < 3) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks == 2) {
+                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    if (kt0 < kt1) {
+        const int nlist = (kte - kt0 + 2) * BK;
+        for (int t = tid; t < nlist; t += 256) {
+            const int32_t v = t < (kt1 - kt0) * BK ? idx[kt0 * BK + t] : -1;
+            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
+        }
+        __syncthreads();
+        load_rows(kt0, rows);
+        dma(rA, lda2, ma2, sA0, 0, 8, rows);
+        dma(rB, ldb2, nb2, sB0, 0, 8, rows);
+        load_rows(kt0 + 1, rows);
+        dma(rA, lda2, ma2, sA1, 0, 8, rows);
+        dma(rB, ldb2, nb2, sB1, 0, 8, rows);
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_tr(sB0, 0, wn * WTN, fb[0]);
+        read_tr(sA0, 0, wm * WTM, fa[0]);
+        for (int kt = kt0; kt < kte; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+    uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : w == 2 ? sB0 : sB1;
+    store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
+}
+
 // Reduced product for one or two 64-entry K steps (kpad = 64 or 128), both
 // operands in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I],
 // i.e. the kept columns of the keys for Q K^T).  Such products are bound by
@@ -1426,6 +1617,24 @@ static bool bdma_ok(int64_t kpad, int splits, int64_t d, int transB) {
     return (per3 + 2) * BK <= kBdmaListRows && per3 * 100 <= per * 102;
 }
 
+// The two-operand LDS-DMA kernel keeps the list of a split's K range (plus
+// the two steps loaded past it) in 16 KB.
+static bool tdma_ok(int64_t kpad, int splits, int64_t d) {
+    if (d >= 0xffff) return false;
+    const int64_t KT = kpad / BK;
+    const int64_t per = std::min<int64_t>(((KT + splits - 1) / splits + 1) & ~1LL, KT);
+    return (per + 2) * BK <= kTdmaListRows;
+}
+
+GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d) {
+    GemmConfig c = gemm_choose_tile(n, m, k, 1);
+    if (c.tile == 0 && tdma_ok((k + 127) / 128 * 128, c.splits, d))
+        c.tile = 5;
+    else
+        c.tile = -1;
+    return c;
+}
+
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB) {
     if (transB && k <= 2 * BK && ((n + 255) / 256) * ((m + 255) / 256) * batch >= 512) {
         // one or two K steps, many tiles (scores Q K^T): write-bound streaming kernel
@@ -1510,6 +1719,16 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
             gemm_stream_kernel<4><<<grid, 256, 0, stream>>>(a);
         else
             gemm_stream_kernel<8><<<grid, 256, 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    if (c.tile == 5) {
+        if (a.bmode != 0 || a.batch != 1 || !tdma_ok(a.kpad, a.splits, 0)) return hipErrorInvalidValue;
+        const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
+        dim3 grid((unsigned)tiles, (unsigned)a.splits, 1);
+        if (a.splits > 1)
+            gemm_tdma_kernel<true><<<grid, 256, 0, stream>>>(a);
+        else
+            gemm_tdma_kernel<false><<<grid, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {

@@ -176,6 +176,100 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_rows_kernel(const uint16
     }
 }
 
+// bf16 column sums of squares that also write the transposed copy At (d x n,
+// rows ldt apart) of the block: the gather source of the two-operand GEMM,
+// whose kept rows At[I_t, :] are then contiguous like the rows of B.  The
+// pass reads A once, as the plain partial kernel does, and writes it once.
+// Workgroup: a 64-column strip x a chunk of 4 * TPW * 64 rows; wave w takes
+// the 64-row tiles w, w + 4, ...  Lane l owns row block rb = l / 8 (eight
+// rows) and column chunk cc = l % 8 (eight columns): eight 16-byte loads,
+// all issued before the first use, give it an 8 x 8 block, which it
+// transposes in registers with byte permutes and writes as eight 16-byte
+// pieces of At (each store instruction: eight 128-byte row runs).  Squares
+// are summed per lane in row order, then over the eight row blocks of the
+// wave (xor 8, 16, 32) and over the four waves in order: the partial of a
+// column and chunk has a fixed summation order.  n % 8 == 0, so a row block
+// below the chunk end is whole.
+template <int TPW>
+__global__ __launch_bounds__(kNormThreads) void colnorm_transpose_kernel(const uint16_t *__restrict__ A, int64_t n,
+                                                                        int64_t d, int64_t lda,
+                                                                        int64_t rows_per_chunk, int64_t a_bytes,
+                                                                        uint16_t *__restrict__ At, int64_t ldt,
+                                                                        float *__restrict__ part) {
+    __shared__ float red[4][64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rb = lane >> 3, cc = lane & 7;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+    const int64_t r1 = min(n, r0 + rows_per_chunk);
+    const int64_t col = c0 + 8 * cc;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A), (short)0, (int)a_bytes, 0x00020000);
+    uint4 v[TPW][8];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int64_t rbase = r0 + (int64_t)(w + 4 * t) * 64 + 8 * rb;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int64_t row = rbase + q;
+            const uint32_t off = (row < r1 && col < d) ? (uint32_t)((row * lda + col) * 2) : 0x80000000u;
+            v[t][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        }
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int64_t rbase = r0 + (int64_t)(w + 4 * t) * 64 + 8 * rb;
+        uint32_t wd[8][4];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            wd[q][0] = v[t][q].x;
+            wd[q][1] = v[t][q].y;
+            wd[q][2] = v[t][q].z;
+            wd[q][3] = v[t][q].w;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float lo = __uint_as_float(wd[q][h] << 16), hi = __uint_as_float(wd[q][h] & 0xffff0000u);
+                acc[2 * h] = fmaf(lo, lo, acc[2 * h]);
+                acc[2 * h + 1] = fmaf(hi, hi, acc[2 * h + 1]);
+            }
+        if (rbase < r1 && col < d) {
+            // column e of the block: the low (e even) or high (e odd) halves
+            // of word e / 2 of rows 0..7, paired into four words
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                uint4 o;
+                o.x = __builtin_amdgcn_perm(wd[1][e >> 1], wd[0][e >> 1], sel);
+                o.y = __builtin_amdgcn_perm(wd[3][e >> 1], wd[2][e >> 1], sel);
+                o.z = __builtin_amdgcn_perm(wd[5][e >> 1], wd[4][e >> 1], sel);
+                o.w = __builtin_amdgcn_perm(wd[7][e >> 1], wd[6][e >> 1], sel);
+                *reinterpret_cast<uint4 *>(At + (col + e) * ldt + rbase) = o;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float x = acc[e];
+        x += __shfl_xor(x, 8, 64);
+        x += __shfl_xor(x, 16, 64);
+        x += __shfl_xor(x, 32, 64);
+        acc[e] = x;
+    }
+    if (rb == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[w][8 * cc + e] = acc[e];
+    }
+    __syncthreads();
+    if (tid < 64 && c0 + tid < d)
+        part[(int64_t)blockIdx.y * d + c0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
 // ------------------------------------------------------------------ block scan
 template <int BS>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sm, int &total) {
@@ -777,6 +871,37 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
     else
         colnorm_partial_kernel<float><<<grid, kNormThreads, 0, stream>>>(
             static_cast<const float *>(A), n, d, lda, strideA, p.tc, p.rows_per_chunk, vec_ok, part);
+    return hipGetLastError();
+}
+
+// 512-row chunks where that still gives at least 512 workgroups, else 256
+// (measured on MI355X: 14.2 us for the 4096 x 4096 block, 26.7 us for
+// 2048 x 14336, reading and writing 4.3-4.7 TB/s).
+ColnormPlan colnorm_transpose_plan(int64_t n, int64_t d) {
+    ColnormPlan p;
+    p.tc = 0;
+    p.strips = (int)((d + 63) / 64);
+    const int64_t big = (int64_t)p.strips * ((n + 511) / 512);
+    p.rows_per_chunk = big >= 512 ? 512 : 256;
+    p.rpt = (int)(p.rows_per_chunk / 256);
+    p.chunks = (int)((n + p.rows_per_chunk - 1) / p.rows_per_chunk);
+    return p;
+}
+
+hipError_t launch_colnorm_transpose(const void *A, int64_t n, int64_t d, int64_t lda, const ColnormPlan &p,
+                                    uint16_t *At, int64_t ldt, float *part, hipStream_t stream) {
+    const int64_t a_bytes = ((n - 1) * lda + d) * 2;
+    if (n % 8 || d % 8 || lda % 8 || ldt % 8 || ((uintptr_t)A & 15) || ((uintptr_t)At & 15) ||
+        a_bytes >= 0x7fffffff || (p.rpt != 1 && p.rpt != 2))
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)p.strips, (unsigned)p.chunks);
+    const uint16_t *Ab = static_cast<const uint16_t *>(A);
+    if (p.rpt == 2)
+        colnorm_transpose_kernel<2><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, p.rows_per_chunk, a_bytes, At,
+                                                                       ldt, part);
+    else
+        colnorm_transpose_kernel<1><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, p.rows_per_chunk, a_bytes, At,
+                                                                       ldt, part);
     return hipGetLastError();
 }
 

@@ -93,13 +93,20 @@ struct Plan {
     int64_t k, kpad;
     bool shortcut;   // rho = 1 fast path: no norms or selection
     bool directA;    // MFMA reads A in place (no pack)
+    bool transA;     // the norm pass writes A^T and the GEMM gathers its rows (no pack)
     ColnormPlan cp;
     GemmConfig gc;
     int gsplits;
     int64_t a_rows;  // rows of the packed A buffer per batch entry
     int64_t b_rows;  // rows of the packed B^T buffer per batch entry
-    size_t off_part, off_s, off_idx, off_Ap, off_Bp, off_gpart, off_aval, total;
+    size_t off_part, off_s, off_idx, off_Ap, off_At, off_Bp, off_gpart, off_aval, total;
 };
+
+// Largest output width for which the A^T route is taken.  It replaces the
+// pack pass (about 15 us on the 4096 x 4096 block) by a second write of A in
+// the norm pass (+5 us) and a GEMM 2-5% slower per step; once m grows the
+// GEMM term dominates (a 4096 x 8192 x 28672 product would lose ~30 us).
+constexpr int64_t kTransAMaxM = 8192;
 
 // Host-side rho -> k (Sec. 3.2); see rmm_k in rmm.h for the rounding rule.
 int64_t k_of(double rho, int64_t d) {
@@ -185,15 +192,25 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     };
     const int64_t batch = ds->batch, d = ds->d, n = ds->n, m = ds->m;
     const bool norms = !p.shortcut && p.route != ROUTE_DECODE;
+    // A^T route: one bf16 product of at most kTransAMaxM output columns with
+    // B stored d x m, whose norms are computed anyway
+    if (p.route == ROUTE_MFMA && norms && batch == 1 && !ds->transB && m <= kTransAMaxM && n % 8 == 0 &&
+        d % 8 == 0 && n * d * 2 < kMaxBufferBytes) {
+        p.gc = gemm_choose_transposed(n, m, k, d);
+        p.transA = p.gc.tile == 5;
+    }
     if (norms) {
-        p.cp = colnorm_plan(ds->dtype, n, d, batch);
+        p.cp = p.transA ? colnorm_transpose_plan(n, d) : colnorm_plan(ds->dtype, n, d, batch);
         p.off_part = take((size_t)p.cp.chunks * d * batch * 4);
         p.off_s = take((size_t)d * batch * 4);
     }
     // the streaming kernel runs one or two whole 64-entry K steps
     if (p.route == ROUTE_MFMA && gemm_choose(n, m, k, batch, d, ds->transB).tile == 3) p.kpad = k <= 64 ? 64 : 128;
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
-    if (p.route == ROUTE_MFMA) {
+    if (p.transA) {
+        p.off_At = take((size_t)d * n * 2);
+        if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * n * m * 4);
+    } else if (p.route == ROUTE_MFMA) {
         p.gc = gemm_choose(n, m, k, batch, d, ds->transB);
         const bool blocks = p.gc.tile >= 2;  // operands in MFMA operand blocks
         if (p.gc.tile == 3) p.kpad = k <= 64 ? 64 : 128;
@@ -331,6 +348,7 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
 
     const Plan p = make_plan(desc, k, A, B, Y);
     if (p.total > 0 && (!workspace || ws_bytes < p.total)) return RMM_ERR_WORKSPACE;
+    if (p.total > 0 && ((uintptr_t)workspace & 255)) return RMM_ERR_INVALID_ARG;  // pieces are 256-byte aligned
     char *ws = static_cast<char *>(workspace);
     if (p.total > 0 && (overlaps(ws, (int64_t)p.total, Y, extY * esz) || overlaps(ws, (int64_t)p.total, A, extA * esz) ||
                         overlaps(ws, (int64_t)p.total, B, extB * esz)))
@@ -359,8 +377,13 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     } else {
         float *part = reinterpret_cast<float *>(ws + p.off_part);
         float *s = reinterpret_cast<float *>(ws + p.off_s);
-        RMM_LAUNCH(RMM_KERNEL_COLNORM,
-                   launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
+        if (p.transA)
+            RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_transpose(A, n, d, ds.lda, p.cp,
+                                                                    reinterpret_cast<uint16_t *>(ws + p.off_At), n,
+                                                                    part, stream));
+        else
+            RMM_LAUNCH(RMM_KERNEL_COLNORM,
+                       launch_colnorm_partial(A, ds.dtype, n, d, ds.lda, batch, ds.strideA, p.cp, part, stream));
         if (norm_select_ok(p.cp.chunks, d)) {
             RMM_LAUNCH(RMM_KERNEL_SELECT, launch_norm_select(part, p.cp.chunks, d, batch, k, idx_out, k, pidx, p.kpad,
                                                              stream));
@@ -399,6 +422,37 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     // ROUTE_MFMA: step 3 (gather) then step 4 (reduced product)
     GemmArgs g;
     memset(&g, 0, sizeof(g));
+    if (p.transA) {
+        // both operands gathered by rows inside the GEMM: rows I_t of A^T and of B
+        g.A = reinterpret_cast<const uint16_t *>(ws + p.off_At);
+        g.lda = n;
+        g.strideA = 0;
+        g.a_bytes = d * n * 2;
+        g.B = static_cast<const uint16_t *>(B);
+        g.ldb = ds.ldb;
+        g.strideB = 0;
+        g.group = 1;
+        g.bmode = 0;
+        g.idx = pidx;
+        g.ld_idx = p.kpad;
+        g.Y = static_cast<uint16_t *>(Y);
+        g.ldy = ds.ldy;
+        g.strideY = 0;
+        g.n = n;
+        g.m = m;
+        g.k = k;
+        g.kpad = p.kpad;
+        g.b_bytes = b_extent_bytes(desc);
+        g.batch = 1;
+        g.alpha = ds.alpha;
+        g.splits = p.gc.splits;
+        g.part = p.gc.splits > 1 ? reinterpret_cast<float *>(ws + p.off_gpart) : nullptr;
+        RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
+        if (p.gc.splits > 1)
+            RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(g.part, p.gc.splits, n, m, 1, ds.alpha,
+                                                               static_cast<uint16_t *>(Y), ds.ldy, 0, stream));
+        return RMM_OK;
+    }
     if (p.directA) {
         g.A = static_cast<const uint16_t *>(A);
         g.lda = ds.lda;

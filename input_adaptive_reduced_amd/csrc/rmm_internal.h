@@ -62,6 +62,13 @@ ColnormPlan colnorm_plan(rmm_dtype_t dt, int64_t n, int64_t d, int64_t batch);
 hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
                                   int64_t batch, int64_t strideA, const ColnormPlan &p, float *part,
                                   hipStream_t stream);
+// The same partials (one batch entry, bf16) from a pass that also writes
+// At = A^T (d x n, rows ldt apart), the gather source of gemm_tdma_kernel.
+// n, d, lda and ldt multiples of 8; A and At 16-byte aligned.  The plan's
+// rpt field holds the 64-row tiles per wave (1 or 2).
+ColnormPlan colnorm_transpose_plan(int64_t n, int64_t d);
+hipError_t launch_colnorm_transpose(const void *A, int64_t n, int64_t d, int64_t lda, const ColnormPlan &p,
+                                    uint16_t *At, int64_t ldt, float *part, hipStream_t stream);
 // s[b][j] = sqrt(sum_r part[b][r][j]) in a fixed order.
 hipError_t launch_colnorm_finalize(const float *part, int64_t chunks, int64_t d, int64_t batch, float *s,
                                    hipStream_t stream);
@@ -125,10 +132,15 @@ struct GemmArgs {
 struct GemmConfig {
     int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
                  // 3: persistent single-K-step kernel, both operands in operand blocks,
-                 // 4: as 2 with B rows staged by LDS-DMA loads (gemm_bdma_kernel)
+                 // 4: as 2 with B rows staged by LDS-DMA loads (gemm_bdma_kernel),
+                 // 5: both operands gathered by rows into LDS (gemm_tdma_kernel;
+                 //    A is then A^T, d x n, lda = its row length)
     int splits;  // >= 1
 };
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);
+// Tile 5 with its K splits for a single product whose A is given transposed,
+// or tile -1 when the shape does not suit it.
+GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d);
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream);
 // Y = alpha * sum_s part[s] (s ascending), rounded to bf16.
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,

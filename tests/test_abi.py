@@ -68,6 +68,12 @@ def test_workspace_sizing_and_validation_on_host(lib):
     assert lib.rmm_matmul(None, 1, 1, 0.5, 1, None, None, 0, None) == 1
     assert lib.rmm_select(None, 1, 10, 3, None, None) == 1
     assert lib.rmm_colnorm(None, 1, 2, 2, 2, None, None, 0, None) == 1
+    # a workspace that is not 256-byte aligned is refused before any launch
+    lib.rmm_desc_init(ctypes.byref(ds), r.BF16, 64, 256, 128)
+    need = lib.rmm_workspace_size(ctypes.byref(ds), 0.5)
+    A, B, Y, W = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+    assert lib.rmm_matmul(ctypes.byref(ds), A, B, 0.5, Y, None, W + 16, need, None) == 1
+    assert lib.rmm_matmul(ctypes.byref(ds), A, B, 0.5, Y, None, W, need - 1, None) == 3
 
 
 def test_plan_info_on_host(lib):
@@ -88,8 +94,12 @@ def test_plan_info_on_host(lib):
         st = lib.rmm_plan_info(ctypes.byref(ds), rho, out)
         return st, tuple(out)
 
-    assert info(r.BF16, 4096, 4096, 4096, 0.8) == (0, (1, 2, 1))       # c2: MFMA route, A-direct kernel
-    assert info(r.BF16, 2048, 14336, 4096, 0.8) == (0, (1, 4, 2))      # c3: LDS-DMA kernel, two K splits
+    # c2 and c3: the norm pass writes A^T, both operands gathered by rows (no pack)
+    assert info(r.BF16, 4096, 4096, 4096, 0.8) == (0, (1, 5, 1))
+    assert info(r.BF16, 2048, 14336, 4096, 0.8) == (0, (1, 5, 2))      # two K splits
+    assert info(r.BF16, 4096, 4096, 4096, 1.0) == (0, (1, 2, 1))       # rho = 1 shortcut: no norms, A packed
+    assert info(r.BF16, 4100, 4096, 4096, 0.8) == (0, (1, 2, 1))       # n % 8 != 0: A packed, A-direct kernel
+    assert info(r.BF16, 4096, 8192, 28672, 0.8) == (0, (1, 4, 1))      # c5: wide output keeps the pack; LDS-DMA B
     st, (route, gemm, splits) = info(r.BF16, 1, 8192, 28672, 0.8)     # decode: gathered GEMV
     assert st == 0 and route == 2 and gemm == -1 and splits > 1
     assert info(r.BF16, 4096, 128, 4096, 0.5, transB=1, batch=32, group=4) == (0, (1, 3, 1))  # c4 scores

@@ -80,26 +80,36 @@ def test_small_linear_all_rho(rmm, name, scale):
 
 
 RAGGED = [
-    # (scale, rho, kernel, split K): the 256x256 operand-block kernels with n
-    # not a multiple of 32 and m not a multiple of 256.  bdma rounds each
-    # split's K steps up to a multiple of three with zero steps: 104 -> 105
-    # steps at d = 8200, and 16 -> 18 in the last of two splits at d = 4200,
-    # rho = 0.5.
-    (dict(n=3100, d=1504, m=4000), 0.5, "bdma", False),
-    (dict(n=3100, d=8200, m=4000), 0.8, "bdma", False),
-    (dict(n=2050, d=4200, m=3080), 0.5, "bdma", True),
-    (dict(n=2050, d=4200, m=3080), 0.8, "bdma", True),
-    (dict(n=3100, d=1504, m=4000), 0.8, "adirect", False),
-    (dict(n=2050, d=4200, m=3080), 0.48, "adirect", True),
+    # (scale, rho, kernel, split K, full path): the 256x256 kernels with
+    # ragged n and m not a multiple of 256.  With n % 8 != 0 the operand-block
+    # kernels run (A packed); bdma rounds each split's K steps up to a
+    # multiple of three with zero steps: 104 -> 105 steps at d = 8200, and
+    # 16 -> 18 in the last of two splits at d = 4200, rho = 0.5.
+    (dict(n=3100, d=1504, m=4000), 0.5, "bdma", False, False),
+    (dict(n=3100, d=8200, m=4000), 0.8, "bdma", False, False),
+    (dict(n=2050, d=4200, m=3080), 0.5, "bdma", True, False),
+    (dict(n=2050, d=4200, m=3080), 0.8, "bdma", True, False),
+    (dict(n=3100, d=1504, m=4000), 0.8, "adirect", False, False),
+    (dict(n=2050, d=4200, m=3080), 0.48, "adirect", True, False),
     # rho = 1 (the identity set, A packed through the index list 0..d-1)
-    (dict(n=3100, d=1536, m=4000), 1.0, "bdma", False),
-    (dict(n=2050, d=4224, m=3080), 1.0, "adirect", True),
+    (dict(n=3100, d=1536, m=4000), 1.0, "bdma", False, False),
+    (dict(n=2050, d=4224, m=3080), 1.0, "adirect", True, False),
+    # n % 8 == 0: the norm pass writes A^T and both operands are gathered by
+    # rows (no pack); the last row tile is partly past n, the last column
+    # tile partly past m; two and three K splits (the last split of the
+    # rho = 0.5 case runs 16 of 18 steps); the full path at rho = 1
+    (dict(n=3104, d=1504, m=4000), 0.5, "tdma", False, False),
+    (dict(n=3104, d=8200, m=4000), 0.8, "tdma", False, False),
+    (dict(n=2048, d=4200, m=3080), 0.5, "tdma", True, False),
+    (dict(n=2048, d=4200, m=3080), 0.8, "tdma", True, False),
+    (dict(n=3104, d=1536, m=4000), 1.0, "tdma", False, True),
 ]
 
 
-@pytest.mark.parametrize("scale,rho,kernel,split", RAGGED,
-                         ids=[f"{k}{'-splitk' if s else ''}-d{c['d']}-rho{r}" for c, r, k, s in RAGGED])
-def test_ragged_large_tiles(rmm, scale, rho, kernel, split):
+@pytest.mark.parametrize("scale,rho,kernel,split,full", RAGGED,
+                         ids=[f"{k}{'-splitk' if s else ''}-d{c['d']}-rho{r}{'-full' if f else ''}"
+                              for c, r, k, s, f in RAGGED])
+def test_ragged_large_tiles(rmm, scale, rho, kernel, split, full):
     # sampled rows include the last rows of the ragged final row block
     torch = pytest.importorskip("torch")
     case, A, B64 = linear_case("c2", scale, rhos=(rho,))
@@ -107,9 +117,9 @@ def test_ragged_large_tiles(rmm, scale, rho, kernel, split):
     rows = sorted(set(sample_rows(n, 12, seed=5)) | {n - 1, n - 2, n - 17, n - 33})
     Am = torch.empty(A.shape, dtype=torch.bfloat16, device="meta")
     Bm = torch.empty(case.B.shape, dtype=torch.bfloat16, device="meta")
-    info = rmm.plan_info(Am, Bm, rho)
+    info = rmm.plan_info(Am, Bm, rho, full_path=full)
     assert info["gemm"] == kernel and (info["splits"] > 1) == split, info
-    check_linear(rmm, case, A, B64, rho, rows=rows)
+    check_linear(rmm, case, A, B64, rho, rows=rows, full_path=full)
 
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c5"])

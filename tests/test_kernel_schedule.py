@@ -4,15 +4,21 @@
    point to either LDS or global memory compiles to flat accesses, which wait
    on both counters and serialise a gather (this once cost the A pack a fifth
    of its time).
-2. An ordering argument the LDS-DMA product kernel relies on.
+2. Ordering arguments the LDS-DMA product kernels rely on.
 
 gemm_bdma_kernel waits for its own LDS-DMA loads of the next K step with
 ``s_waitcnt vmcnt(28)``: vector-memory loads retire in issue order, so the
 wait covers those loads only if at least 28 loads are issued after the last
 of them and before the wait.  The kernel fences its sub-steps with scheduling
 barriers so that this holds by construction; this test compiles the kernel
-to gfx950 assembly and checks it in every loop that contains the wait.  No
-GPU is used.
+to gfx950 assembly and checks it in every loop that contains the wait.
+
+gemm_tdma_kernel keeps two LDS stages per operand: each wave waits for all
+of its own LDS-DMA loads (vmcnt(0)) right before the workgroup barrier, and
+refills a stage only after that barrier, since only then has every wave
+read its last operands from it.  The test checks that in the compiled loop
+every barrier directly follows such a wait and that all 16 LDS-DMA loads of
+a step come after a barrier and before the next wait.  No GPU is used.
 """
 import os
 import re
@@ -104,3 +110,39 @@ def test_bdma_wait_covers_its_dma(gemm_asm):
         for seq in seqs:
             assert seq.count("W") % 3 == 0
             assert min_younger(seq) >= 28, "".join(seq)
+
+
+def loop_tokens(asm: str, kernel: str):
+    """Per loop of `kernel` that contains a barrier: D = LDS-DMA load,
+    W = wait for every vector-memory load, B = barrier."""
+    lines = asm.split("\n")
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*" + kernel + r"\S*:", l))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    body = lines[start:end]
+    for h, l in enumerate(body):
+        if "Loop Header" not in l:
+            continue
+        stop = next((i for i in range(h + 1, len(body))
+                     if body[i].startswith(".LBB") and "in Loop" not in body[i]), len(body))
+        seq = []
+        for x in body[h:stop]:
+            x = x.strip()
+            if x.startswith("buffer_load") and " lds" in x:
+                seq.append("D")
+            elif x.startswith("s_waitcnt") and "vmcnt(0)" in x:
+                seq.append("W")
+            elif x.startswith("s_barrier"):
+                seq.append("B")
+        if "B" in seq:
+            yield "".join(seq)
+
+
+def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm):
+    for split in ("0", "1"):
+        loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernelILb" + split))
+        assert loops, "no K loop with a barrier found"
+        for seq in loops:
+            assert seq.count("B") == 2, seq  # two K steps per iteration, one barrier each
+            # rotate to start at a barrier: then B D^16 W B D^16 W
+            r = seq[seq.index("B"):] + seq[:seq.index("B")]
+            assert re.fullmatch(r"(BD{16}W){2}", r), seq
