@@ -159,10 +159,12 @@ class Runner:
 
 
 def time_steps(torch, fn, steps, warmup, copies, graph):
-    """Mean ms per step over `steps` calls of fn(i) rotating over copies."""
-    for i in range(warmup):
-        fn(i % copies)
-    torch.cuda.synchronize()
+    """Mean ms per step over `steps` calls of fn(i) rotating over copies.
+
+    With graphs, each input set's step is captured once (after one eager call
+    per set on the capture stream); the `warmup` untimed steps are then replays
+    of the same graphs the timed steps replay, so the timed region starts with
+    the GPU already running that exact work."""
     if graph:
         graphs = []
         s = torch.cuda.Stream()
@@ -177,12 +179,12 @@ def time_steps(torch, fn, steps, warmup, copies, graph):
             with torch.cuda.graph(g):
                 fn(i)
             graphs.append(g)
-        for i in range(copies):
-            graphs[i].replay()
-        torch.cuda.synchronize()
         run = lambda i: graphs[i % copies].replay()  # noqa: E731
     else:
         run = lambda i: fn(i % copies)  # noqa: E731
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

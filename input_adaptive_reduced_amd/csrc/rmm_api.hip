@@ -103,10 +103,12 @@ struct Plan {
 };
 
 // Largest output width for which the A^T route is taken.  It replaces the
-// pack pass (about 15 us on the 4096 x 4096 block) by a second write of A in
-// the norm pass (+5 us) and a GEMM 2-5% slower per step; once m grows the
-// GEMM term dominates (a 4096 x 8192 x 28672 product would lose ~30 us).
-constexpr int64_t kTransAMaxM = 8192;
+// pack pass by a second write of A in the norm pass, and its two-operand
+// GEMM runs a K step as fast as the operand-block kernels up to m = 4096 and
+// 0.7% slower at m = 28672 (MI355X): on a 4096 x 8192 block the pack costs
+// 28 us and the extra write 15 us, so the route still gains ~5 us on a
+// 4096 x 8192 x 28672 product and would break even near m = 57000.
+constexpr int64_t kTransAMaxM = 32768;
 
 // Host-side rho -> k (Sec. 3.2); see rmm_k in rmm.h for the rounding rule.
 int64_t k_of(double rho, int64_t d) {

@@ -99,7 +99,8 @@ def test_plan_info_on_host(lib):
     assert info(r.BF16, 2048, 14336, 4096, 0.8) == (0, (1, 5, 2))      # two K splits
     assert info(r.BF16, 4096, 4096, 4096, 1.0) == (0, (1, 2, 1))       # rho = 1 shortcut: no norms, A packed
     assert info(r.BF16, 4100, 4096, 4096, 0.8) == (0, (1, 2, 1))       # n % 8 != 0: A packed, A-direct kernel
-    assert info(r.BF16, 4096, 8192, 28672, 0.8) == (0, (1, 4, 1))      # c5: wide output keeps the pack; LDS-DMA B
+    assert info(r.BF16, 4096, 8192, 28672, 0.8) == (0, (1, 5, 1))      # c5
+    assert info(r.BF16, 4096, 8192, 40960, 0.8) == (0, (1, 4, 1))      # wider output keeps the pack; LDS-DMA B
     st, (route, gemm, splits) = info(r.BF16, 1, 8192, 28672, 0.8)     # decode: gathered GEMV
     assert st == 0 and route == 2 and gemm == -1 and splits > 1
     assert info(r.BF16, 4096, 128, 4096, 0.5, transB=1, batch=32, group=4) == (0, (1, 3, 1))  # c4 scores
