@@ -826,13 +826,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
 // (vmcnt(0): the LDS-DMA loads are its only vector-memory loads), and the
 // barrier both publishes stage kt+1 and certifies that every wave has read
 // its last operands of stage kt (sub-step 3's fragments were read during
-// sub-step 2).  Sub-step 3 then refills stage kt with step kt+2 (16 loads
-// per wave, interleaved with its MFMAs) and reads sub-step 0 of step kt+1,
-// so a step's loads have a step and a quarter to land.  The kept row list
-// lives in LDS as 16-bit numbers (kTdmaListRows entries per split, 0xffff
-// for padding: such rows read as zero).  Measured on MI355X at the shape of
-// a 4096 x 4096 x 4096 projection: 2-5% slower per step than the A-direct
-// kernel, which is less than the pack pass it makes unnecessary.
+// sub-step 2).  The loads are spread over two sub-steps, eight per wave in
+// each, interleaved with the MFMAs: sub-step 3 of step kt refills the A
+// stage of step kt with step kt+2 (a step and a quarter to land) and
+// sub-step 0 of step kt fills the B stage of step kt+1, free since the
+// barrier of step kt-1 (three quarters of a step).  Issuing all sixteen in
+// sub-step 3 measured 4-5% slower on MI355X.  The kept row list lives in LDS
+// as 16-bit numbers (kTdmaListRows entries per split, 0xffff for padding:
+// such rows read as zero).  Per K step it is as fast as the A-direct kernel
+// on a 4096 x 4096 x 4096 projection and 2-4% faster than gemm_bdma_kernel
+// on a 2048 x 14336 x 4096 one, without the pack pass either needs.
 template <bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128;
@@ -929,8 +932,11 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
         const uint4 *cB = stB(std::integral_constant<int, S>{});
         const uint4 *oA = stA(std::integral_constant<int, S + 1>{});
         const uint4 *oB = stB(std::integral_constant<int, S + 1>{});
-        uint4 *dA = stA(std::integral_constant<int, S>{});
-        uint4 *dB = stB(std::integral_constant<int, S>{});
+        uint4 *dA = stA(std::integral_constant<int, S>{});        // receives A of step kt+2
+        uint4 *dB = stB(std::integral_constant<int, S + 1>{});    // receives B of step kt+1
+        uint32_t next[8];  // rows of step kt+1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) next[i] = rows[i];
         load_rows(kt + 2, rows);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -940,26 +946,28 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
             } else {
                 read_tr(oB, 0, wn * WTN, fb[0]);
                 read_tr(oA, 0, wm * WTM, fa[0]);
-                dma(rA, lda2, ma2, dA, 0, 8, rows);
-                dma(rB, ldb2, nb2, dB, 0, 8, rows);
             }
+            if (ks == 0) dma(rB, ldb2, nb2, dB, 0, 8, next);
+            if (ks == 3) dma(rA, lda2, ma2, dA, 0, 8, rows);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
-            if (ks < 3) {
+            if (ks == 0 || ks == 3) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // LDS-DMA load
                 }
             } else {
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -978,12 +986,12 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
             sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
         }
         __syncthreads();
+        // steps kt0 (both operands) and kt0+1 (A; its B is loaded in step kt0's sub-step 0)
         load_rows(kt0, rows);
         dma(rA, lda2, ma2, sA0, 0, 8, rows);
         dma(rB, ldb2, nb2, sB0, 0, 8, rows);
         load_rows(kt0 + 1, rows);
         dma(rA, lda2, ma2, sA1, 0, 8, rows);
-        dma(rB, ldb2, nb2, sB1, 0, 8, rows);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
