@@ -193,6 +193,31 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
                         int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The reduced product over a caller-supplied kept set: steps 3-4 of
+ * rmm_matmul with I given instead of selected.  This is the static variant
+ * of the selection (Sec. 4, "Baselines": one subset of feature dimensions
+ * fixed, e.g. from the prefill activations, and reused for later calls).
+ *   idx      device, batch x k int32 (row b at idx + b*k): the kept indices
+ *            of batch entry b, strictly ascending in [0, d).  An entry that
+ *            is outside [0, d), or not above every earlier in-range entry of
+ *            its row, is dropped: Y is then the product over the remaining
+ *            entries (a list that meets the precondition loses nothing)
+ *   k        1 <= k <= d
+ *   workspace device scratch of rmm_workspace_size_indexed(desc, k) bytes,
+ *            256-byte aligned; any contents on entry
+ * A, B, Y, the descriptor, precision and the fixed summation order are as
+ * for rmm_matmul (the same kept set gives the same Y, bit for bit).
+ * Errors: RMM_ERR_INVALID_ARG for an invalid descriptor, NULL A, B, Y or
+ * idx, k outside [1, d], idx overlapping Y or the workspace, or a workspace
+ * that is not 256-byte aligned; RMM_ERR_WORKSPACE when ws_bytes is too small;
+ * RMM_ERR_HIP when a launch fails.  rmm_workspace_size_indexed returns
+ * SIZE_MAX for an invalid descriptor or k.
+ */
+size_t rmm_workspace_size_indexed(const rmm_desc_t *desc, int64_t k);
+rmm_status_t rmm_matmul_indexed(const rmm_desc_t *desc, const void *A, const void *B, const int32_t *idx,
+                                int64_t k, void *Y, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Optional per-kernel timing for measurement tools.  While enabled, every
  * kernel rmm_matmul enqueues is bracketed by a pair of HIP events recorded
  * on the call's stream (at most `capacity` pairs are kept; later kernels are

@@ -22,6 +22,7 @@ from typing import Optional, Tuple
 __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
+    "matmul_indexed", "plan_info",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,6 +108,10 @@ def load():
     L.rmm_workspace_size.restype = sz
     L.rmm_matmul.argtypes = [ctypes.POINTER(Desc), vp, vp, ctypes.c_double, vp, vp, vp, sz, vp]
     L.rmm_matmul.restype = ctypes.c_int
+    L.rmm_workspace_size_indexed.argtypes = [ctypes.POINTER(Desc), i64]
+    L.rmm_workspace_size_indexed.restype = sz
+    L.rmm_matmul_indexed.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, vp, vp, sz, vp]
+    L.rmm_matmul_indexed.restype = ctypes.c_int
     L.rmm_plan_info.argtypes = [ctypes.POINTER(Desc), ctypes.c_double, ctypes.POINTER(i32)]
     L.rmm_plan_info.restype = ctypes.c_int
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
@@ -311,3 +316,38 @@ def timing_collect() -> dict:
     cnt = (ctypes.c_int64 * n)()
     _check(load().rmm_timing_collect(ms, cnt), "rmm_timing_collect")
     return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def matmul_indexed(A, B, idx, *, transB: bool = False, b_group: int = 1, alpha: float = 1.0, out=None,
+                   workspace=None):
+    """Y = alpha * A[:, I] B[I, :] over a given kept set I (rmm_matmul_indexed).
+
+    idx: int32 device tensor of shape (k,), or (batch, k) for a batched A,
+    each row strictly ascending in [0, d); entries that break this are
+    dropped by the library.  A, B and the other arguments are as for
+    ``matmul``.  Returns Y.
+    """
+    torch = _torch()
+    _require_gpu(A, B)
+    L = load()
+    ds, shape = _desc_for(A, B, transB, b_group, alpha, False, out)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.device != A.device:
+        raise ValueError("idx must be a contiguous int32 tensor on A's device")
+    if idx.dim() != (2 if A.dim() == 3 else 1) or (A.dim() == 3 and idx.shape[0] != ds.batch):
+        raise ValueError("idx must have shape (k,) or (batch, k)")
+    k = int(idx.shape[-1])
+    if out is None:
+        out = torch.empty(shape, dtype=A.dtype, device=A.device)
+    elif tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    need = L.rmm_workspace_size_indexed(ctypes.byref(ds), k)
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(1, "rmm_workspace_size_indexed")
+    if workspace is None:
+        ws, wsb = _workspace(need, A.device)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.rmm_matmul_indexed(ctypes.byref(ds), A.data_ptr(), B.data_ptr(), idx.data_ptr(), k, out.data_ptr(),
+                              None if ws is None else ws.data_ptr(), wsb, _stream(A))
+    _check(st, "rmm_matmul_indexed")
+    return out

@@ -435,6 +435,99 @@ __global__ __launch_bounds__(BS) void select_big_kernel(const float *__restrict_
     }
 }
 
+// ------------------------------------------------------------------ caller-supplied index set
+// Block-wide exclusive maximum (identity -1) of one int per thread.
+template <int BS>
+__device__ __forceinline__ int block_exclusive_max(int v, int *sm, int &total) {
+    constexpr int NW = BS / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x = max(x, y);
+    }
+    if (lane == 63) sm[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        const int t = lane < NW ? sm[lane] : -1;
+        int u = t;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const int y = __shfl_up(u, o, 64);
+            if (lane >= o) u = max(u, y);
+        }
+        const int ex = __shfl_up(u, 1, 64);
+        if (lane < NW) sm[lane] = lane == 0 ? -1 : ex;
+        if (lane == NW - 1) sm[NW] = u;
+    }
+    __syncthreads();
+    const int below = __shfl_up(x, 1, 64);
+    const int res = max(sm[w], lane == 0 ? -1 : below);
+    total = sm[NW];
+    __syncthreads();
+    return res;
+}
+
+// A caller-supplied kept set (the static variant of the selection: the same
+// I reused across calls) turned into the padded list the gather kernels
+// read.  Entry t of row b is kept when it lies in [0, d) and exceeds every
+// earlier in-range entry of the row, so the kept entries are strictly
+// ascending whatever the input; they are compacted to the front and the
+// rest of the ld_pad slots are -1.  For a decode row (a_row given) the kept
+// values a[I_t] go to aval, and the slots from the kept count up to k read
+// row 0 with value 0 instead of -1 (the GEMV reads k slots).  One workgroup
+// per row; the k entries are taken in segments of BS * EP.
+template <int BS, int EP>
+__global__ __launch_bounds__(BS) void index_prepare_kernel(const int32_t *__restrict__ idx_all, int64_t k, int64_t d,
+                                                           int32_t *__restrict__ pad_all, int64_t ld_pad,
+                                                           const uint16_t *__restrict__ a_row,
+                                                           float *__restrict__ aval) {
+    __shared__ int sm[BS / 64 + 1];
+    const int64_t b = blockIdx.x;
+    const int32_t *idx = idx_all + b * k;
+    int32_t *pad = pad_all + b * ld_pad;
+    int carry_max = -1, carry_pos = 0;
+    for (int64_t s0 = 0; s0 < k; s0 += (int64_t)BS * EP) {
+        const int64_t j0 = s0 + (int64_t)threadIdx.x * EP;
+        int32_t v[EP];
+        int tmax = -1;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            v[e] = j0 + e < k ? idx[j0 + e] : -1;
+            if (v[e] >= 0 && v[e] < d) tmax = max(tmax, v[e]);
+        }
+        int seg_max;
+        const int before = max(carry_max, block_exclusive_max<BS>(tmax, sm, seg_max));
+        int run = before, cnt = 0;
+        bool keep[EP];
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            const bool in = v[e] >= 0 && v[e] < d;
+            keep[e] = in && v[e] > run;
+            if (in) run = max(run, v[e]);
+            cnt += keep[e];
+        }
+        int seg_cnt;
+        int pos = carry_pos + block_exclusive_scan<BS>(cnt, sm, seg_cnt);
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+            if (keep[e]) {
+                pad[pos] = v[e];
+                if (aval) aval[b * k + pos] = bf16_to_f32(a_row[v[e]]);
+                ++pos;
+            }
+        }
+        carry_max = max(carry_max, seg_max);
+        carry_pos += seg_cnt;
+    }
+    for (int64_t q = carry_pos + threadIdx.x; q < ld_pad; q += BS) {
+        const bool gemv_slot = aval && q < k;
+        pad[q] = gemv_slot ? 0 : -1;
+        if (gemv_slot) aval[b * k + q] = 0.f;
+    }
+}
+
 // ------------------------------------------------------------------ wave helpers (DPP)
 // Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
 // row (row_shr 1, 2, 4, 8), then row broadcasts of lane 15 and lane 31.
@@ -1006,6 +1099,15 @@ hipError_t launch_select(const float *s, const void *a_src, rmm_dtype_t a_dt, in
         select_big_kernel<1024><<<g, 1024, lds, stream>>>(s, a_src, a_bf16, a_stride, d, k, idx, ld_idx, idx_pad,
                                                           ld_pad, aval, use_lds);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_prepare(const int32_t *idx, int64_t batch, int64_t k, int64_t d, int32_t *idx_pad,
+                                int64_t ld_pad, const void *a_row, float *aval, hipStream_t stream) {
+    if (k < 1 || ld_pad < k || batch < 1 || batch > 65535 || d > INT32_MAX || (aval && (!a_row || batch != 1)))
+        return hipErrorInvalidValue;
+    index_prepare_kernel<1024, 4><<<(unsigned)batch, 1024, 0, stream>>>(idx, k, d, idx_pad, ld_pad,
+                                                                        static_cast<const uint16_t *>(a_row), aval);
     return hipGetLastError();
 }
 

@@ -165,14 +165,14 @@ bool mfma_extents_ok(const rmm_desc_t *ds, int64_t kpad) {
 
 // Alignment-based part of the route choice; pointers may be null when only
 // sizing (then alignment is assumed, which can only over-size).
-Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, const void *Y) {
+Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, const void *Y, bool given = false) {
     Plan p;
     memset(&p, 0, sizeof(p));
     p.k = k;
     // The MFMA kernel runs an even number of 64-wide K steps; the padded
     // columns of packed operands are zero and padded index entries are -1.
     p.kpad = (k + 127) / 128 * 128;
-    p.shortcut = (k == ds->d) && !(ds->flags & RMM_FLAG_FULL_PATH);
+    p.shortcut = !given && (k == ds->d) && !(ds->flags & RMM_FLAG_FULL_PATH);
     const bool bf = ds->dtype == RMM_BF16;
     const bool ptr_ok = (!A || aligned16(A)) && (!B || aligned16(B)) && (!Y || aligned16(Y));
     const bool ld_ok = ds->lda % 8 == 0 && ds->ldb % 8 == 0 && ds->ldy % 8 == 0 && ds->m % 8 == 0 &&
@@ -193,7 +193,7 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
         return o;
     };
     const int64_t batch = ds->batch, d = ds->d, n = ds->n, m = ds->m;
-    const bool norms = !p.shortcut && p.route != ROUTE_DECODE;
+    const bool norms = !given && !p.shortcut && p.route != ROUTE_DECODE;
     // A^T route: one bf16 product of at most kTransAMaxM output columns with
     // B stored d x m, whose norms are computed anyway
     if (p.route == ROUTE_MFMA && norms && batch == 1 && !ds->transB && m <= kTransAMaxM && n % 8 == 0 &&
@@ -232,6 +232,10 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
 }
 
 thread_local hipError_t g_last_error = hipSuccess;
+
+rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, int64_t k, const int32_t *idx_in,
+                        void *Y, int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream,
+                        int64_t extA, int64_t extB, int64_t extY);
 
 #define RMM_LAUNCH(kind, call)              \
     do {                                    \
@@ -340,6 +344,35 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     if (!A || !B || !Y) return RMM_ERR_INVALID_ARG;
     const int64_t k = k_of(rho, desc->d);
     if (k < 1) return RMM_ERR_INVALID_ARG;
+    return run_matmul(desc, A, B, k, nullptr, Y, idx_out, workspace, ws_bytes, stream, extA, extB, extY);
+}
+
+size_t rmm_workspace_size_indexed(const rmm_desc_t *desc, int64_t k) {
+    int64_t ea, eb, ey;
+    if (check_desc(desc, ea, eb, ey) != RMM_OK || k < 1 || k > desc->d) return SIZE_MAX;
+    return make_plan(desc, k, nullptr, nullptr, nullptr, true).total;
+}
+
+rmm_status_t rmm_matmul_indexed(const rmm_desc_t *desc, const void *A, const void *B, const int32_t *idx,
+                                int64_t k, void *Y, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    int64_t extA, extB, extY;
+    rmm_status_t st = check_desc(desc, extA, extB, extY);
+    if (st != RMM_OK) return st;
+    if (!A || !B || !Y || !idx || k < 1 || k > desc->d) return RMM_ERR_INVALID_ARG;
+    return run_matmul(desc, A, B, k, idx, Y, nullptr, workspace, ws_bytes, stream, extA, extB, extY);
+}
+
+}  // extern "C"
+
+namespace rmm {
+namespace {
+
+// Steps 1-4 of rmm_matmul once the arguments are known to be valid; with
+// idx_in (rmm_matmul_indexed) the kept set is the caller's instead of steps
+// 1-2.
+rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, int64_t k, const int32_t *idx_in,
+                        void *Y, int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream,
+                        int64_t extA, int64_t extB, int64_t extY) {
     const rmm_desc_t &ds = *desc;
     const int64_t esz = ds.dtype == RMM_BF16 ? 2 : 4;
     if (overlaps(Y, extY * esz, A, extA * esz) || overlaps(Y, extY * esz, B, extB * esz)) return RMM_ERR_INVALID_ARG;
@@ -347,13 +380,15 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
                     overlaps(idx_out, k * ds.batch * 4, A, extA * esz) ||
                     overlaps(idx_out, k * ds.batch * 4, B, extB * esz)))
         return RMM_ERR_INVALID_ARG;
+    if (idx_in && overlaps(idx_in, k * ds.batch * 4, Y, extY * esz)) return RMM_ERR_INVALID_ARG;
 
-    const Plan p = make_plan(desc, k, A, B, Y);
+    const Plan p = make_plan(desc, k, A, B, Y, idx_in != nullptr);
     if (p.total > 0 && (!workspace || ws_bytes < p.total)) return RMM_ERR_WORKSPACE;
     if (p.total > 0 && ((uintptr_t)workspace & 255)) return RMM_ERR_INVALID_ARG;  // pieces are 256-byte aligned
     char *ws = static_cast<char *>(workspace);
     if (p.total > 0 && (overlaps(ws, (int64_t)p.total, Y, extY * esz) || overlaps(ws, (int64_t)p.total, A, extA * esz) ||
-                        overlaps(ws, (int64_t)p.total, B, extB * esz)))
+                        overlaps(ws, (int64_t)p.total, B, extB * esz) ||
+                        (idx_in && overlaps(ws, (int64_t)p.total, idx_in, k * ds.batch * 4))))
         return RMM_ERR_INVALID_ARG;
 
     const int64_t n = ds.n, d = ds.d, m = ds.m, batch = ds.batch;
@@ -362,8 +397,11 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
     if (p.route == ROUTE_DECODE) {
         float *aval = reinterpret_cast<float *>(ws + p.off_aval);
         float *gpart = reinterpret_cast<float *>(ws + p.off_gpart);
-        RMM_LAUNCH(RMM_KERNEL_SELECT,
-                   launch_select(nullptr, A, RMM_BF16, 0, 1, d, k, idx_out, k, pidx, p.kpad, aval, stream));
+        if (idx_in)
+            RMM_LAUNCH(RMM_KERNEL_SELECT, launch_index_prepare(idx_in, 1, k, d, pidx, p.kpad, A, aval, stream));
+        else
+            RMM_LAUNCH(RMM_KERNEL_SELECT,
+                       launch_select(nullptr, A, RMM_BF16, 0, 1, d, k, idx_out, k, pidx, p.kpad, aval, stream));
         RMM_LAUNCH(RMM_KERNEL_GEMV, launch_gemv_partial(static_cast<const uint16_t *>(B), ds.ldb, m, pidx, aval, k,
                                                         p.gsplits, gpart, stream));
         RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(gpart, p.gsplits, 1, m, 1, ds.alpha,
@@ -373,7 +411,9 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
 
     // steps 1-2: scores and selection (or every index at rho = 1)
     const int32_t *gemm_idx = pidx;
-    if (p.shortcut) {
+    if (idx_in) {
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_index_prepare(idx_in, batch, k, d, pidx, p.kpad, nullptr, nullptr, stream));
+    } else if (p.shortcut) {
         if (idx_out) RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(idx_out, k, k, batch, stream));
         gemm_idx = nullptr;  // identity
     } else {
@@ -519,6 +559,11 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
                                                            static_cast<uint16_t *>(Y), ds.ldy, ds.strideY, stream));
     return RMM_OK;
 }
+
+}  // namespace
+}  // namespace rmm
+
+extern "C" {
 
 rmm_status_t rmm_timing_enable(int32_t enable, int32_t capacity) {
     TimingState &t = g_timing;

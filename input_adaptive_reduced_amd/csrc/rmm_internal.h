@@ -107,6 +107,14 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
                        int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad,
                        void *dst, int64_t dst_stride, int64_t batch, int layout, hipStream_t stream);
 
+// A caller-supplied index set (batch rows of k int32, row b at idx + b*k)
+// into the padded list: entries in [0, d) that exceed every earlier in-range
+// entry of their row, compacted ascending, then -1 up to ld_pad.  With a_row
+// (a bf16 decode row, batch 1) the kept values go to aval[0..k) and the
+// slots after the kept ones up to k hold row 0 with value 0.
+hipError_t launch_index_prepare(const int32_t *idx, int64_t batch, int64_t k, int64_t d, int32_t *idx_pad,
+                                int64_t ld_pad, const void *a_row, float *aval, hipStream_t stream);
+
 // Index rows 0..k-1 then -1 up to ld, per batch entry (rho = 1 shortcut).
 hipError_t launch_iota(int32_t *idx, int64_t k, int64_t ld, int64_t batch, hipStream_t stream);
 

@@ -74,6 +74,23 @@ def test_workspace_sizing_and_validation_on_host(lib):
     A, B, Y, W = 1 << 40, 2 << 40, 3 << 40, 4 << 40
     assert lib.rmm_matmul(ctypes.byref(ds), A, B, 0.5, Y, None, W + 16, need, None) == 1
     assert lib.rmm_matmul(ctypes.byref(ds), A, B, 0.5, Y, None, W, need - 1, None) == 3
+    # the caller-supplied index variant: sizes, argument checks, alignment
+    lib.rmm_workspace_size_indexed.restype = ctypes.c_size_t
+    lib.rmm_workspace_size_indexed.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    lib.rmm_matmul_indexed.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                               ctypes.c_size_t, ctypes.c_void_p]
+    bad = ctypes.c_size_t(-1).value
+    assert lib.rmm_workspace_size_indexed(ctypes.byref(ds), 0) == bad
+    assert lib.rmm_workspace_size_indexed(ctypes.byref(ds), 257) == bad   # k > d
+    need_i = lib.rmm_workspace_size_indexed(ctypes.byref(ds), 128)
+    assert 0 < need_i <= need                                             # no norm buffers
+    I = 5 << 40
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, None, 128, Y, W, need_i, None) == 1
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, I, 0, Y, W, need_i, None) == 1
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, I, 257, Y, W, need_i, None) == 1
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, I, 128, Y, W + 16, need_i, None) == 1
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, I, 128, Y, W, need_i - 1, None) == 3
+    assert lib.rmm_matmul_indexed(ctypes.byref(ds), A, B, Y, 128, Y, W, need_i, None) == 1  # idx inside Y
 
 
 def test_plan_info_on_host(lib):
