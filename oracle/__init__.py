@@ -18,6 +18,12 @@ LLM Inference":
   K head, scaled by 1/sqrt(d_h)                             (Sec. 3.3)
 * ``diagnostics`` -- retained energy (App. B.4 / eq. 16), the Prop. 1 bound
   (eq. 12), the Cor. 1 bound (eq. 14) and the relative bound (eq. 17).
+* ``gated_mlp`` -- the gated MLP block with RMM on its three projections
+  (App. D.1 (ii), eqs. 3-4): Up and Gate select from the model dimension of
+  their input x, Down from the intermediate dimension of its input h, each
+  set from its own input; the gate is SiLU (reading: the Llama block,
+  h = SiLU(x W_gate) * (x W_up), y = h W_down), and h is held in bf16
+  between the two stages, as the GPU stores it.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, library routines, brute force or invariants that the paper fixes.
@@ -211,3 +217,61 @@ def diagnostics(A: np.ndarray, B: np.ndarray, idx: np.ndarray) -> dict:
         "normA_F": float(np.sqrt(ea_tot)),
         "normB_F": float(np.sqrt(eb_tot)),
     }
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 values rounded to the nearest bf16 (ties to even), returned as fp64.
+
+    bf16 keeps the sign, the 8-bit exponent and 7 stored significand bits of
+    binary32, so a normal fp64 value keeps its top 7 of 52 significand bits:
+    the low 45 bits are rounded away to nearest, ties to the even neighbour.
+    Values beyond the largest finite bf16 become infinities; the normal range
+    is what the block produces (no bf16 subnormals are modelled)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    u = a.view(np.uint64).copy()
+    keep_lsb = (u >> np.uint64(45)) & np.uint64(1)
+    u = (u + np.uint64((1 << 44) - 1) + keep_lsb) & ~np.uint64((1 << 45) - 1)
+    r = u.view(np.float64)
+    big = np.abs(r) > 3.3895313892515355e38  # largest finite bf16: (2 - 2^-7) * 2^127
+    if np.any(big & np.isfinite(a)):
+        r = np.where(big & np.isfinite(a), np.copysign(np.inf, a), r)
+    return r
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z), fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+@dataclasses.dataclass
+class MLPResult:
+    idx_in: np.ndarray     # kept model-dimension indices (Up and Gate), int32 ascending
+    h: np.ndarray          # SiLU(gate) * up, rounded to bf16 (fp64 values), all rows
+    idx_h: np.ndarray      # kept intermediate-dimension indices (Down), int32 ascending
+    Y: np.ndarray          # fp64 output rows requested
+
+
+def gated_mlp(x: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, rho_in: float, rho_h: float,
+              rows: Optional[Sequence[int]] = None, threads: Optional[int] = None) -> MLPResult:
+    """The gated MLP block with RMM on Up, Gate and Down (App. D.1 (ii)).
+
+    x is N x d, Wg and Wu are d x m, Wd is m x d (B layouts).  Up and Gate
+    take ceil(rho_in d) indices of x's columns (both from the same input, so
+    the same set); Down takes ceil(rho_h m) indices of h's columns, h being
+    computed for every row because its column norms run over all of them."""
+    d = np.shape(x)[1]
+    m = np.shape(Wg)[1]
+    if np.shape(Wu) != (d, m) or np.shape(Wd)[0] != m:
+        raise ValueError("gated_mlp expects Wg, Wu of shape (d, m) and Wd with m rows")
+    k_in, k_h = k_of(rho_in, d), k_of(rho_h, m)
+    if k_in == 0 or k_h == 0:
+        raise ValueError("invalid retention ratio")
+    idx_in = topk(colnorm(x), k_in)
+    g = reduced_product(x, Wg, idx_in, 1.0, None, threads)
+    u = reduced_product(x, Wu, idx_in, 1.0, None, threads)
+    h = round_bf16(silu(g) * u)
+    idx_h = topk(colnorm(h), k_h)
+    Y = reduced_product(h, Wd, idx_h, 1.0, rows, threads)
+    return MLPResult(idx_in, h, idx_h, Y)
