@@ -218,6 +218,46 @@ rmm_status_t rmm_matmul_indexed(const rmm_desc_t *desc, const void *A, const voi
                                 int64_t k, void *Y, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The gated MLP block with RMM on its three projections (App. D.1 (ii),
+ * eqs. 3-4): Up and Gate map the model dimension d to the intermediate
+ * dimension m and select from x's columns, Down maps m back to d and selects
+ * from h's columns, each set from its own input:
+ *   I = TopK(||x[:, j]||, ceil(rho_in d)),  h = SiLU(x_I Wg_I) * (x_I Wu_I),
+ *   J = TopK(||h[:, j]||, ceil(rho_h m)),   Y = h_J Wd_J.
+ * The gate is SiLU(z) = z / (1 + e^-z) (the Llama block the paper
+ * evaluates); h is rounded to bf16, and its norms are taken from those
+ * bf16 values.  Up and Gate read the same x, so one norm pass and one
+ * selection serve both, and one GEMM over their interleaved weights
+ * computes h with SwiGLU in its epilogue.
+ *
+ * rmm_gated_weights prepares that operand once, outside the hot path:
+ *   Wg, Wu   device bf16, d x m row-major (transposed = 0), or m x d (the
+ *            nn.Linear layout, transposed = 1)
+ *   Wgu      device bf16, d x 2m, 16-byte aligned: columns 64c..64c+31 hold
+ *            Wg's columns 32c..32c+31 and 64c+32..64c+63 Wu's
+ * Errors: RMM_ERR_INVALID_ARG for NULL pointers, d < 1, m not a positive
+ * multiple of 32, an unaligned Wgu or more than 2^31 bytes.
+ *
+ * rmm_gated_mlp:
+ *   x        device bf16, n x d row-major (dense)
+ *   Wgu      from rmm_gated_weights; Wd device bf16, m x d row-major
+ *   Y        device bf16, n x d; h_out (n x m bf16), idx_in_out (ceil(rho_in d)
+ *            int32, ascending) and idx_h_out (ceil(rho_h m) int32) may be NULL
+ *   workspace rmm_gated_mlp_workspace_size(n, d, m, rho_in, rho_h) bytes,
+ *            256-byte aligned
+ * Supported: n and d multiples of 8, m a multiple of 32, 2m <= 32768, every
+ * pointer 16-byte aligned, each operand under 2^31 bytes; otherwise
+ * RMM_ERR_UNSUPPORTED (the size query returns SIZE_MAX).  Other errors as for
+ * rmm_matmul.  Outputs are bit-reproducible (fixed summation orders).
+ */
+rmm_status_t rmm_gated_weights(const void *Wg, const void *Wu, int64_t d, int64_t m, int32_t transposed, void *Wgu,
+                               hipStream_t stream);
+size_t rmm_gated_mlp_workspace_size(int64_t n, int64_t d, int64_t m, double rho_in, double rho_h);
+rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64_t n, int64_t d, int64_t m,
+                           double rho_in, double rho_h, void *Y, void *h_out, int32_t *idx_in_out,
+                           int32_t *idx_h_out, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Optional per-kernel timing for measurement tools.  While enabled, every
  * kernel rmm_matmul enqueues is bracketed by a pair of HIP events recorded
  * on the call's stream (at most `capacity` pairs are kept; later kernels are

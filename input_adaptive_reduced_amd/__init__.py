@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
-    "matmul_indexed", "plan_info",
+    "matmul_indexed", "plan_info", "gated_weights", "gated_mlp",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -112,6 +112,13 @@ def load():
     L.rmm_workspace_size_indexed.restype = sz
     L.rmm_matmul_indexed.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, vp, vp, sz, vp]
     L.rmm_matmul_indexed.restype = ctypes.c_int
+    L.rmm_gated_weights.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.rmm_gated_weights.restype = ctypes.c_int
+    L.rmm_gated_mlp_workspace_size.argtypes = [i64, i64, i64, ctypes.c_double, ctypes.c_double]
+    L.rmm_gated_mlp_workspace_size.restype = sz
+    L.rmm_gated_mlp.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp, vp, sz,
+                                vp]
+    L.rmm_gated_mlp.restype = ctypes.c_int
     L.rmm_plan_info.argtypes = [ctypes.POINTER(Desc), ctypes.c_double, ctypes.POINTER(i32)]
     L.rmm_plan_info.restype = ctypes.c_int
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
@@ -351,3 +358,55 @@ def matmul_indexed(A, B, idx, *, transB: bool = False, b_group: int = 1, alpha: 
                               None if ws is None else ws.data_ptr(), wsb, _stream(A))
     _check(st, "rmm_matmul_indexed")
     return out
+
+
+def gated_weights(Wg, Wu, transposed: bool = False):
+    """The interleaved Gate/Up operand for ``gated_mlp`` (rmm_gated_weights).
+
+    Wg, Wu: bf16 (d, m), or (m, d) nn.Linear weights with ``transposed``.
+    Returns a (d, 2m) bf16 tensor."""
+    torch = _torch()
+    _require_gpu(Wg, Wu)
+    if Wg.dtype != torch.bfloat16 or Wu.dtype != torch.bfloat16 or Wg.shape != Wu.shape or Wg.dim() != 2:
+        raise ValueError("Wg and Wu must be bf16 matrices of one shape")
+    if not (Wg.is_contiguous() and Wu.is_contiguous()):
+        raise ValueError("Wg and Wu must be contiguous")
+    d, m = (Wg.shape[1], Wg.shape[0]) if transposed else (Wg.shape[0], Wg.shape[1])
+    out = torch.empty((d, 2 * m), dtype=torch.bfloat16, device=Wg.device)
+    _check(load().rmm_gated_weights(Wg.data_ptr(), Wu.data_ptr(), d, m, 1 if transposed else 0, out.data_ptr(),
+                                    _stream(Wg)), "rmm_gated_weights")
+    return out
+
+
+def gated_mlp(x, Wgu, Wd, rho_in: float, rho_h: float, *, out=None, return_h: bool = False, workspace=None):
+    """The gated MLP block with RMM on Up, Gate and Down (rmm_gated_mlp).
+
+    x: bf16 (n, d); Wgu: from ``gated_weights``; Wd: bf16 (m, d).  Returns
+    (Y, idx_in, idx_h) and h when ``return_h``."""
+    torch = _torch()
+    _require_gpu(x, Wgu, Wd)
+    L = load()
+    n, d = x.shape
+    m = Wd.shape[0]
+    if (x.dtype, Wgu.dtype, Wd.dtype) != (torch.bfloat16,) * 3 or Wgu.shape != (d, 2 * m) or Wd.shape != (m, d):
+        raise ValueError("expected bf16 x (n, d), Wgu (d, 2m), Wd (m, d)")
+    if not (x.is_contiguous() and Wgu.is_contiguous() and Wd.is_contiguous()):
+        raise ValueError("operands must be contiguous")
+    need = L.rmm_gated_mlp_workspace_size(n, d, m, float(rho_in), float(rho_h))
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(2, "rmm_gated_mlp_workspace_size")
+    k_in, k_h = int(L.rmm_k(float(rho_in), d)), int(L.rmm_k(float(rho_h), m))
+    if out is None:
+        out = torch.empty((n, d), dtype=torch.bfloat16, device=x.device)
+    idx_in = torch.empty(k_in, dtype=torch.int32, device=x.device)
+    idx_h = torch.empty(k_h, dtype=torch.int32, device=x.device)
+    h = torch.empty((n, m), dtype=torch.bfloat16, device=x.device) if return_h else None
+    if workspace is None:
+        ws, wsb = _workspace(need, x.device)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.rmm_gated_mlp(x.data_ptr(), Wgu.data_ptr(), Wd.data_ptr(), n, d, m, float(rho_in), float(rho_h),
+                         out.data_ptr(), None if h is None else h.data_ptr(), idx_in.data_ptr(), idx_h.data_ptr(),
+                         ws.data_ptr(), wsb, _stream(x))
+    _check(st, "rmm_gated_mlp")
+    return (out, idx_in, idx_h, h) if return_h else (out, idx_in, idx_h)

@@ -433,6 +433,50 @@ __device__ __forceinline__ void store_tile_256(const GemmArgs &g, const f32x16_t
     }
 }
 
+// SwiGLU epilogue of a 256x256 tile whose B columns interleave gate and up
+// weights in 32-column blocks (launch_gated_weights): a wave's column blocks
+// j = 0, 2 are gate and j = 1, 3 the matching up columns, so lane l holds
+// gate and up of the same four outputs in acc[i][2jj] and acc[i][2jj + 1].
+// Each wave writes h = SiLU(gate) * up, rounded to bf16, for its 128 rows x
+// 64 outputs (columns 128 tn + 64 wn ..) through its LDS region (16-byte
+// chunk c of row r at c ^ (r % 8)): 16 stores of 8 rows x 128 bytes.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
+
+__device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x16_t (&acc)[4][4], uint4 *stage,
+                                                  int64_t m0, int64_t hcol0, int wm, int lane) {
+    constexpr int CPW = 8;  // 16-byte chunks per staged row (64 outputs)
+    char *st = reinterpret_cast<char *>(stage);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + (lane & 31);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c4 = jj * 8 + q * 2 + (lane >> 5);
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    h[e] = silu_f32(g.alpha * acc[i][2 * jj][4 * q + e]) * (g.alpha * acc[i][2 * jj + 1][4 * q + e]);
+                const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
+                *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) =
+                    make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int r = it * 8 + lane / CPW;
+        const int c = lane % CPW;
+        const uint4 v = stage[r * CPW + (c ^ (r & (CPW - 1)))];
+        const int64_t row = m0 + wm * 128 + r;
+        const int64_t col = hcol0 + c * 8;
+        if (row < g.n && col < g.m / 2) *reinterpret_cast<uint4 *>(g.Y + row * g.ldy + col) = v;
+    }
+}
+
 // Reduced product with A fragments loaded straight from HBM into registers
 // (256x256 output tile, 4 waves in a 2x2 grid, each wave 128x128).
 //
@@ -836,7 +880,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
 // such rows read as zero).  Per K step it is as fast as the A-direct kernel
 // on a 4096 x 4096 x 4096 projection and 2-4% faster than gemm_bdma_kernel
 // on a 2048 x 14336 x 4096 one, without the pack pass either needs.
-template <bool SPLIT>
+template <bool SPLIT, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128;
     constexpr int FM = 4, FN = 4;
@@ -1005,7 +1049,10 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
     uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : w == 2 ? sB0 : sB1;
-    store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
+    if constexpr (EPI == 1)
+        store_tile_swiglu(g, acc, stage, m0, n0 / 2 + wn * 64, wm, lane);
+    else
+        store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
 // Reduced product for one or two 64-entry K steps (kpad = 64 or 128), both
@@ -1634,6 +1681,8 @@ static bool tdma_ok(int64_t kpad, int splits, int64_t d) {
     return (per + 2) * BK <= kTdmaListRows;
 }
 
+bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d) { return tdma_ok(kpad, splits, d); }
+
 GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d) {
     GemmConfig c = gemm_choose_tile(n, m, k, 1);
     if (c.tile == 0 && tdma_ok((k + 127) / 128 * 128, c.splits, d))
@@ -1733,10 +1782,15 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         if (a.bmode != 0 || a.batch != 1 || !tdma_ok(a.kpad, a.splits, 0)) return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
         dim3 grid((unsigned)tiles, (unsigned)a.splits, 1);
-        if (a.splits > 1)
-            gemm_tdma_kernel<true><<<grid, 256, 0, stream>>>(a);
-        else
-            gemm_tdma_kernel<false><<<grid, 256, 0, stream>>>(a);
+        if (a.epi == 1) {
+            // SwiGLU needs whole sums: one K range; the interleaved operand is 2 x (outputs) wide
+            if (a.splits != 1 || a.m % 64 != 0 || a.ldy < a.m / 2) return hipErrorInvalidValue;
+            gemm_tdma_kernel<false, 1><<<grid, 256, 0, stream>>>(a);
+        } else if (a.splits > 1) {
+            gemm_tdma_kernel<true, 0><<<grid, 256, 0, stream>>>(a);
+        } else {
+            gemm_tdma_kernel<false, 0><<<grid, 256, 0, stream>>>(a);
+        }
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {
@@ -1758,6 +1812,34 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
     }
     if (c.tile == 0) return launch_tile<256, 256, 2, 2>(a, stream);
     return launch_tile<128, 128, 2, 2>(a, stream);
+}
+
+namespace {
+// One thread per 16-byte piece (8 outputs) of a row of the interleaved operand.
+__global__ __launch_bounds__(256) void gated_weights_kernel(const uint16_t *__restrict__ Wg,
+                                                            const uint16_t *__restrict__ Wu, int64_t d, int64_t m,
+                                                            int transposed, uint16_t *__restrict__ Wgu) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // piece index
+    const int64_t per_row = 2 * m / 8;
+    if (q >= d * per_row) return;
+    const int64_t row = q / per_row, oc = (q - row * per_row) * 8;
+    const int64_t blk = oc / 64, within = oc % 64;
+    const uint16_t *W = within < 32 ? Wg : Wu;
+    const int64_t c = blk * 32 + within % 32;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = transposed ? W[(c + e) * d + row] : W[row * m + c + e];
+    *reinterpret_cast<uint4 *>(Wgu + row * 2 * m + oc) =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+}  // namespace
+
+hipError_t launch_gated_weights(const uint16_t *Wg, const uint16_t *Wu, int64_t d, int64_t m, int transposed,
+                                uint16_t *Wgu, hipStream_t stream) {
+    if (d < 1 || m < 32 || m % 32 || ((uintptr_t)Wgu & 15)) return hipErrorInvalidValue;
+    const int64_t pieces = d * (2 * m / 8);
+    gated_weights_kernel<<<(unsigned)((pieces + 255) / 256), 256, 0, stream>>>(Wg, Wu, d, m, transposed, Wgu);
+    return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,

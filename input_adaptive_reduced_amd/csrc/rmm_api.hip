@@ -237,6 +237,50 @@ rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, in
                         void *Y, int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream,
                         int64_t extA, int64_t extB, int64_t extY);
 
+// ------------------------------------------------------------------ gated MLP block
+struct MlpPlan {
+    int64_t k_in, kpad_in, k_h;
+    ColnormPlan cp;
+    GemmConfig gc;
+    rmm_desc_t down;
+    size_t off_part, off_idx, off_xt, off_h, off_down, down_bytes, total;
+};
+
+rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n, int64_t d, int64_t m, double rho_in,
+                      double rho_h, MlpPlan &p) {
+    memset(&p, 0, sizeof(p));
+    if (n < 1 || d < 1 || m < 1) return RMM_ERR_INVALID_ARG;
+    p.k_in = k_of(rho_in, d);
+    p.k_h = k_of(rho_h, m);
+    if (p.k_in < 1 || p.k_h < 1) return RMM_ERR_INVALID_ARG;
+    if (n % 8 || d % 8 || m % 32 || 2 * m > kTransAMaxM || n * d * 2 >= kMaxBufferBytes ||
+        d * 2 * m * 2 >= kMaxBufferBytes || n * m * 2 >= kMaxBufferBytes || m * d * 2 >= kMaxBufferBytes ||
+        (x && !aligned16(x)) || (Wgu && !aligned16(Wgu)) || (Wd && !aligned16(Wd)))
+        return RMM_ERR_UNSUPPORTED;
+    p.kpad_in = (p.k_in + 127) / 128 * 128;
+    // the two-operand kernel at any size, over one K range (SwiGLU needs whole sums)
+    if (!gemm_tdma_fits(p.kpad_in, 1, d)) return RMM_ERR_UNSUPPORTED;
+    p.gc.tile = 5;
+    p.gc.splits = 1;
+    p.cp = colnorm_transpose_plan(n, d);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    p.off_part = take((size_t)p.cp.chunks * d * 4 + (size_t)d * 4);  // partials, then s
+    p.off_idx = take((size_t)p.kpad_in * 4);
+    p.off_xt = take((size_t)d * n * 2);
+    p.off_h = take((size_t)n * m * 2);
+    rmm_desc_init(&p.down, RMM_BF16, n, m, d);
+    p.down_bytes = make_plan(&p.down, p.k_h, nullptr, nullptr, nullptr).total;
+    p.off_down = take(p.down_bytes);
+    p.total = off;
+    return RMM_OK;
+}
+
+
 #define RMM_LAUNCH(kind, call)              \
     do {                                    \
         timing_begin(stream, kind);         \
@@ -362,9 +406,93 @@ rmm_status_t rmm_matmul_indexed(const rmm_desc_t *desc, const void *A, const voi
     return run_matmul(desc, A, B, k, idx, Y, nullptr, workspace, ws_bytes, stream, extA, extB, extY);
 }
 
+rmm_status_t rmm_gated_weights(const void *Wg, const void *Wu, int64_t d, int64_t m, int32_t transposed, void *Wgu,
+                               hipStream_t stream) {
+    if (!Wg || !Wu || !Wgu || d < 1 || m < 32 || m % 32 || (transposed != 0 && transposed != 1) ||
+        !aligned16(Wgu) || d * 2 * m * 2 >= kMaxBufferBytes)
+        return RMM_ERR_INVALID_ARG;
+    RMM_LAUNCH(RMM_KERNEL_OTHER, launch_gated_weights(static_cast<const uint16_t *>(Wg),
+                                                      static_cast<const uint16_t *>(Wu), d, m, transposed,
+                                                      static_cast<uint16_t *>(Wgu), stream));
+    return RMM_OK;
+}
+
+size_t rmm_gated_mlp_workspace_size(int64_t n, int64_t d, int64_t m, double rho_in, double rho_h) {
+    MlpPlan p;
+    if (mlp_plan(nullptr, nullptr, nullptr, n, d, m, rho_in, rho_h, p) != RMM_OK) return SIZE_MAX;
+    return p.total;
+}
+
+rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64_t n, int64_t d, int64_t m,
+                           double rho_in, double rho_h, void *Y, void *h_out, int32_t *idx_in_out,
+                           int32_t *idx_h_out, void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !Wgu || !Wd || !Y) return RMM_ERR_INVALID_ARG;
+    MlpPlan p;
+    rmm_status_t st = mlp_plan(x, Wgu, Wd, n, d, m, rho_in, rho_h, p);
+    if (st != RMM_OK) return st;
+    if (!aligned16(Y) || (h_out && !aligned16(h_out))) return RMM_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < p.total) return RMM_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return RMM_ERR_INVALID_ARG;
+    char *ws = static_cast<char *>(workspace);
+    const int64_t xb = n * d * 2, wb = d * 2 * m * 2, db = m * d * 2, yb = n * d * 2, hb = n * m * 2;
+    if (overlaps(Y, yb, x, xb) || overlaps(Y, yb, Wgu, wb) || overlaps(Y, yb, Wd, db) ||
+        overlaps(ws, (int64_t)p.total, x, xb) || overlaps(ws, (int64_t)p.total, Wgu, wb) ||
+        overlaps(ws, (int64_t)p.total, Wd, db) || overlaps(ws, (int64_t)p.total, Y, yb) ||
+        (h_out && (overlaps(h_out, hb, x, xb) || overlaps(h_out, hb, Y, yb) || overlaps(h_out, hb, ws, (int64_t)p.total) ||
+                   overlaps(h_out, hb, Wgu, wb) || overlaps(h_out, hb, Wd, db))) ||
+        (idx_in_out && (overlaps(idx_in_out, p.k_in * 4, Y, yb) || overlaps(idx_in_out, p.k_in * 4, ws, (int64_t)p.total))) ||
+        (idx_h_out && (overlaps(idx_h_out, p.k_h * 4, Y, yb) || overlaps(idx_h_out, p.k_h * 4, ws, (int64_t)p.total))))
+        return RMM_ERR_INVALID_ARG;
+    float *part = reinterpret_cast<float *>(ws + p.off_part);
+    int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);
+    uint16_t *xt = reinterpret_cast<uint16_t *>(ws + p.off_xt);
+    uint16_t *h = h_out ? static_cast<uint16_t *>(h_out) : reinterpret_cast<uint16_t *>(ws + p.off_h);
+    // Up and Gate: one norm pass (also writing x^T), one selection (the same input gives the same set)
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_transpose(x, n, d, d, p.cp, xt, n, part, stream));
+    if (norm_select_ok(p.cp.chunks, d)) {
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_norm_select(part, p.cp.chunks, d, 1, p.k_in, idx_in_out, p.k_in, pidx, p.kpad_in, stream));
+    } else {
+        float *s = part + p.cp.chunks * d;
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, 1, s, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, 1, d, p.k_in, idx_in_out, p.k_in, pidx,
+                                                    p.kpad_in, nullptr, stream));
+    }
+    // h = SiLU(x_I Wg_I) * (x_I Wu_I): one GEMM over the interleaved operand, SwiGLU in its epilogue
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = xt;
+    g.lda = n;
+    g.a_bytes = d * n * 2;
+    g.B = static_cast<const uint16_t *>(Wgu);
+    g.ldb = 2 * m;
+    g.b_bytes = wb;
+    g.group = 1;
+    g.bmode = 0;
+    g.idx = pidx;
+    g.ld_idx = p.kpad_in;
+    g.Y = h;
+    g.ldy = m;
+    g.n = n;
+    g.m = 2 * m;
+    g.k = p.k_in;
+    g.kpad = p.kpad_in;
+    g.batch = 1;
+    g.alpha = 1.f;
+    g.splits = 1;
+    g.epi = 1;
+    RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
+    // Down: the reduced product over h's own selection
+    int64_t eA, eB, eY;
+    if (check_desc(&p.down, eA, eB, eY) != RMM_OK) return RMM_ERR_INVALID_ARG;
+    return run_matmul(&p.down, h, Wd, p.k_h, nullptr, Y, idx_h_out, ws + p.off_down, p.down_bytes, stream, eA, eB,
+                      eY);
+}
+
 }  // extern "C"
 
 namespace rmm {
+
 namespace {
 
 // Steps 1-4 of rmm_matmul once the arguments are known to be valid; with

@@ -136,6 +136,7 @@ struct GemmArgs {
     int splits;
     int bmode;
     float alpha;
+    int epi;             // tile 5 only: 0 = Y, 1 = SwiGLU of interleaved gate/up column blocks (see gemm.hip)
 };
 struct GemmConfig {
     int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
@@ -149,7 +150,16 @@ GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d
 // Tile 5 with its K splits for a single product whose A is given transposed,
 // or tile -1 when the shape does not suit it.
 GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d);
+// Whether tile 5 can run a K range of kpad padded entries in `splits` splits
+// (its kept-row list must fit in LDS) for contraction length d.
+bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d);
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream);
+// Gate and up weights of a gated MLP (d x m each; stored m x d, the nn.Linear
+// layout, when `transposed`) interleaved in 32-column blocks into one d x 2m
+// operand: columns 64c..64c+31 = gate columns 32c.., 64c+32..64c+63 = up
+// columns 32c..  m % 32 == 0, 16-byte aligned output.
+hipError_t launch_gated_weights(const uint16_t *Wg, const uint16_t *Wu, int64_t d, int64_t m, int transposed,
+                                uint16_t *Wgu, hipStream_t stream);
 // Y = alpha * sum_s part[s] (s ascending), rounded to bf16.
 hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_t m, int64_t batch, float alpha,
                                 uint16_t *Y, int64_t ldy, int64_t strideY, hipStream_t stream);

@@ -1,0 +1,157 @@
+"""GPU parity of the gated MLP block with RMM on Up, Gate and Down
+(``rmm_gated_mlp``, App. D.1 (ii) of the paper) against the CPU oracle.
+
+* The Up/Gate selection from x's column norms is compared bit for bit (the
+  inputs' TopK boundary gap is opened as for the other products).
+* h = SiLU(x_I Wg_I) * (x_I Wu_I) in bf16 is compared elementwise with the
+  oracle's h within a bound from the arithmetic: fp32 accumulation of the two
+  products (as for a reduced GEMM), the fp32 SiLU, and one bf16 rounding on
+  each side (two values straddling a rounding boundary land one bf16 step,
+  at most 2^-7 relative, apart).
+* h is computed, so its selection cannot have an enforced gap: the Down set
+  is checked against the oracle's TopK of the GPU's own bf16 h, exactly where
+  the gap at the boundary exceeds fp32 norm noise, and the Down product over
+  that set is compared with the oracle's.
+The block's inputs are seeded synthetic stand-ins shaped like a Llama-3.1-8B
+MLP: x with log-normal column scales and 0.5% outlier columns (the recipe of
+the 4096 x 4096 projection workload), weights N(0, 1/fan_in) in bf16."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from gpu_util import assert_close, sample_rows, to_device, to_host
+from oracle.fixup import enforce_gap
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rmm():
+    import input_adaptive_reduced_amd as r
+    r.load()
+    return r
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    return torch
+
+
+def block(seed, n, d, m, rho_in):
+    rng = np.random.default_rng(seed)
+    c = np.exp(rng.standard_normal(d))
+    c[rng.choice(d, size=max(1, int(np.ceil(0.005 * d))), replace=False)] *= 20.0
+    x = synthetic.round_to_bf16((rng.standard_normal((n, d)) * c).astype(np.float32))
+    x, _ = enforce_gap(x, [oracle.k_of(rho_in, d)], "bf16")
+    Wg = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
+    Wu = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
+    Wd = synthetic.round_to_bf16((rng.standard_normal((m, d)) / np.sqrt(m)).astype(np.float32))
+    return x, Wg, Wu, Wd
+
+
+def check_h(h_gpu, x, Wg, Wu, idx, rows):
+    """Elementwise bound for h on the given rows (see the module docstring)."""
+    k = idx.size
+    xa = np.abs(x)
+    g = oracle.reduced_product(x, Wg, idx, 1.0, rows)
+    u = oracle.reduced_product(x, Wu, idx, 1.0, rows)
+    eg = (k + 68) * 2.0 ** -24 * oracle.reduced_product(xa, np.abs(Wg), idx, 1.0, rows) * (1 + 2.0 ** -8)
+    eu = (k + 68) * 2.0 ** -24 * oracle.reduced_product(xa, np.abs(Wu), idx, 1.0, rows) * (1 + 2.0 ** -8)
+    h_ref = oracle.round_bf16(oracle.silu(g) * u)
+    pre = 1.1 * (np.abs(u) + eu) * eg + (np.abs(oracle.silu(g)) + 1.1 * eg) * eu  # product error before rounding
+    pre += 2.0 ** -20 * np.abs(oracle.silu(g) * u)                              # fp32 SiLU and product
+    bound = 2.0 ** -7 * np.abs(h_ref) + 2 * pre + 2.0 ** -133
+    err = np.abs(h_gpu - h_ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), f"h at {worst}: {h_gpu[worst]} vs {h_ref[worst]} (bound {bound[worst]})"
+    rel = np.linalg.norm(h_gpu - h_ref) / max(np.linalg.norm(h_ref), 1e-300)
+    assert rel <= 1e-2, rel
+
+
+def check_down_set(h_gpu, idx_h):
+    """idx_h against the oracle's TopK of the GPU's own h, exactly where the
+    boundary gap exceeds fp32 norm noise; elsewhere the scores of what was
+    kept must not fall below those of what was dropped by more than it."""
+    s = oracle.colnorm(h_gpu)
+    k = idx_h.size
+    ref = oracle.topk(s, k)
+    if k == s.size:
+        assert np.array_equal(idx_h, ref)
+        return
+    order = np.sort(s)[::-1]
+    gap = (order[k - 1] - order[k]) / order[k - 1]
+    if gap > 1e-5:
+        assert np.array_equal(idx_h, ref), f"gap {gap:.2e}"
+    else:
+        assert np.all(np.diff(idx_h) > 0) and idx_h.size == k
+        kept = np.zeros(s.size, bool)
+        kept[idx_h] = True
+        assert s[kept].min() >= s[~kept].max() * (1 - 1e-5)
+
+
+def test_gated_weights_layout(rmm, torch):
+    rng = np.random.default_rng(1)
+    d, m = 72, 96
+    Wg = synthetic.round_to_bf16(rng.standard_normal((d, m)).astype(np.float32))
+    Wu = synthetic.round_to_bf16(rng.standard_normal((d, m)).astype(np.float32))
+    want = np.empty((d, 2 * m), np.float32)
+    for c in range(m // 32):
+        want[:, 64 * c:64 * c + 32] = Wg[:, 32 * c:32 * c + 32]
+        want[:, 64 * c + 32:64 * c + 64] = Wu[:, 32 * c:32 * c + 32]
+    got = to_host(rmm.gated_weights(to_device(Wg, "bf16"), to_device(Wu, "bf16")))
+    assert np.array_equal(got, want)
+    got_t = to_host(rmm.gated_weights(to_device(np.ascontiguousarray(Wg.T), "bf16"),
+                                      to_device(np.ascontiguousarray(Wu.T), "bf16"), transposed=True))
+    assert np.array_equal(got_t, want)
+
+
+MLP = [
+    # (n, d, m, rho_in, rho_h, full rows checked)
+    (512, 1024, 2048, 0.8, 0.7, True),
+    (264, 520, 1056, 0.5, 0.5, True),       # ragged tiles in every dimension
+    (128, 256, 512, 1.0, 1.0, True),        # every index kept
+    (2048, 4096, 14336, 0.8, 0.8, False),   # the 8B MLP block, sampled rows
+]
+
+
+@pytest.mark.parametrize("n,d,m,rho_in,rho_h,full", MLP, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}" for c in MLP])
+def test_gated_mlp_against_oracle(rmm, torch, n, d, m, rho_in, rho_h, full):
+    x, Wg, Wu, Wd = block(n + d + m, n, d, m, rho_in)
+    Wgu = rmm.gated_weights(to_device(Wg, "bf16"), to_device(Wu, "bf16"))
+    Y, idx_in, idx_h, h = rmm.gated_mlp(to_device(x, "bf16"), Wgu, to_device(Wd, "bf16"), rho_in, rho_h,
+                                        return_h=True)
+    torch.cuda.synchronize()
+    k_in = oracle.k_of(rho_in, d)
+    ref_in = oracle.topk(oracle.colnorm(x), k_in)
+    assert np.array_equal(idx_in.cpu().numpy(), ref_in)
+    h_gpu = to_host(h).astype(np.float64)
+    rows = None if full else sample_rows(n, 12, seed=9)
+    check_h(h_gpu if rows is None else h_gpu[rows], x, Wg, Wu, ref_in, rows)
+    idx_h_gpu = idx_h.cpu().numpy()
+    assert idx_h_gpu.size == oracle.k_of(rho_h, m)
+    check_down_set(h_gpu, idx_h_gpu)
+    Wd64 = Wd.astype(np.float64)
+    Yh = to_host(Y) if rows is None else to_host(Y)[rows]
+    assert_close(Yh, oracle.reduced_product(h_gpu, Wd64, idx_h_gpu, 1.0, rows),
+                 oracle.reduced_product(np.abs(h_gpu), np.abs(Wd64), idx_h_gpu, 1.0, rows), idx_h_gpu.size, "bf16",
+                 "down projection")
+
+
+def test_gated_mlp_repeatable_and_h_optional(rmm, torch):
+    x, Wg, Wu, Wd = block(5, 256, 512, 1024, 0.7)
+    xd, Wdd = to_device(x, "bf16"), to_device(Wd, "bf16")
+    Wgu = rmm.gated_weights(to_device(Wg, "bf16"), to_device(Wu, "bf16"))
+    Y1, i1, j1 = rmm.gated_mlp(xd, Wgu, Wdd, 0.7, 0.6)
+    Y2, i2, j2, _ = rmm.gated_mlp(xd, Wgu, Wdd, 0.7, 0.6, return_h=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(i1, i2) and torch.equal(j1, j2)
+
+
+def test_gated_mlp_unsupported_shapes(rmm, torch):
+    x = torch.zeros((100, 256), dtype=torch.bfloat16, device="cuda")  # n % 8 != 0
+    Wgu = torch.zeros((256, 1024), dtype=torch.bfloat16, device="cuda")
+    Wd = torch.zeros((512, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(rmm.RMMError):
+        rmm.gated_mlp(x, Wgu, Wd, 0.5, 0.5)

@@ -137,9 +137,10 @@ def loop_tokens(asm: str, kernel: str):
             yield "".join(seq)
 
 
-def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm):
-    for split in ("0", "1"):
-        loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernelILb" + split))
+@pytest.mark.parametrize("inst", ["ILb0ELi0E", "ILb1ELi0E", "ILb0ELi1E"])  # (split K, epilogue)
+def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm, inst):
+    for split in (inst,):
+        loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernel" + split))
         assert loops, "no K loop with a barrier found"
         for seq in loops:
             assert seq.count("B") == 2, seq  # two K steps per iteration, one barrier each
