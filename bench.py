@@ -51,6 +51,9 @@ WORKLOADS = {
                       label="70B up projection decode: a 1x8192 bf16 x B 8192x28672 bf16"),
     "c4": dict(case="c4", rho=0.5, sweep=(0.5, 0.8, 1.0),
                label="QK^T with head-dim selection: Q 32x4096x128, K 8 GQA heads x4096x128 bf16"),
+    "mlp": dict(case="mlp", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0), mlp=True,
+                label="Llama-3.1-8B-shaped gated MLP block: x 2048x4096, Up/Gate 4096x14336, Down 14336x4096 bf16, "
+                      "one rho for all three projections"),
 }
 
 
@@ -156,6 +159,67 @@ class Runner:
             torch.matmul(self.A[i], self.B[i].t(), out=self.Y[i])
         else:
             torch.matmul(self.A[i], self.B[i], out=self.Y[i])
+
+
+class MLPRunner:
+    """The gated MLP block (rmm_gated_mlp) with its inputs, rotated over copies."""
+
+    def __init__(self, torch, rmm, copies):
+        import numpy as np
+        import synthetic
+        self.torch, self.rmm = torch, rmm
+        dev = torch.device("cuda:0")
+        c = synthetic.make_mlp_case()
+
+        def up(x):
+            bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
+            return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+        x0, Wg0, Wu0, Wd0 = up(c.x), up(c.Wg), up(c.Wu), up(c.Wd)
+        Wgu0 = rmm.gated_weights(Wg0, Wu0)
+        per_set = (x0.numel() + Wgu0.numel() + Wd0.numel()) * 2
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2 * MALL_BYTES / per_set)))
+        self.copies = copies
+        self.x = [x0] + [x0.clone() for _ in range(copies - 1)]
+        self.Wgu = [Wgu0] + [Wgu0.clone() for _ in range(copies - 1)]
+        self.Wd = [Wd0] + [Wd0.clone() for _ in range(copies - 1)]
+        self.Wg = [Wg0] + [Wg0.clone() for _ in range(copies - 1)]
+        self.Wu = [Wu0] + [Wu0.clone() for _ in range(copies - 1)]
+        self.n, self.d = c.x.shape
+        self.m = c.Wg.shape[1]
+        self.batch = 1
+        self.Y = [torch.empty((self.n, self.d), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+        self.G = torch.empty((self.n, self.m), dtype=torch.bfloat16, device=dev)
+        self.U = torch.empty((self.n, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws = {}
+        self.idx = {}
+
+    def flops(self, rho):
+        k_in, k_h = self.rmm.k_of(rho, self.d), self.rmm.k_of(rho, self.m)
+        return 2.0 * self.n * k_in * 2 * self.m + 2.0 * self.n * k_h * self.d
+
+    def call(self, i, rho, full_path=False):
+        torch, rmm = self.torch, self.rmm
+        if rho not in self.ws:
+            import ctypes
+            need = rmm.load().rmm_gated_mlp_workspace_size(self.n, self.d, self.m, rho, rho)
+            if need == ctypes.c_size_t(-1).value:
+                raise rmm.RMMError(2, "rmm_gated_mlp_workspace_size")
+            self.ws[rho] = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+        rmm.gated_mlp(self.x[i], self.Wgu[i], self.Wd[i], rho, rho, out=self.Y[i], workspace=self.ws[rho])
+
+    def plan(self, rho):
+        return {"route": "mfma", "gemm": "tdma", "splits": 1}
+
+    def dense(self, i):
+        """The dense block as torch runs it: Gate and Up products, SiLU * up, Down product."""
+        torch = self.torch
+        torch.matmul(self.x[i], self.Wg[i], out=self.G)
+        torch.matmul(self.x[i], self.Wu[i], out=self.U)
+        h = torch.nn.functional.silu(self.G)
+        h.mul_(self.U)
+        torch.matmul(h, self.Wd[i], out=self.Y[i])
 
 
 def time_steps(torch, fn, steps, warmup, copies, graph):
@@ -291,8 +355,12 @@ def main(argv=None):
         return 0
 
     wl = WORKLOADS[args.workload]
-    case = synthetic.make_case(wl["case"])
-    runner = Runner(torch, rmm, case, wl.get("decode", False), args.copies)
+    is_mlp = wl.get("mlp", False)
+    if is_mlp:
+        runner = MLPRunner(torch, rmm, args.copies)
+    else:
+        case = synthetic.make_case(wl["case"])
+        runner = Runner(torch, rmm, case, wl.get("decode", False), args.copies)
     rho = wl["rho"]
     graph = not args.no_graph
     log(f"workload {args.workload}: {wl['label']}; copies={runner.copies} graph={graph}")
@@ -308,7 +376,7 @@ def main(argv=None):
         dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
         log(f"dense torch.matmul: {dense_ms * 1e3:.1f} us/step")
         for r in wl["sweep"]:
-            for full in ((False, True) if r == 1.0 else (False,)):
+            for full in ((False, True) if r == 1.0 and not is_mlp else (False,)):
                 t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
                                runner.copies, graph)
                 ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
@@ -344,7 +412,7 @@ def main(argv=None):
                 "kernel_ms": gemm_ms}
     else:
         dom = "gemm"
-        gemm_ms = kt["gemm"][0]
+        gemm_ms = kt["gemm"][0] * max(1.0, kt["gemm"][1])  # every GEMM launch of the step (Up/Gate and Down)
         achieved = runner.flops(rho) / (gemm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "gemm_" + runner.plan(rho)["gemm"], "achieved": achieved,
                 "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -354,7 +422,7 @@ def main(argv=None):
     roof["per_kernel_ms"] = {kk: v[0] for kk, v in kt.items() if v[1]}
 
     cpu = None
-    if rank == 0 and not args.no_cpu_baseline:
+    if rank == 0 and not args.no_cpu_baseline and not is_mlp:  # the fp64 block needs every row of h: no bounded sample
         cpu = cpu_baseline(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 

@@ -220,6 +220,31 @@ def make_case(name: str, scale: Optional[dict] = None) -> Case:
     raise KeyError(name)
 
 
+@dataclasses.dataclass
+class MLPCase:
+    """A gated MLP block: x (n x d) and weights Wg, Wu (d x m), Wd (m x d)."""
+    x: np.ndarray
+    Wg: np.ndarray
+    Wu: np.ndarray
+    Wd: np.ndarray
+    rhos: tuple
+
+
+def make_mlp_case(scale: Optional[dict] = None, seed: int = 6) -> MLPCase:
+    """Llama-3.1-8B-shaped gated MLP block (n = 2048 tokens, d = 4096,
+    m = 14336): x from the 8B projection recipe (log-normal column scales,
+    0.5% outlier columns x20), then Wg, Wu ~ N(0, 1/d) and Wd ~ N(0, 1/m), all
+    bf16, drawn in that order.  ``scale`` overrides n, d, m."""
+    s = dict(scale or {})
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n, d, m = s.get("n", 2048), s.get("d", 4096), s.get("m", 14336)
+    x, _ = lognormal_outlier_activations(rng, n, d, "bf16", n_outliers=math.ceil(0.005 * d))
+    Wg = gaussian_weights(rng, d, m, "bf16")
+    Wu = gaussian_weights(rng, d, m, "bf16")
+    Wd = gaussian_weights(rng, m, d, "bf16")
+    return MLPCase(x, Wg, Wu, Wd, (0.5, 0.7, 0.8, 1.0))
+
+
 def make_decode_case(case: Case, seed: int = 55) -> Case:
     """n = 1 decode row for a linear case: a fresh N(0,1) row times the same c_j."""
     if case.scales is None or case.A.ndim != 2:

@@ -12,9 +12,9 @@
   is checked against the oracle's TopK of the GPU's own bf16 h, exactly where
   the gap at the boundary exceeds fp32 norm noise, and the Down product over
   that set is compared with the oracle's.
-The block's inputs are seeded synthetic stand-ins shaped like a Llama-3.1-8B
-MLP: x with log-normal column scales and 0.5% outlier columns (the recipe of
-the 4096 x 4096 projection workload), weights N(0, 1/fan_in) in bf16."""
+The block's inputs are the seeded synthetic stand-ins of
+``synthetic.make_mlp_case`` (a Llama-3.1-8B-shaped block; smaller sizes for
+the quick cases), with the TopK boundary gap of x opened."""
 import numpy as np
 import pytest
 
@@ -40,15 +40,9 @@ def torch():
 
 
 def block(seed, n, d, m, rho_in):
-    rng = np.random.default_rng(seed)
-    c = np.exp(rng.standard_normal(d))
-    c[rng.choice(d, size=max(1, int(np.ceil(0.005 * d))), replace=False)] *= 20.0
-    x = synthetic.round_to_bf16((rng.standard_normal((n, d)) * c).astype(np.float32))
-    x, _ = enforce_gap(x, [oracle.k_of(rho_in, d)], "bf16")
-    Wg = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
-    Wu = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
-    Wd = synthetic.round_to_bf16((rng.standard_normal((m, d)) / np.sqrt(m)).astype(np.float32))
-    return x, Wg, Wu, Wd
+    c = synthetic.make_mlp_case(dict(n=n, d=d, m=m), seed=seed)
+    x, _ = enforce_gap(c.x, [oracle.k_of(rho_in, d)], "bf16")
+    return x, c.Wg, c.Wu, c.Wd
 
 
 def check_h(h_gpu, x, Wg, Wu, idx, rows):
@@ -118,7 +112,7 @@ MLP = [
 
 @pytest.mark.parametrize("n,d,m,rho_in,rho_h,full", MLP, ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}" for c in MLP])
 def test_gated_mlp_against_oracle(rmm, torch, n, d, m, rho_in, rho_h, full):
-    x, Wg, Wu, Wd = block(n + d + m, n, d, m, rho_in)
+    x, Wg, Wu, Wd = block(6 if (n, d, m) == (2048, 4096, 14336) else n + d + m, n, d, m, rho_in)
     Wgu = rmm.gated_weights(to_device(Wg, "bf16"), to_device(Wu, "bf16"))
     Y, idx_in, idx_h, h = rmm.gated_mlp(to_device(x, "bf16"), Wgu, to_device(Wd, "bf16"), rho_in, rho_h,
                                         return_h=True)
