@@ -437,43 +437,107 @@ __device__ __forceinline__ void store_tile_256(const GemmArgs &g, const f32x16_t
 // weights in 32-column blocks (launch_gated_weights): a wave's column blocks
 // j = 0, 2 are gate and j = 1, 3 the matching up columns, so lane l holds
 // gate and up of the same four outputs in acc[i][2jj] and acc[i][2jj + 1].
-// Each wave writes h = SiLU(gate) * up, rounded to bf16, for its 128 rows x
-// 64 outputs (columns 128 tn + 64 wn ..) through its LDS region (16-byte
-// chunk c of row r at c ^ (r % 8)): 16 stores of 8 rows x 128 bytes.
+// Each wave forms h = SiLU(gate) * up, rounded to bf16, for its 128 rows x
+// 64 outputs (columns 128 tn + 64 wn ..) and, through its LDS region,
+//  * writes h row-major to Y when Y is given (16-byte chunk c of staged row
+//    r at c ^ (r % 8); 16 stores of 8 rows x 128 bytes), and
+//  * writes h^T to Yt when Yt is given (staged as 64 rows of the wave's 128
+//    h rows, 136 elements apart; 16 stores of 4 rows x 256 bytes), with the
+//    sums of squares of the bf16 values of each column over the wave's rows
+//    below n, in row order, into npart[128-row chunk][column]: the column
+//    norms of h for the next projection's selection, without another pass.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
 
 __device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x16_t (&acc)[4][4], uint4 *stage,
-                                                  int64_t m0, int64_t hcol0, int wm, int lane) {
+                                                  int64_t m0, int64_t hcol0, int tm, int wm, int lane) {
     constexpr int CPW = 8;  // 16-byte chunks per staged row (64 outputs)
-    char *st = reinterpret_cast<char *>(stage);
+    const int64_t mh = g.m / 2;
+    uint32_t hp[4][2][4][2];  // [i][jj][q][half]: bf16 pairs of h
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = i * 32 + (lane & 31);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int c4 = jj * 8 + q * 2 + (lane >> 5);
                 float h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     h[e] = silu_f32(g.alpha * acc[i][2 * jj][4 * q + e]) * (g.alpha * acc[i][2 * jj + 1][4 * q + e]);
-                const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
-                *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) =
-                    make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                hp[i][jj][q][0] = pack_bf16x2(h[0], h[1]);
+                hp[i][jj][q][1] = pack_bf16x2(h[2], h[3]);
+            }
+    char *st = reinterpret_cast<char *>(stage);
+    if (g.Y) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c4 = jj * 8 + q * 2 + (lane >> 5);
+                    const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
+                    *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) =
+                        make_uint2(hp[i][jj][q][0], hp[i][jj][q][1]);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int r = it * 8 + lane / CPW;
+            const int c = lane % CPW;
+            const uint4 v = stage[r * CPW + (c ^ (r & (CPW - 1)))];
+            const int64_t row = m0 + wm * 128 + r;
+            const int64_t col = hcol0 + c * 8;
+            if (row < g.n && col < mh) *reinterpret_cast<uint4 *>(g.Y + row * g.ldy + col) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // the region's reads are done before it is rewritten
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (g.Yt) {
+        constexpr int TS = 136;  // staged h^T row: 128 values + 8 of padding (272 bytes)
+        uint16_t *t = reinterpret_cast<uint16_t *>(stage);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = jj * 32 + q * 8 + 4 * (lane >> 5);  // first of this lane's four columns
+                    t[(c + 0) * TS + r] = (uint16_t)(hp[i][jj][q][0] & 0xffffu);
+                    t[(c + 1) * TS + r] = (uint16_t)(hp[i][jj][q][0] >> 16);
+                    t[(c + 2) * TS + r] = (uint16_t)(hp[i][jj][q][1] & 0xffffu);
+                    t[(c + 3) * TS + r] = (uint16_t)(hp[i][jj][q][1] >> 16);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        const int64_t r0 = m0 + wm * 128;
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int c = it * 4 + lane / 16;  // staged h^T row = h column within the wave's 64
+            const int ch = lane % 16;          // 16-byte chunk of the 128 rows
+            const uint4 v = *reinterpret_cast<const uint4 *>(t + c * TS + ch * 8);
+            const int64_t col = hcol0 + c, row = r0 + ch * 8;
+            if (col < mh && row < g.n) *reinterpret_cast<uint4 *>(g.Yt + col * g.n + row) = v;  // n % 8 == 0
+        }
+        // column sums of squares, one column per lane, rows in order
+        const int nrows = (int)max((int64_t)0, min((int64_t)128, g.n - r0));
+        const uint16_t *tc = t + lane * TS;
+        float sq = 0.f;
+        for (int r8 = 0; r8 < nrows; r8 += 8) {  // nrows % 8 == 0
+            const uint4 v = *reinterpret_cast<const uint4 *>(tc + r8);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xffff0000u);
+                sq = fmaf(lo, lo, sq);
+                sq = fmaf(hi, hi, sq);
             }
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-        const int r = it * 8 + lane / CPW;
-        const int c = lane % CPW;
-        const uint4 v = stage[r * CPW + (c ^ (r & (CPW - 1)))];
-        const int64_t row = m0 + wm * 128 + r;
-        const int64_t col = hcol0 + c * 8;
-        if (row < g.n && col < g.m / 2) *reinterpret_cast<uint4 *>(g.Y + row * g.ldy + col) = v;
+        if (hcol0 + lane < mh) g.npart[(int64_t)(2 * tm + wm) * mh + hcol0 + lane] = sq;
     }
 }
 
@@ -1050,7 +1114,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     __syncthreads();
     uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : w == 2 ? sB0 : sB1;
     if constexpr (EPI == 1)
-        store_tile_swiglu(g, acc, stage, m0, n0 / 2 + wn * 64, wm, lane);
+        store_tile_swiglu(g, acc, stage, m0, n0 / 2 + wn * 64, tm, wm, lane);
     else
         store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
@@ -1784,7 +1848,9 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         dim3 grid((unsigned)tiles, (unsigned)a.splits, 1);
         if (a.epi == 1) {
             // SwiGLU needs whole sums: one K range; the interleaved operand is 2 x (outputs) wide
-            if (a.splits != 1 || a.m % 64 != 0 || a.ldy < a.m / 2) return hipErrorInvalidValue;
+            if (a.splits != 1 || a.m % 64 != 0 || (a.Y && a.ldy < a.m / 2) || (a.Yt && (!a.npart || a.n % 8)) ||
+                (!a.Y && !a.Yt))
+                return hipErrorInvalidValue;
             gemm_tdma_kernel<false, 1><<<grid, 256, 0, stream>>>(a);
         } else if (a.splits > 1) {
             gemm_tdma_kernel<true, 0><<<grid, 256, 0, stream>>>(a);

@@ -239,11 +239,10 @@ rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, in
 
 // ------------------------------------------------------------------ gated MLP block
 struct MlpPlan {
-    int64_t k_in, kpad_in, k_h;
+    int64_t k_in, kpad_in, k_h, kpad_h, chunks_h;
     ColnormPlan cp;
-    GemmConfig gc;
-    rmm_desc_t down;
-    size_t off_part, off_idx, off_xt, off_h, off_down, down_bytes, total;
+    GemmConfig gc, gc_h;
+    size_t off_part, off_idx, off_xt, off_ht, off_hpart, off_idx_h, off_gpart, total;
 };
 
 rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n, int64_t d, int64_t m, double rho_in,
@@ -263,6 +262,16 @@ rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n,
     p.gc.tile = 5;
     p.gc.splits = 1;
     p.cp = colnorm_transpose_plan(n, d);
+    // Down: h^T and the column sums of h^2 per 128-row chunk come from the
+    // SwiGLU epilogue; its selection, then the two-operand GEMM over h^T rows
+    p.kpad_h = (p.k_h + 127) / 128 * 128;
+    p.chunks_h = (n + 255) / 256 * 2;
+    p.gc_h = gemm_choose_transposed(n, d, p.k_h, m);
+    if (p.gc_h.tile != 5) {
+        if (!gemm_tdma_fits(p.kpad_h, 1, m)) return RMM_ERR_UNSUPPORTED;
+        p.gc_h.tile = 5;
+        p.gc_h.splits = 1;
+    }
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -272,10 +281,10 @@ rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n,
     p.off_part = take((size_t)p.cp.chunks * d * 4 + (size_t)d * 4);  // partials, then s
     p.off_idx = take((size_t)p.kpad_in * 4);
     p.off_xt = take((size_t)d * n * 2);
-    p.off_h = take((size_t)n * m * 2);
-    rmm_desc_init(&p.down, RMM_BF16, n, m, d);
-    p.down_bytes = make_plan(&p.down, p.k_h, nullptr, nullptr, nullptr).total;
-    p.off_down = take(p.down_bytes);
+    p.off_ht = take((size_t)m * n * 2);
+    p.off_hpart = take((size_t)p.chunks_h * m * 4 + (size_t)m * 4);  // partials, then s of h
+    p.off_idx_h = take((size_t)p.kpad_h * 4);
+    if (p.gc_h.splits > 1) p.off_gpart = take((size_t)p.gc_h.splits * n * d * 4);
     p.total = off;
     return RMM_OK;
 }
@@ -446,7 +455,9 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
     float *part = reinterpret_cast<float *>(ws + p.off_part);
     int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);
     uint16_t *xt = reinterpret_cast<uint16_t *>(ws + p.off_xt);
-    uint16_t *h = h_out ? static_cast<uint16_t *>(h_out) : reinterpret_cast<uint16_t *>(ws + p.off_h);
+    uint16_t *ht = reinterpret_cast<uint16_t *>(ws + p.off_ht);
+    float *hpart = reinterpret_cast<float *>(ws + p.off_hpart);
+    int32_t *pidx_h = reinterpret_cast<int32_t *>(ws + p.off_idx_h);
     // Up and Gate: one norm pass (also writing x^T), one selection (the same input gives the same set)
     RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_transpose(x, n, d, d, p.cp, xt, n, part, stream));
     if (norm_select_ok(p.cp.chunks, d)) {
@@ -458,7 +469,8 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
         RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(s, nullptr, RMM_F32, 0, 1, d, p.k_in, idx_in_out, p.k_in, pidx,
                                                     p.kpad_in, nullptr, stream));
     }
-    // h = SiLU(x_I Wg_I) * (x_I Wu_I): one GEMM over the interleaved operand, SwiGLU in its epilogue
+    // h = SiLU(x_I Wg_I) * (x_I Wu_I): one GEMM over the interleaved operand, SwiGLU in its epilogue,
+    // which writes h^T and the column sums of h^2 (and h itself when asked for)
     GemmArgs g;
     memset(&g, 0, sizeof(g));
     g.A = xt;
@@ -471,8 +483,10 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
     g.bmode = 0;
     g.idx = pidx;
     g.ld_idx = p.kpad_in;
-    g.Y = h;
+    g.Y = static_cast<uint16_t *>(h_out);
     g.ldy = m;
+    g.Yt = ht;
+    g.npart = hpart;
     g.n = n;
     g.m = 2 * m;
     g.k = p.k_in;
@@ -482,11 +496,43 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
     g.splits = 1;
     g.epi = 1;
     RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
-    // Down: the reduced product over h's own selection
-    int64_t eA, eB, eY;
-    if (check_desc(&p.down, eA, eB, eY) != RMM_OK) return RMM_ERR_INVALID_ARG;
-    return run_matmul(&p.down, h, Wd, p.k_h, nullptr, Y, idx_h_out, ws + p.off_down, p.down_bytes, stream, eA, eB,
-                      eY);
+    // Down: h's column norms from the epilogue's partials, its own selection, rows of h^T and Wd
+    if (norm_select_ok(p.chunks_h, m)) {
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_norm_select(hpart, p.chunks_h, m, 1, p.k_h, idx_h_out, p.k_h, pidx_h, p.kpad_h, stream));
+    } else {
+        float *sh = hpart + p.chunks_h * m;
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(hpart, p.chunks_h, m, 1, sh, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(sh, nullptr, RMM_F32, 0, 1, m, p.k_h, idx_h_out, p.k_h, pidx_h,
+                                                    p.kpad_h, nullptr, stream));
+    }
+    GemmArgs gd;
+    memset(&gd, 0, sizeof(gd));
+    gd.A = ht;
+    gd.lda = n;
+    gd.a_bytes = m * n * 2;
+    gd.B = static_cast<const uint16_t *>(Wd);
+    gd.ldb = d;
+    gd.b_bytes = db;
+    gd.group = 1;
+    gd.bmode = 0;
+    gd.idx = pidx_h;
+    gd.ld_idx = p.kpad_h;
+    gd.Y = static_cast<uint16_t *>(Y);
+    gd.ldy = d;
+    gd.n = n;
+    gd.m = d;
+    gd.k = p.k_h;
+    gd.kpad = p.kpad_h;
+    gd.batch = 1;
+    gd.alpha = 1.f;
+    gd.splits = p.gc_h.splits;
+    gd.part = p.gc_h.splits > 1 ? reinterpret_cast<float *>(ws + p.off_gpart) : nullptr;
+    RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(gd, p.gc_h, stream));
+    if (p.gc_h.splits > 1)
+        RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(gd.part, p.gc_h.splits, n, d, 1, 1.f,
+                                                           static_cast<uint16_t *>(Y), d, 0, stream));
+    return RMM_OK;
 }
 
 }  // extern "C"

@@ -137,6 +137,8 @@ struct GemmArgs {
     int bmode;
     float alpha;
     int epi;             // tile 5 only: 0 = Y, 1 = SwiGLU of interleaved gate/up column blocks (see gemm.hip)
+    uint16_t *Yt;        // epi 1: h^T (m/2 x n, rows n apart), or NULL
+    float *npart;        // epi 1 with Yt: column sums of h^2 per 128-row chunk [chunk][m/2]
 };
 struct GemmConfig {
     int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
