@@ -51,6 +51,9 @@ WORKLOADS = {
                       label="70B up projection decode: a 1x8192 bf16 x B 8192x28672 bf16"),
     "c4": dict(case="c4", rho=0.5, sweep=(0.5, 0.8, 1.0),
                label="QK^T with head-dim selection: Q 32x4096x128, K 8 GQA heads x4096x128 bf16"),
+    "pv": dict(case="pv", rho=0.5, sweep=(0.5, 0.8, 1.0),
+               label="attention value product with token selection: P 32x4096x4096 causal weights, "
+                     "V 8 GQA heads x4096x128 bf16"),
     "mlp": dict(case="mlp", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0), mlp=True,
                 label="Llama-3.1-8B-shaped gated MLP block: x 2048x4096, Up/Gate 4096x14336, Down 14336x4096 bf16, "
                       "one rho for all three projections"),
@@ -114,7 +117,8 @@ class Runner:
         self.group = case.group
         self.alpha = case.alpha
         if self.batched:
-            self.n, self.d, self.m = case.A.shape[1], case.A.shape[2], case.B.shape[1]
+            self.n, self.d = case.A.shape[1], case.A.shape[2]
+            self.m = case.B.shape[1] if case.transB else case.B.shape[2]
             self.batch = case.A.shape[0]
         else:
             self.n, self.d = case.A.shape
@@ -149,10 +153,11 @@ class Runner:
         """Dense bf16 product of the same shape (hipBLASLt through torch)."""
         torch = self.torch
         if self.batched:
-            # K^T per query head, materialised once outside the timed region so
-            # the batched product's right operand is a plain contiguous tensor
+            # the right operand per query head (K^T, or V), materialised once
+            # outside the timed region as a plain contiguous tensor
             if not hasattr(self, "_kt"):
-                self._kt = [b.transpose(1, 2).repeat_interleave(self.group, dim=0).contiguous() for b in self.B]
+                self._kt = [(b.transpose(1, 2) if self.transB else b).repeat_interleave(self.group, dim=0)
+                            .contiguous() for b in self.B]
             torch.baddbmm(self.Y[i], self.A[i], self._kt[i], beta=0.0, alpha=self.alpha, out=self.Y[i])
             return
         if self.transB:
@@ -279,7 +284,8 @@ def cpu_baseline(runner, rho, budget_s=12.0):
     import oracle
     threads = oracle.host_threads()
     A = runner.A_host if not runner.batched else runner.A_host[0]
-    B = runner.B_host if not runner.batched else np.ascontiguousarray(runner.B_host[0].T)
+    B = runner.B_host if not runner.batched else np.ascontiguousarray(
+        runner.B_host[0].T if runner.transB else runner.B_host[0])
     n, d = A.shape
     m = B.shape[1]
     A64 = np.ascontiguousarray(A, dtype=np.float64)
@@ -359,7 +365,7 @@ def main(argv=None):
     if is_mlp:
         runner = MLPRunner(torch, rmm, args.copies)
     else:
-        case = synthetic.make_case(wl["case"])
+        case = synthetic.make_pv_case() if wl["case"] == "pv" else synthetic.make_case(wl["case"])
         runner = Runner(torch, rmm, case, wl.get("decode", False), args.copies)
     rho = wl["rho"]
     graph = not args.no_graph
@@ -400,6 +406,15 @@ def main(argv=None):
         roof = {"bound": "hbm", "kernel": "gemv_partial", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes,
                 "kernel_ms": gemv_ms}
+    elif runner.plan(rho)["gemm"] == "gcol":
+        # narrow product (attention's P V): bound by reading the kept entries of A
+        dom = "gemm"
+        gemm_ms = kt["gemm"][0]
+        algo_bytes = 2 * runner.batch * (runner.n * k + k * runner.m + runner.n * runner.m)
+        achieved = algo_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "gemm_gcol", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes,
+                "kernel_ms": gemm_ms}
     elif stream:
         # single-K-step product (scores Q K^T): bound by writing Y; bytes = Y
         # plus both packed operands read once

@@ -165,8 +165,11 @@ enum {
     RMM_GEMM_ADIRECT = 2, /* 256x256, A in operand blocks straight to registers */
     RMM_GEMM_STREAM = 3,  /* persistent single-K-step kernel (scores Q K^T) */
     RMM_GEMM_BDMA = 4,    /* as ADIRECT, B rows staged by LDS-DMA loads */
-    RMM_GEMM_TDMA = 5     /* 256x256, rows of A^T (written by the norm pass in
+    RMM_GEMM_TDMA = 5,    /* 256x256, rows of A^T (written by the norm pass in
                              place of a pack) and of B staged by LDS-DMA loads */
+    RMM_GEMM_GCOL = 6     /* narrow output (m <= 128, the P V product of
+                             attention): 128-row tiles, A's kept columns
+                             gathered from 64-column windows staged in LDS */
 };
 rmm_status_t rmm_plan_info(const rmm_desc_t *desc, double rho, int32_t *info);
 

@@ -259,7 +259,7 @@ def workspace_size(A, B, rho: float, transB: bool = False, b_group: int = 1, ful
 
 
 ROUTES = ("generic", "mfma", "decode")
-GEMM_KERNELS = ("tile256", "tile128", "adirect", "stream", "bdma", "tdma")
+GEMM_KERNELS = ("tile256", "tile128", "adirect", "stream", "bdma", "tdma", "gcol")
 
 
 def plan_info(A, B, rho: float, transB: bool = False, b_group: int = 1, full_path: bool = False) -> dict:

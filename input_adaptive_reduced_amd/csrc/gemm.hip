@@ -1119,6 +1119,230 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
         store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
+// Reduced product with a narrow output (m <= 128) whose kept A columns are
+// gathered inside the kernel: the token-axis product P[:, T] V[T, :] of an
+// attention head (Sec. 3.2, "Attention"), where A = P is L_q x L_k, B = V is
+// L_k x d_v and T is the kept token set.  With m = d_v = 128 the output is a
+// thin strip, so packing A[:, I] (a k x n write and read) would cost more
+// than the product; instead the kernel reads A once, in coalesced pieces.
+//
+// A workgroup owns 128 rows of one batch entry (and one 128-column block of
+// the output).  The kept list is split by 64-column windows of A; for each
+// window holding at least one kept column, the 128 x 64 block of A (128-byte
+// row pieces) and the window's kept rows of B (compacted, zero rows up to a
+// multiple of 16) are copied into one of three LDS stages by LDS-DMA buffer
+// loads, two windows ahead.  Each wave then multiplies its 32 rows: the A
+// fragments are gathered from the staged block at the kept positions
+// (16-bit LDS reads; slots past the window's count read as zero), the B
+// fragments are read with ds_read_b64_tr_b16, and the four 32x32 column
+// blocks accumulate in fp32 over every kept column in ascending order.
+// Windows without kept columns are never read.
+//
+// Layouts: staged A row r holds its eight 16-byte chunks at c ^ (r & 7);
+// staged B row k at c ^ 2(k & 3) (16 chunks of 8 columns).  Every thread
+// issues exactly eight LDS-DMA loads per window (four of A, four of B, rows
+// past n or past the window's count read as zero), so "window e landed" is
+// vmcnt(8) while window e+1 is in flight.  One barrier per window publishes
+// its stage and certifies that the stage refilled next (read for the
+// previous window) is no longer read.  Workgroups are dealt to XCDs in
+// contiguous runs of row blocks of one batch entry, so the entries sharing
+// one B (grouped-query attention) read its rows from the same L2.
+constexpr int kGcolListRows = (int)kGcolMaxD;  // kept entries a workgroup keeps in LDS
+
+template <int S>
+__device__ __forceinline__ uint4 *gcol_stage(uint4 *a0, uint4 *a1, uint4 *a2) {
+    if constexpr (S % 3 == 0) return a0;
+    else if constexpr (S % 3 == 1) return a1;
+    else return a2;
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
+    constexpr int BM = 128, BN = 128, W = 64;
+    constexpr int PCH = W / 8;      // 16-byte chunks per staged A row
+    constexpr int VCH = BN / 8;     // 16-byte chunks per staged B row
+    constexpr int PBUF = BM * PCH;  // uint4 per A stage (16 KB)
+    constexpr int VBUF = W * VCH;   // uint4 per B stage (16 KB)
+    constexpr int MAXWIN = kGcolListRows / W;
+    __shared__ uint4 sP0[PBUF];
+    __shared__ uint4 sP1[PBUF];
+    __shared__ uint4 sP2[PBUF];
+    __shared__ uint4 sV0[VBUF];
+    __shared__ uint4 sV1[VBUF];
+    __shared__ uint4 sV2[VBUF];
+    __shared__ __align__(16) uint16_t sIdx[kGcolListRows];
+    __shared__ uint16_t sWin[MAXWIN + 4];
+    __shared__ uint16_t sBeg[MAXWIN + 4];
+    __shared__ int sCnt[4];
+    typedef __attribute__((address_space(3))) void lds_t;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tiles_m = (int)((g.n + BM - 1) / BM), tiles_n = (int)((g.m + BN - 1) / BN);
+    const int T = tiles_m * tiles_n * (int)g.batch;
+    int t = blockIdx.x;
+    if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+    const int64_t b = t / (tiles_m * tiles_n);
+    const int rem = t - (int)b * tiles_m * tiles_n;
+    const int tm = rem % tiles_m, tn = rem / tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + b * g.strideA, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g.B + (b / g.group) * g.strideB, g.b_bytes);
+    const int32_t *idx = g.idx + b * g.ld_idx;
+    const int k = (int)g.k;
+    const uint32_t lda2 = (uint32_t)(g.lda * 2), ldb2 = (uint32_t)(g.ldb * 2);
+
+    // the kept list (entries -1 read as 0xffff, above every column), then the
+    // windows holding kept columns: window u's entries are [lb(64u), lb(64u+64))
+    for (int j = tid; j < k; j += 256) sIdx[j] = (uint16_t)idx[j];
+    __syncthreads();
+    auto lower = [&](int v) {
+        int lo = 0, hi = k;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)sIdx[mid] < v) lo = mid + 1; else hi = mid;
+        }
+        return lo;
+    };
+    int nwin = 0;
+    for (int u0 = 0; u0 < MAXWIN; u0 += 256) {
+        const int u = u0 + tid;
+        const int beg = lower(u * W), end = lower(u * W + W);
+        const bool ne = end > beg;
+        const uint64_t bal = __ballot(ne);
+        if (lane == 0) sCnt[w] = __popcll(bal);
+        __syncthreads();
+        int off = nwin;
+        for (int i = 0; i < w; ++i) off += sCnt[i];
+        const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
+        if (ne) {
+            sWin[pos] = (uint16_t)u;
+            sBeg[pos] = (uint16_t)beg;
+        }
+        nwin += sCnt[0] + sCnt[1] + sCnt[2] + sCnt[3];
+        __syncthreads();
+    }
+    // up to two empty windows pad the count to a multiple of three (the
+    // unrolled stage rotation); they load zeros and multiply nothing
+    const int npad = (nwin + 2) / 3 * 3;
+    if (tid == 0) {
+        const uint16_t end = (uint16_t)min(k, lower(MAXWIN * W));
+        for (int e = nwin; e <= npad + 1; ++e) {  // index npad is the refill past the end
+            sBeg[e] = end;
+            sWin[e] = 0;
+        }
+    }
+    __syncthreads();
+
+    // loads of window e into stage S: rows 32w + 8q + lane/8 of A (chunk
+    // lane%8 of the stage row), kept rows 16w + 4q + lane/16 of B; always
+    // eight per thread (a padding window reads zeros)
+    auto issue = [&](int e, uint4 *dP, uint4 *dV) {
+        const bool real = e < nwin;
+        const int u = sWin[e], beg = sBeg[e], cnt = (int)sBeg[e + 1] - beg;  // padding: cnt = 0
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 32 * w + 8 * q + (lane >> 3);
+            const uint32_t c = (uint32_t)((lane & 7) ^ (r & 7));
+            const uint32_t off =
+                real && m0 + r < g.n ? (uint32_t)((m0 + r) * lda2 + (uint32_t)(u * W) * 2u + c * 16u) : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t *)&dP[(32 * w + 8 * q) * PCH], 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kk = 16 * w + 4 * q + (lane >> 4);
+            const uint32_t c = (uint32_t)((lane & 15) ^ ((kk & 3) << 1));
+            const int64_t col = n0 + 8 * c;
+            const uint32_t off = kk < cnt && col < g.m ? (uint32_t)sIdx[beg + kk] * ldb2 + (uint32_t)col * 2u : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t *)&dV[(16 * w + 4 * q) * VCH], 16, off, 0, 0, 0);
+        }
+    };
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+
+    const int ar = 32 * w + (lane & 31);  // this lane's staged A row
+    const int hsel = lane >> 5;
+    auto compute = [&](int e, const uint4 *cP, const uint4 *cV) {
+        const int u = sWin[e], beg = sBeg[e], cnt = (int)sBeg[e + 1] - beg;
+        const char *prow = reinterpret_cast<const char *>(cP) + ar * (PCH * 16);
+        for (int ks = 0; ks * 16 < cnt; ++ks) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                uint32_t v2[2];
+#pragma unroll
+                for (int z = 0; z < 2; ++z) {
+                    const int j = ks * 16 + hsel * 8 + 2 * h + z;
+                    const int p = (int)sIdx[beg + min(j, cnt - 1)] - u * W;
+                    const uint16_t x =
+                        *reinterpret_cast<const uint16_t *>(prow + ((((p >> 3) ^ (ar & 7)) << 4) | ((p & 7) << 1)));
+                    v2[z] = j < cnt ? (uint32_t)x : 0u;
+                }
+                pk[h] = v2[0] | (v2[1] << 16);
+            }
+            const bf16x8_t fa = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            const int gq = lane >> 4, li = lane & 15;
+            const int kbase = ks * 16 + 8 * (gq >> 1) + (li >> 2);
+#pragma unroll
+            for (int jn = 0; jn < 4; ++jn) {
+                const int nn = jn * 32 + 16 * (gq & 1) + 4 * (li & 3);
+                union {
+                    v4i16_t h[2];
+                    bf16x8_t v;
+                } fb;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kr = kbase + 4 * hh;
+                    const char *p = reinterpret_cast<const char *>(&cV[kr * VCH + ((nn >> 3) ^ ((kr & 3) << 1))]) +
+                                    ((nn >> 2) & 1) * 8;
+                    fb.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
+                }
+                // operands swapped: lane l holds output row l % 32
+                acc[jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb.v, fa, acc[jn], 0, 0, 0);
+            }
+        }
+    };
+
+    // window e: its loads landed once only window e+1's eight are younger
+    auto window = [&](int e, auto Sc) {
+        constexpr int S = decltype(Sc)::value;
+        __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(min(e + 2, npad), gcol_stage<S + 2>(sP0, sP1, sP2), gcol_stage<S + 2>(sV0, sV1, sV2));
+        compute(e, gcol_stage<S>(sP0, sP1, sP2), gcol_stage<S>(sV0, sV1, sV2));
+    };
+
+    if (npad > 0) {
+        issue(0, sP0, sV0);
+        issue(1, sP1, sV1);
+        for (int e = 0; e < npad; e += 3) {
+            window(e, std::integral_constant<int, 0>{});
+            window(e + 1, std::integral_constant<int, 1>{});
+            window(e + 2, std::integral_constant<int, 2>{});
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load outlives the workgroup
+
+    // lane l: row 32w + l % 32, columns 32 jn + 8 q + 4 (l / 32) + 0..3
+    const int64_t row = m0 + ar;
+    if (row < g.n) {
+        uint16_t *yrow = g.Y + b * g.strideY + row * g.ldy;
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + jn * 32 + q * 8 + hsel * 4;
+                if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
+                const uint32_t lo = pack_bf16x2(g.alpha * acc[jn][4 * q], g.alpha * acc[jn][4 * q + 1]);
+                const uint32_t hi = pack_bf16x2(g.alpha * acc[jn][4 * q + 2], g.alpha * acc[jn][4 * q + 3]);
+                *reinterpret_cast<uint2 *>(yrow + col) = make_uint2(lo, hi);
+            }
+    }
+}
+
 // Reduced product for one or two 64-entry K steps (kpad = 64 or 128), both
 // operands in MFMA operand blocks (A: rows of A[:, I]; B: rows of B^T[:, I],
 // i.e. the kept columns of the keys for Q K^T).  Such products are bound by
@@ -1857,6 +2081,14 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         } else {
             gemm_tdma_kernel<false, 0><<<grid, 256, 0, stream>>>(a);
         }
+        return hipGetLastError();
+    }
+    if (c.tile == 6) {
+        if (a.bmode != 0 || a.splits != 1 || a.k > kGcolMaxD || a.m % 8 || a.n < 1 || a.batch < 1)
+            return hipErrorInvalidValue;
+        const int64_t T = ((a.n + 127) / 128) * ((a.m + 127) / 128) * a.batch;
+        if (T > INT32_MAX) return hipErrorInvalidValue;
+        gemm_gcol_kernel<<<(unsigned)T, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {

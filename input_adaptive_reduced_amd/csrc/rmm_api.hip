@@ -194,9 +194,13 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     };
     const int64_t batch = ds->batch, d = ds->d, n = ds->n, m = ds->m;
     const bool norms = !given && !p.shortcut && p.route != ROUTE_DECODE;
+    // narrow output (attention's P V: m = d_v): A read in place, its kept
+    // columns gathered inside the GEMM, so no pack of A[:, I]
+    const bool gcol = p.route == ROUTE_MFMA && !ds->transB && m <= kGcolMaxM && n >= 128 && d <= kGcolMaxD &&
+                      d % 8 == 0 && a_extent_bytes(ds) < kMaxBufferBytes;
     // A^T route: one bf16 product of at most kTransAMaxM output columns with
     // B stored d x m, whose norms are computed anyway
-    if (p.route == ROUTE_MFMA && norms && batch == 1 && !ds->transB && m <= kTransAMaxM && n % 8 == 0 &&
+    if (!gcol && p.route == ROUTE_MFMA && norms && batch == 1 && !ds->transB && m <= kTransAMaxM && n % 8 == 0 &&
         d % 8 == 0 && n * d * 2 < kMaxBufferBytes) {
         p.gc = gemm_choose_transposed(n, m, k, d);
         p.transA = p.gc.tile == 5;
@@ -209,7 +213,10 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     // the streaming kernel runs one or two whole 64-entry K steps
     if (p.route == ROUTE_MFMA && gemm_choose(n, m, k, batch, d, ds->transB).tile == 3) p.kpad = k <= 64 ? 64 : 128;
     p.off_idx = take((size_t)p.kpad * batch * 4);  // padded index rows (-1 beyond k)
-    if (p.transA) {
+    if (gcol) {
+        p.gc.tile = 6;
+        p.gc.splits = 1;
+    } else if (p.transA) {
         p.off_At = take((size_t)d * n * 2);
         if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * n * m * 4);
     } else if (p.route == ROUTE_MFMA) {
@@ -667,6 +674,37 @@ rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, in
         if (p.gc.splits > 1)
             RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(g.part, p.gc.splits, n, m, 1, ds.alpha,
                                                                static_cast<uint16_t *>(Y), ds.ldy, 0, stream));
+        return RMM_OK;
+    }
+    if (p.gc.tile == 6) {
+        // A in place: the GEMM gathers the kept columns of 64-column windows itself
+        if (!gemm_idx) {  // rho = 1 shortcut: every column, in order
+            RMM_LAUNCH(RMM_KERNEL_OTHER, launch_iota(pidx, k, p.kpad, batch, stream));
+            gemm_idx = pidx;
+        }
+        g.A = static_cast<const uint16_t *>(A);
+        g.lda = ds.lda;
+        g.strideA = ds.strideA;
+        g.a_bytes = ((n - 1) * ds.lda + d) * 2;  // one entry: the last row ends at column d
+        g.B = static_cast<const uint16_t *>(B);
+        g.ldb = ds.ldb;
+        g.strideB = ds.strideB;
+        g.b_bytes = b_extent_bytes(desc);
+        g.group = ds.b_group;
+        g.bmode = 0;
+        g.idx = gemm_idx;
+        g.ld_idx = p.kpad;
+        g.Y = static_cast<uint16_t *>(Y);
+        g.ldy = ds.ldy;
+        g.strideY = ds.strideY;
+        g.n = n;
+        g.m = m;
+        g.k = k;
+        g.kpad = p.kpad;
+        g.batch = batch;
+        g.alpha = ds.alpha;
+        g.splits = 1;
+        RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
         return RMM_OK;
     }
     if (p.directA) {

@@ -145,9 +145,14 @@ struct GemmConfig {
                  // 3: persistent single-K-step kernel, both operands in operand blocks,
                  // 4: as 2 with B rows staged by LDS-DMA loads (gemm_bdma_kernel),
                  // 5: both operands gathered by rows into LDS (gemm_tdma_kernel;
-                 //    A is then A^T, d x n, lda = its row length)
+                 //    A is then A^T, d x n, lda = its row length),
+                 // 6: narrow output, A read in place with its kept columns gathered in
+                 //    the kernel (gemm_gcol_kernel; m <= kGcolMaxM, d <= kGcolMaxD, d % 8 == 0)
     int splits;  // >= 1
 };
+// Largest output width and contraction length of tile 6.
+constexpr int64_t kGcolMaxM = 128;
+constexpr int64_t kGcolMaxD = 16384;
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);
 // Tile 5 with its K splits for a single product whose A is given transposed,
 // or tile -1 when the shape does not suit it.

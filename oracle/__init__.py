@@ -16,6 +16,11 @@ LLM Inference":
 * ``rmm``        -- the four steps in the paper's order
 * ``attention_scores`` -- per-Q-head selection applied to the matching GQA
   K head, scaled by 1/sqrt(d_h)                             (Sec. 3.3)
+* ``attention_pv`` -- the token-axis product of attention: token scores
+  a_t = ||P_h[:, t]||_2 over the query rows, T = TopK(a, ceil(rho L_k)), and
+  P_h[:, T] V_g[T, :] with g the GQA key/value head of query head h
+  (Sec. 3.2, "Attention", and eq. 2 of App. D.1); no renormalisation of the
+  kept weights (reading: the paragraph writes the product over T alone).
 * ``diagnostics`` -- retained energy (App. B.4 / eq. 16), the Prop. 1 bound
   (eq. 12), the Cor. 1 bound (eq. 14) and the relative bound (eq. 17).
 * ``gated_mlp`` -- the gated MLP block with RMM on its three projections
@@ -188,6 +193,24 @@ def attention_scores(Q: np.ndarray, K: np.ndarray, rho: float, alpha: float,
         Bt = np.ascontiguousarray(np.asarray(K[h // group], dtype=np.float64).T)  # d_h x L_k
         out.append(rmm(Q[h], Bt if with_product else None, rho, alpha, rows, threads))
     return out
+
+
+def attention_pv(P: np.ndarray, V: np.ndarray, rho: float, heads: Optional[Sequence[int]] = None,
+                 rows: Optional[Sequence[int]] = None, threads: Optional[int] = None):
+    """Token-axis RMM of attention's value product, per query head.
+
+    P is (H_q, L_q, L_k) attention weights, V is (H_kv, L_k, d_v).  For head h
+    the token scores are the column norms of P_h over its L_q rows, the kept
+    set T is their TopK of size ceil(rho L_k), and the output is
+    P_h[:, T] V_g[T, :] with g = h // (H_q / H_kv) (Sec. 3.2, "Attention").
+    The same four steps as ``rmm`` with A = P_h and B = V_g.  Returns a list
+    of Result (one per requested head).
+    """
+    hq, hkv = P.shape[0], V.shape[0]
+    if hq % hkv or P.shape[2] != V.shape[1]:
+        raise ValueError("P must be (H_q, L_q, L_k) and V (H_kv, L_k, d_v) with H_kv dividing H_q")
+    group = hq // hkv
+    return [rmm(P[h], V[h // group], rho, 1.0, rows, threads) for h in (range(hq) if heads is None else heads)]
 
 
 def diagnostics(A: np.ndarray, B: np.ndarray, idx: np.ndarray) -> dict:

@@ -44,6 +44,8 @@ __all__ = [
     "gaussian_weights",
     "make_case",
     "make_decode_case",
+    "attention_weights",
+    "make_pv_case",
     "CONFIGS",
     "sha256_of",
 ]
@@ -168,6 +170,7 @@ CONFIGS = {
     "c3": "8B MLP down: A 2048x14336 gated lognormal, B 14336x4096, bf16, rho .5/.7/.8/1",
     "c4": "QK^T GQA: Q 32x4096x128, K 8x4096x128, per-(head,dim) lognormal, bf16, rho .5 (+1)",
     "c5": "70B MLP up: A 4096x8192 lognormal+4 outliers, B 8192x28672, bf16, rho .8 (+1)",
+    "pv": "PV token axis: P 32x4096x4096 causal attention weights, V 8x4096x128, bf16, rho .5/.8 (+1)",
 }
 
 
@@ -243,6 +246,57 @@ def make_mlp_case(scale: Optional[dict] = None, seed: int = 6) -> MLPCase:
     Wu = gaussian_weights(rng, d, m, "bf16")
     Wd = gaussian_weights(rng, m, d, "bf16")
     return MLPCase(x, Wg, Wu, Wd, (0.5, 0.7, 0.8, 1.0))
+
+
+def attention_weights(rng: np.random.Generator, Lq: int, Lk: int, dtype: str, sinks: int = 4) -> np.ndarray:
+    """One head's causal attention weights: an Lq x Lk row-stochastic matrix
+    whose row i spreads over the keys t <= i + (Lk - Lq) (the queries are the
+    last Lq positions) and is zero past them.
+
+    Logits are drawn, not computed from queries and keys: a per-key salience
+    N(0, 1.5^2) with ``sinks`` leading keys raised by 6 (the attention sinks
+    of trained models), a per-head recency decay r log(1 + i' - t) with
+    r = exp(N(0, 0.5^2)) and i' = i + Lk - Lq, and N(0, 1) noise per entry;
+    each row is then exponentiated relative to its maximum over the visible
+    keys and divided by its sum.  Draw order: r, salience, noise (row-major).
+    """
+    if not 0 < Lq <= Lk:
+        raise ValueError("causal weights need 0 < Lq <= Lk (every query sees at least one key)")
+    r = float(np.exp(0.5 * rng.standard_normal()))
+    sal = 1.5 * rng.standard_normal(Lk)
+    sal[:min(sinks, Lk)] += 6.0
+    z = rng.standard_normal((Lq, Lk), dtype=np.float32)  # float32 arithmetic from here on
+    dist = (np.arange(Lq, dtype=np.int64)[:, None] + (Lk - Lq)) - np.arange(Lk)[None, :]
+    decay = np.log1p(np.maximum(dist, 0).astype(np.float32))
+    decay *= np.float32(r)
+    z += sal.astype(np.float32)[None, :]
+    z -= decay
+    z[dist < 0] = -np.inf
+    z -= z.max(axis=1, keepdims=True)
+    np.exp(z, out=z)
+    z /= z.sum(axis=1, keepdims=True)
+    return _store(z, dtype)
+
+
+def make_pv_case(scale: Optional[dict] = None, seed: int = 7) -> Case:
+    """The value product of a Llama-3.1-8B-shaped attention layer at 4096
+    tokens: P (32 query heads, 4096 x 4096 causal attention weights from
+    ``attention_weights``) and V (8 key/value heads, 4096 x 128, N(0, 1)),
+    grouped-query attention with 4 query heads per V head, all bf16.  Draw
+    order: P head by head, then V.  ``scale`` overrides heads, kv_heads, Lq,
+    Lk, dv."""
+    s = dict(scale or {})
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hq, hkv = s.get("heads", 32), s.get("kv_heads", 8)
+    Lk = s.get("Lk", 4096)
+    Lq, dv = s.get("Lq", Lk), s.get("dv", 128)
+    P = np.empty((hq, Lq, Lk), dtype=np.float32)
+    for h in range(hq):
+        P[h] = attention_weights(rng, Lq, Lk, "bf16")
+    V = np.empty((hkv, Lk, dv), dtype=np.float32)
+    for g in range(hkv):
+        V[g] = _store(rng.standard_normal((Lk, dv)), "bf16")
+    return Case("pv", "bf16", P, V, (0.5, 0.8, 1.0), group=hq // hkv)
 
 
 def make_decode_case(case: Case, seed: int = 55) -> Case:

@@ -121,6 +121,14 @@ def test_plan_info_on_host(lib):
     st, (route, gemm, splits) = info(r.BF16, 1, 8192, 28672, 0.8)     # decode: gathered GEMV
     assert st == 0 and route == 2 and gemm == -1 and splits > 1
     assert info(r.BF16, 4096, 128, 4096, 0.5, transB=1, batch=32, group=4) == (0, (1, 3, 1))  # c4 scores
+    # attention's P V (m = d_v): A's kept columns gathered inside the narrow-output kernel
+    assert info(r.BF16, 4096, 4096, 128, 0.5, batch=32, group=4) == (0, (1, 6, 1))
+    assert info(r.BF16, 1024, 2048, 128, 0.5) == (0, (1, 6, 1))        # one head: not the A^T route
+    assert info(r.BF16, 300, 520, 40, 1.0) == (0, (1, 6, 1))           # rho = 1 shortcut reads an identity list
+    assert info(r.BF16, 1024, 2048, 136, 0.5)[1][1] != 6                # wider than one 128-column tile
+    assert info(r.BF16, 64, 2048, 128, 0.5, batch=8)[1][1] != 6         # fewer rows than one tile
+    assert info(r.BF16, 512, 16392, 128, 0.5)[1][1] != 6                # kept list beyond the kernel's LDS copy
+    assert info(r.BF16, 512, 1004, 128, 0.5)[1][1] != 6                 # d % 8 != 0
     assert info(r.F32, 64, 256, 128, 0.5)[1][:2] == (0, -1)             # fp32: generic route
     assert info(r.BF16, 300, 520, 300, 0.5)[1][:2] == (0, -1)           # m % 8 != 0: generic route
     assert info(r.BF16, 64, 256, 128, 0.0)[0] == 1                      # invalid rho
