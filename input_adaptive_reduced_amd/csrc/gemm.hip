@@ -1126,28 +1126,34 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
 // thin strip, so packing A[:, I] (a k x n write and read) would cost more
 // than the product; instead the kernel reads A once, in coalesced pieces.
 //
-// A workgroup owns 128 rows of one batch entry (and one 128-column block of
-// the output).  The kept list is split by 64-column windows of A; for each
-// window holding at least one kept column, the 128 x 64 block of A (128-byte
-// row pieces) and the window's kept rows of B (compacted, zero rows up to a
-// multiple of 16) are copied into one of three LDS stages by LDS-DMA buffer
-// loads, two windows ahead.  Each wave then multiplies its 32 rows: the A
-// fragments are gathered from the staged block at the kept positions
-// (16-bit LDS reads; slots past the window's count read as zero), the B
-// fragments are read with ds_read_b64_tr_b16, and the four 32x32 column
-// blocks accumulate in fp32 over every kept column in ascending order.
-// Windows without kept columns are never read.
+// A workgroup of eight waves owns 256 rows of one batch entry (and one
+// 128-column block of the output).  The kept list is split by 64-column
+// windows of A; for each window holding at least one kept column, the
+// 256 x 64 block of A (128-byte row pieces, 32 KB) and the window's kept
+// rows of B (compacted, zero rows up to 64) are copied into one of three LDS
+// stages by LDS-DMA buffer loads, two windows ahead, so that 64 KB of A per
+// CU is in flight.  Each wave multiplies its 32 rows: the A fragments are
+// gathered from the staged block at the kept positions (one 8-byte LDS read
+// of eight window offsets, then 16-bit reads; slots past the window's count
+// read as zero), the B fragments are read with ds_read_b64_tr_b16, and four
+// 32x32 column blocks accumulate in fp32 over the kept columns in ascending
+// order.  Windows without kept columns are never read.
 //
-// Layouts: staged A row r holds its eight 16-byte chunks at c ^ (r & 7);
-// staged B row k at c ^ 2(k & 3) (16 chunks of 8 columns).  Every thread
-// issues exactly eight LDS-DMA loads per window (four of A, four of B, rows
-// past n or past the window's count read as zero), so "window e landed" is
-// vmcnt(8) while window e+1 is in flight.  One barrier per window publishes
-// its stage and certifies that the stage refilled next (read for the
-// previous window) is no longer read.  Workgroups are dealt to XCDs in
-// contiguous runs of row blocks of one batch entry, so the entries sharing
-// one B (grouped-query attention) read its rows from the same L2.
-constexpr int kGcolListRows = (int)kGcolMaxD;  // kept entries a workgroup keeps in LDS
+// Set-up: the list is copied into LDS (over the third A stage, free until
+// the first refill), each window's first entry is found by binary search,
+// the non-empty windows are compacted in order and every entry's offset
+// within its window is stored as a byte at [window][rank], the form the
+// gather reads.  Layouts: staged A row r holds its eight 16-byte chunks at
+// c ^ (r & 7); staged B row k at c ^ 2(k & 3) (16 chunks of 8 columns).
+// Every thread issues exactly six LDS-DMA loads per window (four of A, two
+// of B; rows past n, past the window's count or of padding windows read as
+// zero), so "window e landed" is vmcnt(6) while window e+1 is in flight.
+// One barrier per window publishes its stage and certifies that the stage
+// refilled next (read for the previous window) is no longer read.
+// Workgroups are dealt to XCDs in contiguous runs of row blocks of one batch
+// entry, so the entries sharing one B (grouped-query attention) read its
+// rows from the same L2.
+constexpr int kGcolWindows = (int)(kGcolMaxD / 64);
 
 template <int S>
 __device__ __forceinline__ uint4 *gcol_stage(uint4 *a0, uint4 *a1, uint4 *a2) {
@@ -1156,24 +1162,29 @@ __device__ __forceinline__ uint4 *gcol_stage(uint4 *a0, uint4 *a1, uint4 *a2) {
     else return a2;
 }
 
-__global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
-    constexpr int BM = 128, BN = 128, W = 64;
+__global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
+    constexpr int NW = 8, NT = NW * 64;
+    constexpr int BM = 32 * NW, BN = 128, W = 64;
     constexpr int PCH = W / 8;      // 16-byte chunks per staged A row
     constexpr int VCH = BN / 8;     // 16-byte chunks per staged B row
-    constexpr int PBUF = BM * PCH;  // uint4 per A stage (16 KB)
+    constexpr int PBUF = BM * PCH;  // uint4 per A stage (32 KB)
     constexpr int VBUF = W * VCH;   // uint4 per B stage (16 KB)
-    constexpr int MAXWIN = kGcolListRows / W;
+    constexpr int MAXWIN = kGcolWindows;
+    static_assert(kGcolMaxD * 2 <= PBUF * 16, "the list must fit in one A stage");
+    static_assert(MAXWIN < NT, "one thread per window");
     __shared__ uint4 sP0[PBUF];
     __shared__ uint4 sP1[PBUF];
     __shared__ uint4 sP2[PBUF];
     __shared__ uint4 sV0[VBUF];
     __shared__ uint4 sV1[VBUF];
     __shared__ uint4 sV2[VBUF];
-    __shared__ __align__(16) uint16_t sIdx[kGcolListRows];
-    __shared__ uint16_t sWin[MAXWIN + 4];
-    __shared__ uint16_t sBeg[MAXWIN + 4];
-    __shared__ int sCnt[4];
+    __shared__ __align__(16) uint8_t sPos[MAXWIN * W];  // offsets of window u's kept columns, by rank
+    __shared__ uint16_t sStart[MAXWIN + 1];              // first list entry at or past column 64u
+    __shared__ uint16_t sWin[MAXWIN + 4];                // windows holding kept columns (+ padding)
+    __shared__ uint16_t sBeg[MAXWIN + 4];                // their first list entries (+ the end)
+    __shared__ int sCnt[NW];
     typedef __attribute__((address_space(3))) void lds_t;
+    uint16_t *sIdx = reinterpret_cast<uint16_t *>(sP2);  // the list, during set-up only
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int tiles_m = (int)((g.n + BM - 1) / BM), tiles_n = (int)((g.m + BN - 1) / BN);
@@ -1190,51 +1201,48 @@ __global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
     const int k = (int)g.k;
     const uint32_t lda2 = (uint32_t)(g.lda * 2), ldb2 = (uint32_t)(g.ldb * 2);
 
-    // the kept list (entries -1 read as 0xffff, above every column), then the
-    // windows holding kept columns: window u's entries are [lb(64u), lb(64u+64))
-    for (int j = tid; j < k; j += 256) sIdx[j] = (uint16_t)idx[j];
+    // set-up (entries -1 read as 0xffff, above every column)
+    for (int j = tid; j < k; j += NT) sIdx[j] = (uint16_t)idx[j];
     __syncthreads();
-    auto lower = [&](int v) {
+    if (tid <= MAXWIN) {
         int lo = 0, hi = k;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if ((int)sIdx[mid] < v) lo = mid + 1; else hi = mid;
+            if ((int)sIdx[mid] < tid * W) lo = mid + 1; else hi = mid;
         }
-        return lo;
-    };
-    int nwin = 0;
-    for (int u0 = 0; u0 < MAXWIN; u0 += 256) {
-        const int u = u0 + tid;
-        const int beg = lower(u * W), end = lower(u * W + W);
-        const bool ne = end > beg;
-        const uint64_t bal = __ballot(ne);
-        if (lane == 0) sCnt[w] = __popcll(bal);
-        __syncthreads();
-        int off = nwin;
-        for (int i = 0; i < w; ++i) off += sCnt[i];
+        sStart[tid] = (uint16_t)lo;
+    }
+    __syncthreads();
+    const bool ne = tid < MAXWIN && sStart[tid + 1] > sStart[tid];
+    const uint64_t bal = __ballot(ne);
+    if (lane == 0) sCnt[w] = __popcll(bal);
+    for (int j = tid; j < k; j += NT) {
+        const int v = sIdx[j];
+        if (v < MAXWIN * W) sPos[(v >> 6) * W + j - sStart[v >> 6]] = (uint8_t)(v & (W - 1));
+    }
+    __syncthreads();
+    int off = 0, nwin = 0;
+    for (int i = 0; i < NW; ++i) {
+        off += i < w ? sCnt[i] : 0;
+        nwin += sCnt[i];
+    }
+    if (ne) {
         const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
-        if (ne) {
-            sWin[pos] = (uint16_t)u;
-            sBeg[pos] = (uint16_t)beg;
-        }
-        nwin += sCnt[0] + sCnt[1] + sCnt[2] + sCnt[3];
-        __syncthreads();
+        sWin[pos] = (uint16_t)tid;
+        sBeg[pos] = sStart[tid];
     }
     // up to two empty windows pad the count to a multiple of three (the
-    // unrolled stage rotation); they load zeros and multiply nothing
+    // unrolled stage rotation); they load zeros and multiply nothing, and
+    // index npad stands for the refills past the end
     const int npad = (nwin + 2) / 3 * 3;
-    if (tid == 0) {
-        const uint16_t end = (uint16_t)min(k, lower(MAXWIN * W));
-        for (int e = nwin; e <= npad + 1; ++e) {  // index npad is the refill past the end
-            sBeg[e] = end;
-            sWin[e] = 0;
-        }
+    if (tid >= nwin && tid <= npad + 1) {
+        sWin[tid] = 0;
+        sBeg[tid] = sStart[MAXWIN];
     }
     __syncthreads();
 
-    // loads of window e into stage S: rows 32w + 8q + lane/8 of A (chunk
-    // lane%8 of the stage row), kept rows 16w + 4q + lane/16 of B; always
-    // eight per thread (a padding window reads zeros)
+    // loads of window e: rows 32w + 8q + lane/8 of A (chunk lane%8 of the
+    // stage row), kept rows 8w + 4q + lane/16 of B
     auto issue = [&](int e, uint4 *dP, uint4 *dV) {
         const bool real = e < nwin;
         const int u = sWin[e], beg = sBeg[e], cnt = (int)sBeg[e + 1] - beg;  // padding: cnt = 0
@@ -1242,17 +1250,18 @@ __global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
         for (int q = 0; q < 4; ++q) {
             const int r = 32 * w + 8 * q + (lane >> 3);
             const uint32_t c = (uint32_t)((lane & 7) ^ (r & 7));
-            const uint32_t off =
+            const uint32_t o =
                 real && m0 + r < g.n ? (uint32_t)((m0 + r) * lda2 + (uint32_t)(u * W) * 2u + c * 16u) : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t *)&dP[(32 * w + 8 * q) * PCH], 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_t *)&dP[(32 * w + 8 * q) * PCH], 16, o, 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int kk = 16 * w + 4 * q + (lane >> 4);
+        for (int q = 0; q < 2; ++q) {
+            const int kk = 8 * w + 4 * q + (lane >> 4);
             const uint32_t c = (uint32_t)((lane & 15) ^ ((kk & 3) << 1));
             const int64_t col = n0 + 8 * c;
-            const uint32_t off = kk < cnt && col < g.m ? (uint32_t)sIdx[beg + kk] * ldb2 + (uint32_t)col * 2u : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t *)&dV[(16 * w + 4 * q) * VCH], 16, off, 0, 0, 0);
+            const uint32_t row = (uint32_t)(u * W + sPos[u * W + (kk & (W - 1))]);
+            const uint32_t o = kk < cnt && col < g.m ? row * ldb2 + (uint32_t)col * 2u : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t *)&dV[(8 * w + 4 * q) * VCH], 16, o, 0, 0, 0);
         }
     };
 
@@ -1265,17 +1274,19 @@ __global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
     const int ar = 32 * w + (lane & 31);  // this lane's staged A row
     const int hsel = lane >> 5;
     auto compute = [&](int e, const uint4 *cP, const uint4 *cV) {
-        const int u = sWin[e], beg = sBeg[e], cnt = (int)sBeg[e + 1] - beg;
+        const int u = sWin[e], cnt = (int)sBeg[e + 1] - (int)sBeg[e];
         const char *prow = reinterpret_cast<const char *>(cP) + ar * (PCH * 16);
         for (int ks = 0; ks * 16 < cnt; ++ks) {
+            const uint2 pp = *reinterpret_cast<const uint2 *>(sPos + u * W + ks * 16 + hsel * 8);
             uint32_t pk[4];
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
+                const uint32_t word = h < 2 ? pp.x : pp.y;
                 uint32_t v2[2];
 #pragma unroll
                 for (int z = 0; z < 2; ++z) {
                     const int j = ks * 16 + hsel * 8 + 2 * h + z;
-                    const int p = (int)sIdx[beg + min(j, cnt - 1)] - u * W;
+                    const int p = (int)(word >> (8 * (2 * (h & 1) + z))) & (W - 1);
                     const uint16_t x =
                         *reinterpret_cast<const uint16_t *>(prow + ((((p >> 3) ^ (ar & 7)) << 4) | ((p & 7) << 1)));
                     v2[z] = j < cnt ? (uint32_t)x : 0u;
@@ -1295,9 +1306,9 @@ __global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int kr = kbase + 4 * hh;
-                    const char *p = reinterpret_cast<const char *>(&cV[kr * VCH + ((nn >> 3) ^ ((kr & 3) << 1))]) +
-                                    ((nn >> 2) & 1) * 8;
-                    fb.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
+                    const char *pb = reinterpret_cast<const char *>(&cV[kr * VCH + ((nn >> 3) ^ ((kr & 3) << 1))]) +
+                                     ((nn >> 2) & 1) * 8;
+                    fb.h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)pb);
                 }
                 // operands swapped: lane l holds output row l % 32
                 acc[jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb.v, fa, acc[jn], 0, 0, 0);
@@ -1305,10 +1316,10 @@ __global__ __launch_bounds__(256, 1) void gemm_gcol_kernel(GemmArgs g) {
         }
     };
 
-    // window e: its loads landed once only window e+1's eight are younger
+    // window e: its loads landed once only window e+1's six are younger
     auto window = [&](int e, auto Sc) {
         constexpr int S = decltype(Sc)::value;
-        __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+        __builtin_amdgcn_s_waitcnt(0x0f76);  // vmcnt(6)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         issue(min(e + 2, npad), gcol_stage<S + 2>(sP0, sP1, sP2), gcol_stage<S + 2>(sV0, sV1, sV2));
@@ -2086,9 +2097,9 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
     if (c.tile == 6) {
         if (a.bmode != 0 || a.splits != 1 || a.k > kGcolMaxD || a.m % 8 || a.n < 1 || a.batch < 1)
             return hipErrorInvalidValue;
-        const int64_t T = ((a.n + 127) / 128) * ((a.m + 127) / 128) * a.batch;
+        const int64_t T = ((a.n + 255) / 256) * ((a.m + 127) / 128) * a.batch;
         if (T > INT32_MAX) return hipErrorInvalidValue;
-        gemm_gcol_kernel<<<(unsigned)T, 256, 0, stream>>>(a);
+        gemm_gcol_kernel<<<(unsigned)T, 512, 0, stream>>>(a);
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {

@@ -152,7 +152,7 @@ struct GemmConfig {
 };
 // Largest output width and contraction length of tile 6.
 constexpr int64_t kGcolMaxM = 128;
-constexpr int64_t kGcolMaxD = 16384;
+constexpr int64_t kGcolMaxD = 8192;
 GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d, int transB);
 // Tile 5 with its K splits for a single product whose A is given transposed,
 // or tile -1 when the shape does not suit it.
