@@ -605,12 +605,14 @@ __device__ void block_select(SelectShared<BS> &sh, const uint32_t (&key)[E], int
             kmin = min(kmin, key[e]);
             kor |= key[e];
         }
+    // the cross-lane reductions run with every lane active; only the stores are lane 0's
     kmax = wave_max_u32(kmax);
     kmin = ~wave_max_u32(~kmin);
+    kor = (uint32_t)__builtin_amdgcn_readlane((int)wave_or_u32(kor), 63);
     if (lane == 0) {
         sh.wmax[0][w] = kmax;
         sh.wmax[1][w] = ~kmin;
-        sh.wlow[w] = __builtin_amdgcn_readlane((int)wave_or_u32(kor), 63);
+        sh.wlow[w] = kor;
     }
     for (int q = tid; q < 2048; q += BS) sh.hist[0][q] = 0;
     __syncthreads();

@@ -63,6 +63,9 @@ def _sel_case(rng, d, kind):
     if kind == "ties":
         v = np.abs(rng.standard_normal(max(1, d // 10))).astype(np.float32)
         return v[rng.integers(0, v.size, size=d)]
+    if kind == "bf16":  # bf16-valued scores: the low 16 key bits are zero in every key
+        s = (np.abs(rng.standard_normal(d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+        return (s.view(np.uint32) & np.uint32(0xffff0000)).view(np.float32)
     if kind == "const":
         return np.full(d, 3.25, dtype=np.float32)
     if kind == "zeros_and_inf":
@@ -73,8 +76,8 @@ def _sel_case(rng, d, kind):
     raise KeyError(kind)
 
 
-@pytest.mark.parametrize("d", [1, 2, 7, 128, 1000, 2049, 4096, 14336, 30000])
-@pytest.mark.parametrize("kind", ["random", "ties", "const", "zeros_and_inf"])
+@pytest.mark.parametrize("d", [1, 2, 7, 128, 1000, 1024, 2049, 2432, 3008, 4032, 4096, 14336, 30000])
+@pytest.mark.parametrize("kind", ["random", "ties", "bf16", "const", "zeros_and_inf"])
 def test_select_exact(rmm, torch, d, kind):
     rng = np.random.default_rng(d + len(kind))
     s = _sel_case(rng, d, kind)
