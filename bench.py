@@ -54,6 +54,12 @@ WORKLOADS = {
     "pv": dict(case="pv", rho=0.5, sweep=(0.5, 0.8, 1.0),
                label="attention value product with token selection: P 32x4096x4096 causal weights, "
                      "V 8 GQA heads x4096x128 bf16"),
+    "c5-decode-fp8": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), wq="fp8",
+                          label="70B up projection decode over FP8 E4M3 weights with per-column scales: "
+                                "a 1x8192 bf16 x B 8192x28672 fp8"),
+    "c5-decode-int8": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), wq="int8",
+                           label="70B up projection decode over int8 weights with per-column scales: "
+                                 "a 1x8192 bf16 x B 8192x28672 int8"),
     "mlp": dict(case="mlp", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0), mlp=True,
                 label="Llama-3.1-8B-shaped gated MLP block: x 2048x4096, Up/Gate 4096x14336, Down 14336x4096 bf16, "
                       "one rho for all three projections"),
@@ -164,6 +170,61 @@ class Runner:
             torch.matmul(self.A[i], self.B[i].t(), out=self.Y[i])
         else:
             torch.matmul(self.A[i], self.B[i], out=self.Y[i])
+
+
+class WQRunner:
+    """Single-row decode over 8-bit weights (rmm_decode_wq); the dense
+    comparison is the bf16 GEMV over the unquantized weights."""
+
+    def __init__(self, torch, rmm, fmt, copies):
+        import numpy as np
+        import synthetic
+        self.torch, self.rmm, self.fmt = torch, rmm, fmt
+        dev = torch.device("cuda:0")
+        base = synthetic.make_case("c5", dict(n=1))
+        dec = synthetic.make_decode_case(base)
+        codes, scale = synthetic.quantize_columns(base.B, fmt)
+        self.a_host, self.codes_host, self.scale_host = dec.A, codes, scale
+
+        def up(x):
+            bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
+            return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+        a0, q0, s0 = up(dec.A.reshape(-1)), torch.from_numpy(codes).to(dev), torch.from_numpy(scale).to(dev)
+        self.d, self.m = codes.shape
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2 * MALL_BYTES / q0.numel())))
+        self.copies = copies
+        self.a = [a0] + [a0.clone() for _ in range(copies - 1)]
+        self.Bq = [q0] + [q0.clone() for _ in range(copies - 1)]
+        self.scale = [s0] + [s0.clone() for _ in range(copies - 1)]
+        self.B16 = up(base.B)
+        self.n, self.batch = 1, 1
+        self.Y = [torch.empty(self.m, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+        self.Yd = torch.empty((1, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws, self.idx = {}, {}
+
+    def flops(self, rho):
+        return 2.0 * self.rmm.k_of(rho, self.d) * self.m
+
+    def call(self, i, rho, full_path=False):
+        import ctypes
+        torch, rmm = self.torch, self.rmm
+        if rho not in self.ws:
+            need = rmm.load().rmm_decode_wq_workspace_size(self.d, self.m, rho)
+            if need == ctypes.c_size_t(-1).value:
+                raise rmm.RMMError(2, "rmm_decode_wq_workspace_size")
+            self.ws[rho] = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            self.idx[rho] = torch.empty(rmm.k_of(rho, self.d), dtype=torch.int32, device="cuda:0")
+        rmm.decode_wq(self.a[i], self.Bq[i], self.scale[i], rho, self.fmt, out=self.Y[i], idx_out=self.idx[rho],
+                      workspace=self.ws[rho])
+
+    def plan(self, rho):
+        return {"route": "decode", "gemm": None, "splits": None}
+
+    def dense(self, i):
+        # one weight copy: the dense GEMV streams all 470 MB of it, twice the MALL
+        self.torch.matmul(self.a[i].view(1, -1), self.B16, out=self.Yd)
 
 
 class MLPRunner:
@@ -318,6 +379,20 @@ def cpu_baseline(runner, rho, budget_s=12.0):
             "seconds_measured": t_sel + t_rows + t_probe}
 
 
+def cpu_baseline_wq(runner, rho):
+    """The oracle's whole 8-bit-weight decode (decode, select, product) on this host."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.decode_wq(runner.a_host, runner.codes_host, runner.fmt, runner.scale_host, rho)
+    t = time.perf_counter() - t0
+    k = oracle.k_of(rho, runner.d)
+    return {"value": 2.0 * k * runner.m / t / 1e12, "unit": "TFLOP/s", "cores": oracle.host_threads(),
+            "kind": "oracle",
+            "sample": f"the whole fp64 oracle decode: {runner.fmt} codes decoded and scaled ({runner.d}x{runner.m}), "
+                      f"|a| TopK, the reduced row product ({t:.2f} s)",
+            "seconds_measured": t}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,8 +437,11 @@ def main(argv=None):
 
     wl = WORKLOADS[args.workload]
     is_mlp = wl.get("mlp", False)
+    is_wq = "wq" in wl
     if is_mlp:
         runner = MLPRunner(torch, rmm, args.copies)
+    elif is_wq:
+        runner = WQRunner(torch, rmm, wl["wq"], args.copies)
     else:
         case = synthetic.make_pv_case() if wl["case"] == "pv" else synthetic.make_case(wl["case"])
         runner = Runner(torch, rmm, case, wl.get("decode", False), args.copies)
@@ -382,7 +460,7 @@ def main(argv=None):
         dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
         log(f"dense torch.matmul: {dense_ms * 1e3:.1f} us/step")
         for r in wl["sweep"]:
-            for full in ((False, True) if r == 1.0 and not is_mlp else (False,)):
+            for full in ((False, True) if r == 1.0 and not is_mlp and not is_wq else (False,)):
                 t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
                                runner.copies, graph)
                 ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
@@ -402,7 +480,10 @@ def main(argv=None):
     if runner.n == 1:
         dom, bound = "gemv", "hbm"
         gemv_ms = kt["gemv"][0]
-        algo_bytes = k * runner.m * 2 + runner.d * 2 + runner.m * 4  # kept B rows + a + fp32 partial row
+        if is_wq:  # kept 8-bit rows + a + column scales + fp32 partial row
+            algo_bytes = k * runner.m + runner.d * 2 + runner.m * 8
+        else:      # kept B rows + a + fp32 partial row
+            algo_bytes = k * runner.m * 2 + runner.d * 2 + runner.m * 4
         achieved = algo_bytes / (gemv_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "gemv_partial", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes,
@@ -438,7 +519,10 @@ def main(argv=None):
     roof["per_kernel_ms"] = {kk: v[0] for kk, v in kt.items() if v[1]}
 
     cpu = None
-    if rank == 0 and not args.no_cpu_baseline and not is_mlp:  # the fp64 block needs every row of h: no bounded sample
+    if rank == 0 and not args.no_cpu_baseline and is_wq:
+        cpu = cpu_baseline_wq(runner, rho)
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+    elif rank == 0 and not args.no_cpu_baseline and not is_mlp:  # the fp64 block needs every row of h: no bounded sample
         cpu = cpu_baseline(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 

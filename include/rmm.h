@@ -261,6 +261,35 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
                            int32_t *idx_h_out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Single-row decode over 8-bit weights (weight-only quantization, W8A16):
+ * the gathered GEMV of the decode route with B stored as 8-bit codes and one
+ * fp32 scale per output column, the combination of RMM with low-precision
+ * weights that App. B.6 ("Compatibility with INT8 Weight Quantization",
+ * Table 14) evaluates and App. B.7 leaves to fused quantized kernels.
+ *
+ *   I = TopK(|a_j|, k = rmm_k(rho, d))  (Sec. 3.2 with n = 1: s_j = |a_j|)
+ *   y[c] = alpha * scale[c] * sum_{t<k} a[I_t] * q[I_t, c]
+ *
+ * a: 1 x d bf16 (16-byte aligned), d <= 16384.  Bq: d x m codes, rows ldb
+ * bytes apart (m, ldb multiples of 16; 16-byte aligned): fmt
+ * RMM_WQ_FP8_E4M3 = OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 = NaN),
+ * RMM_WQ_INT8 = two's-complement int8.  scale: m fp32, the dequantized
+ * weight being q * scale[c].  y: 1 x m bf16 (16-byte aligned), rounded to
+ * nearest-even from the fp32 sum; the kept rows are summed in fp32 in a
+ * fixed order (bit-reproducible).  idx_out (k int32, ascending) may be NULL.
+ * The caller owns every buffer; workspace: rmm_decode_wq_workspace_size
+ * bytes, 256-byte aligned (SIZE_MAX there means unsupported sizes).
+ * Returns RMM_ERR_INVALID_ARG for null pointers, an unknown fmt, bad sizes
+ * or overlapping buffers, RMM_ERR_UNSUPPORTED for sizes or alignments
+ * outside the above, RMM_ERR_WORKSPACE for a short workspace.
+ */
+enum { RMM_WQ_FP8_E4M3 = 0, RMM_WQ_INT8 = 1 };
+size_t rmm_decode_wq_workspace_size(int64_t d, int64_t m, double rho);
+rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const float *scale, int64_t d, int64_t m,
+                           int64_t ldb, double rho, float alpha, void *y, int32_t *idx_out, void *workspace,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * Optional per-kernel timing for measurement tools.  While enabled, every
  * kernel rmm_matmul enqueues is bracketed by a pair of HIP events recorded
  * on the call's stream (at most `capacity` pairs are kept; later kernels are

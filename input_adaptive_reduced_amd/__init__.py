@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
-    "matmul_indexed", "plan_info", "gated_weights", "gated_mlp",
+    "matmul_indexed", "plan_info", "gated_weights", "gated_mlp", "decode_wq", "WQ_FORMATS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -119,6 +119,10 @@ def load():
     L.rmm_gated_mlp.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp, vp, sz,
                                 vp]
     L.rmm_gated_mlp.restype = ctypes.c_int
+    L.rmm_decode_wq_workspace_size.argtypes = [i64, i64, ctypes.c_double]
+    L.rmm_decode_wq_workspace_size.restype = sz
+    L.rmm_decode_wq.argtypes = [vp, vp, i32, vp, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.rmm_decode_wq.restype = ctypes.c_int
     L.rmm_plan_info.argtypes = [ctypes.POINTER(Desc), ctypes.c_double, ctypes.POINTER(i32)]
     L.rmm_plan_info.restype = ctypes.c_int
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
@@ -376,6 +380,48 @@ def gated_weights(Wg, Wu, transposed: bool = False):
     _check(load().rmm_gated_weights(Wg.data_ptr(), Wu.data_ptr(), d, m, 1 if transposed else 0, out.data_ptr(),
                                     _stream(Wg)), "rmm_gated_weights")
     return out
+
+
+WQ_FORMATS = {"fp8": 0, "int8": 1}
+
+
+def decode_wq(a, Bq, scale, rho: float, fmt: str = "fp8", *, alpha: float = 1.0, out=None, idx_out=None,
+              workspace=None):
+    """Single-row decode over 8-bit weights (rmm_decode_wq).
+
+    a: bf16 (d,) or (1, d); Bq: (d, m) 8-bit codes (uint8, int8 or
+    float8_e4m3fn storage; ``fmt`` "fp8" = OCP E4M3, "int8"); scale: fp32
+    (m,).  Returns (y, idx): y bf16 of a's shape with m columns, idx int32 (k,)
+    ascending."""
+    torch = _torch()
+    _require_gpu(a, Bq, scale)
+    L = load()
+    if fmt not in WQ_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(WQ_FORMATS)}")
+    d = a.shape[-1]
+    if a.dtype != torch.bfloat16 or a.numel() != d or Bq.element_size() != 1 or Bq.dim() != 2 or Bq.shape[0] != d:
+        raise ValueError("expected bf16 a with d entries and 8-bit Bq (d, m)")
+    m = Bq.shape[1]
+    if scale.dtype != torch.float32 or scale.numel() != m or not scale.is_contiguous():
+        raise ValueError("scale must be m contiguous fp32 values")
+    if not a.is_contiguous() or Bq.stride(1) != 1:
+        raise ValueError("a must be contiguous and Bq row-major")
+    need = L.rmm_decode_wq_workspace_size(d, m, float(rho))
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(2, "rmm_decode_wq_workspace_size")
+    k = int(L.rmm_k(float(rho), d))
+    if out is None:
+        out = torch.empty(a.shape[:-1] + (m,), dtype=torch.bfloat16, device=a.device)
+    if idx_out is None:
+        idx_out = torch.empty(k, dtype=torch.int32, device=a.device)
+    if workspace is None:
+        ws, wsb = _workspace(need, a.device)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.rmm_decode_wq(a.data_ptr(), Bq.data_ptr(), WQ_FORMATS[fmt], scale.data_ptr(), d, m, Bq.stride(0),
+                         float(rho), float(alpha), out.data_ptr(), idx_out.data_ptr(), ws.data_ptr(), wsb, _stream(a))
+    _check(st, "rmm_decode_wq")
+    return out, idx_out
 
 
 def gated_mlp(x, Wgu, Wd, rho_in: float, rho_h: float, *, out=None, return_h: bool = False, workspace=None):

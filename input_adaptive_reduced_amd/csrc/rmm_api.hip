@@ -542,6 +542,48 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
     return RMM_OK;
 }
 
+size_t rmm_decode_wq_workspace_size(int64_t d, int64_t m, double rho) {
+    const int64_t k = k_of(rho, d);
+    if (k < 1 || d > kFusedSelectMaxD || m < 16 || m % 16) return SIZE_MAX;
+    const int64_t kpad = (k + 127) / 128 * 128;
+    const int splits = gemv_wq_splits(m, k);
+    return align_up((size_t)kpad * 4) + align_up((size_t)k * 4) + align_up((size_t)splits * m * 4);
+}
+
+rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const float *scale, int64_t d, int64_t m,
+                           int64_t ldb, double rho, float alpha, void *y, int32_t *idx_out, void *workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+    if (!a || !Bq || !scale || !y || (fmt != RMM_WQ_FP8_E4M3 && fmt != RMM_WQ_INT8)) return RMM_ERR_INVALID_ARG;
+    const int64_t k = k_of(rho, d);
+    if (k < 1 || d < 1 || m < 1 || ldb < m) return RMM_ERR_INVALID_ARG;
+    if (d > kFusedSelectMaxD || m % 16 || ldb % 16 || !aligned16(a) || !aligned16(Bq) || !aligned16(y) ||
+        ((uintptr_t)scale & 3))
+        return RMM_ERR_UNSUPPORTED;
+    const size_t need = rmm_decode_wq_workspace_size(d, m, rho);
+    if (!workspace || ws_bytes < need) return RMM_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return RMM_ERR_INVALID_ARG;
+    const int64_t ab = d * 2, bb = (d - 1) * ldb + m, sb = m * 4, yb = m * 2;
+    char *ws = static_cast<char *>(workspace);
+    if (overlaps(y, yb, a, ab) || overlaps(y, yb, Bq, bb) || overlaps(y, yb, scale, sb) ||
+        overlaps(ws, (int64_t)need, a, ab) || overlaps(ws, (int64_t)need, Bq, bb) ||
+        overlaps(ws, (int64_t)need, scale, sb) || overlaps(ws, (int64_t)need, y, yb) ||
+        (idx_out && (overlaps(idx_out, k * 4, y, yb) || overlaps(idx_out, k * 4, ws, (int64_t)need) ||
+                     overlaps(idx_out, k * 4, a, ab) || overlaps(idx_out, k * 4, Bq, bb))))
+        return RMM_ERR_INVALID_ARG;
+    const int64_t kpad = (k + 127) / 128 * 128;
+    const int splits = gemv_wq_splits(m, k);
+    int32_t *pidx = reinterpret_cast<int32_t *>(ws);
+    float *aval = reinterpret_cast<float *>(ws + align_up((size_t)kpad * 4));
+    float *gpart = reinterpret_cast<float *>(ws + align_up((size_t)kpad * 4) + align_up((size_t)k * 4));
+    // the kept rows I = TopK(|a_j|) with their values, the 8-bit GEMV, the split sum
+    RMM_LAUNCH(RMM_KERNEL_SELECT, launch_select(nullptr, a, RMM_BF16, 0, 1, d, k, idx_out, k, pidx, kpad, aval, stream));
+    RMM_LAUNCH(RMM_KERNEL_GEMV, launch_gemv_wq_partial(static_cast<const uint8_t *>(Bq), fmt, ldb, m, scale, pidx,
+                                                       aval, k, splits, gpart, stream));
+    RMM_LAUNCH(RMM_KERNEL_REDUCE,
+               launch_splitk_reduce(gpart, splits, 1, m, 1, alpha, static_cast<uint16_t *>(y), m, 0, stream));
+    return RMM_OK;
+}
+
 }  // extern "C"
 
 namespace rmm {

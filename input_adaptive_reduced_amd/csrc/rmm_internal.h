@@ -190,6 +190,14 @@ hipError_t launch_gemm_generic(const GenericArgs &g, hipStream_t stream);
 
 // Decode: y = alpha * sum_t aval[t] * B[idx[t], :] (split over t, then reduce).
 int gemv_splits(int64_t m, int64_t k);
+// Gathered GEMV over 8-bit weights (fmt 0: OCP FP8 E4M3, 1: int8) with one
+// fp32 scale per column: part[split][c] = scale[c] * sum over the split's
+// kept rows of aval[t] * q[idx[t], c].  m and ldb multiples of 16, B 16-byte
+// aligned.
+int gemv_wq_splits(int64_t m, int64_t k);
+hipError_t launch_gemv_wq_partial(const uint8_t *B, int fmt, int64_t ldb, int64_t m, const float *scale,
+                                  const int32_t *idx, const float *aval, int64_t k, int splits, float *part,
+                                  hipStream_t stream);
 hipError_t launch_gemv_partial(const uint16_t *B, int64_t ldb, int64_t m, const int32_t *idx, const float *aval,
                                int64_t k, int splits, float *part, hipStream_t stream);
 

@@ -21,6 +21,10 @@ LLM Inference":
   P_h[:, T] V_g[T, :] with g the GQA key/value head of query head h
   (Sec. 3.2, "Attention", and eq. 2 of App. D.1); no renormalisation of the
   kept weights (reading: the paragraph writes the product over T alone).
+* ``fp8_e4m3_value``, ``int8_value``, ``decode_wq`` -- single-row decode over
+  8-bit weights with per-column scales (W8A16; App. B.6 combines RMM with
+  INT8 weight quantization): I = TopK(|a_j|, k), y = scale * a[I] q[I, :],
+  with the codes decoded from the OCP FP8 E4M3 definition or as int8.
 * ``diagnostics`` -- retained energy (App. B.4 / eq. 16), the Prop. 1 bound
   (eq. 12), the Cor. 1 bound (eq. 14) and the relative bound (eq. 17).
 * ``gated_mlp`` -- the gated MLP block with RMM on its three projections
@@ -211,6 +215,37 @@ def attention_pv(P: np.ndarray, V: np.ndarray, rho: float, heads: Optional[Seque
         raise ValueError("P must be (H_q, L_q, L_k) and V (H_kv, L_k, d_v) with H_kv dividing H_q")
     group = hq // hkv
     return [rmm(P[h], V[h // group], rho, 1.0, rows, threads) for h in (range(hq) if heads is None else heads)]
+
+
+def fp8_e4m3_value(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes, fp64: sign bit 7, exponent bits 6-3 with
+    bias 7, mantissa bits 2-0; exponent 0 is subnormal (m / 8) 2^-6, the code
+    S.1111.111 is NaN and there are no infinities (max 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def int8_value(codes: np.ndarray) -> np.ndarray:
+    """Values of two's-complement int8 codes stored as bytes, fp64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def decode_wq(a: np.ndarray, codes: np.ndarray, fmt: str, scale: np.ndarray, rho: float, alpha: float = 1.0,
+              threads: Optional[int] = None) -> Result:
+    """Single-row decode over 8-bit weights: the n = 1 case of ``rmm`` (the
+    scores are |a_j|) with B[t, c] = value(q[t, c]) * scale[c]; returns the
+    selection and y = alpha * a[I] B[I, :] (1 x m, fp64)."""
+    values = fp8_e4m3_value(codes) if fmt == "fp8" else int8_value(codes) if fmt == "int8" else None
+    if values is None:
+        raise ValueError("fmt must be 'fp8' or 'int8'")
+    a2 = np.asarray(a, dtype=np.float64).reshape(1, -1)
+    B = values * np.asarray(scale, dtype=np.float64)[None, :]
+    return rmm(a2, B, rho, alpha, None, threads)
 
 
 def diagnostics(A: np.ndarray, B: np.ndarray, idx: np.ndarray) -> dict:

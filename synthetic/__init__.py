@@ -45,6 +45,8 @@ __all__ = [
     "make_case",
     "make_decode_case",
     "attention_weights",
+    "quantize_columns",
+    "make_wq_decode_case",
     "make_pv_case",
     "CONFIGS",
     "sha256_of",
@@ -297,6 +299,64 @@ def make_pv_case(scale: Optional[dict] = None, seed: int = 7) -> Case:
     for g in range(hkv):
         V[g] = _store(rng.standard_normal((Lk, dv)), "bf16")
     return Case("pv", "bf16", P, V, (0.5, 0.8, 1.0), group=hq // hkv)
+
+
+def _e4m3_grid() -> np.ndarray:
+    """The 127 non-negative finite OCP FP8 E4M3 values in code order 0..126
+    (exponent field 0: m 2^-9; else (8 + m) 2^(e-10); code 127 is NaN)."""
+    v = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        v.append(m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10))
+    return np.asarray(v)
+
+
+def quantize_columns(B: np.ndarray, fmt: str, rows_per_chunk: int = 1024):
+    """Weight-only 8-bit quantization with one scale per column: scale_c =
+    max_t |B[t, c]| / Q (Q = 448 for FP8 E4M3, 127 for int8), codes =
+    round-to-nearest-even(B / scale_c) on the format's grid.  Returns
+    (codes uint8 d x m, scale float32 m).  Deterministic (no draws)."""
+    B = np.asarray(B, dtype=np.float32)
+    top = 448.0 if fmt == "fp8" else 127.0 if fmt == "int8" else None
+    if top is None:
+        raise ValueError("fmt must be 'fp8' or 'int8'")
+    amax = np.abs(B).max(axis=0).astype(np.float64)
+    scale = np.where(amax > 0, amax / top, 1.0).astype(np.float32)
+    codes = np.empty(B.shape, dtype=np.uint8)
+    grid = _e4m3_grid()
+    for r0 in range(0, B.shape[0], rows_per_chunk):
+        x = B[r0:r0 + rows_per_chunk].astype(np.float64) / scale.astype(np.float64)[None, :]
+        if fmt == "int8":
+            codes[r0:r0 + rows_per_chunk] = np.clip(np.rint(x), -127, 127).astype(np.int8).view(np.uint8)
+            continue
+        ax = np.minimum(np.abs(x), 448.0)
+        hi = np.clip(np.searchsorted(grid, ax), 1, 126)
+        lo = hi - 1
+        dlo, dhi = ax - grid[lo], grid[hi] - ax
+        pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+        codes[r0:r0 + rows_per_chunk] = (pick | np.where(np.signbit(x) & (pick > 0), 0x80, 0)).astype(np.uint8)
+    return codes, scale
+
+
+@dataclasses.dataclass
+class WQCase:
+    """Single-row decode over 8-bit weights: a (1 x d bf16 values), codes
+    (d x m uint8), scale (m fp32), fmt."""
+    a: np.ndarray
+    codes: np.ndarray
+    scale: np.ndarray
+    fmt: str
+    rhos: tuple
+
+
+def make_wq_decode_case(fmt: str, scale: Optional[dict] = None) -> WQCase:
+    """The 70B up-projection decode (a 1 x 8192 from the c5 recipe, B 8192 x
+    28672 ~ N(0, 1/8192)) with B quantized per column to ``fmt``.  ``scale``
+    overrides n, d, m of the underlying case."""
+    base = make_case("c5", dict(scale or {}, n=1) if scale else dict(n=1))
+    dec = make_decode_case(base)
+    codes, sc = quantize_columns(base.B, fmt)
+    return WQCase(dec.A, codes, sc, fmt, (0.8, 1.0))
 
 
 def make_decode_case(case: Case, seed: int = 55) -> Case:
