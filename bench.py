@@ -60,6 +60,9 @@ WORKLOADS = {
     "c5-decode-int8": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), wq="int8",
                            label="70B up projection decode over int8 weights with per-column scales: "
                                  "a 1x8192 bf16 x B 8192x28672 int8"),
+    "attn": dict(case="attn", rho=0.5, sweep=(0.5, 0.8, 1.0), attn=True,
+                 label="causal attention with reduced scores, softmax fused: Q 32x4096x128, K/V 8 GQA heads "
+                       "x4096x128 bf16"),
     "mlp": dict(case="mlp", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0), mlp=True,
                 label="Llama-3.1-8B-shaped gated MLP block: x 2048x4096, Up/Gate 4096x14336, Down 14336x4096 bf16, "
                       "one rho for all three projections"),
@@ -227,6 +230,70 @@ class WQRunner:
         self.torch.matmul(self.a[i].view(1, -1), self.B16, out=self.Yd)
 
 
+class AttnRunner:
+    """Attention with reduced scores and the softmax fused (rmm_attention);
+    the dense comparison is torch's fused attention kernel (flash or
+    memory-efficient backend only) over the full head dimension."""
+
+    def __init__(self, torch, rmm, copies):
+        import numpy as np
+        import synthetic
+        self.torch, self.rmm = torch, rmm
+        dev = torch.device("cuda:0")
+        Q, K, V = synthetic.make_attention_case()
+
+        def up(x):
+            bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
+            return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+        q0, k0, v0 = up(Q), up(K), up(V)
+        per_set = (q0.numel() + k0.numel() + v0.numel()) * 2
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2 * MALL_BYTES / per_set)))
+        self.copies = copies
+        self.q = [q0] + [q0.clone() for _ in range(copies - 1)]
+        self.k = [k0] + [k0.clone() for _ in range(copies - 1)]
+        self.v = [v0] + [v0.clone() for _ in range(copies - 1)]
+        self.H, self.L, self.dh = Q.shape
+        self.Hkv, self.dv = V.shape[0], V.shape[2]
+        self.n, self.d, self.m, self.batch = self.L, self.dh, self.dv, self.H
+        self.O = [torch.empty((self.H, self.L, self.dv), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+        self.ws, self.idx = {}, {}
+        self._kx = None
+
+    def flops(self, rho):
+        # causal pairs x (reduced scores + value product), per head
+        pairs = self.L * (self.L + 1) / 2
+        return 2.0 * self.H * pairs * (self.rmm.k_of(rho, self.dh) + self.dv)
+
+    def call(self, i, rho, full_path=False):
+        import ctypes
+        torch, rmm = self.torch, self.rmm
+        if rho not in self.ws:
+            need = rmm.load().rmm_attention_workspace_size(self.H, self.Hkv, self.L, self.L, self.dh, rho)
+            if need == ctypes.c_size_t(-1).value:
+                raise rmm.RMMError(2, "rmm_attention_workspace_size")
+            self.ws[rho] = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            self.idx[rho] = torch.empty((self.H, rmm.k_of(rho, self.dh)), dtype=torch.int32, device="cuda:0")
+        rmm.attention(self.q[i], self.k[i], self.v[i], rho, causal=True, out=self.O[i], idx_out=self.idx[rho],
+                      workspace=self.ws[rho])
+
+    def plan(self, rho):
+        return {"route": "attention", "gemm": "attn_fwd", "splits": 1}
+
+    def dense(self, i):
+        torch = self.torch
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        if self._kx is None:
+            g = self.H // self.Hkv
+            self._kx = [kk.repeat_interleave(g, dim=0).contiguous() for kk in self.k]
+            self._vx = [vv.repeat_interleave(g, dim=0).contiguous() for vv in self.v]
+        # fused kernels only: never the unfused bf16 math path
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            self.O[i].copy_(torch.nn.functional.scaled_dot_product_attention(
+                self.q[i].unsqueeze(0), self._kx[i].unsqueeze(0), self._vx[i].unsqueeze(0), is_causal=True)[0])
+
+
 class MLPRunner:
     """The gated MLP block (rmm_gated_mlp) with its inputs, rotated over copies."""
 
@@ -379,6 +446,29 @@ def cpu_baseline(runner, rho, budget_s=12.0):
             "seconds_measured": t_sel + t_rows + t_probe}
 
 
+def cpu_baseline_attn(runner, rho, rows=256):
+    """The oracle's attention for one head on a row sample (norms, TopK and
+    the reduced scores of those rows, softmax, value product), scaled to the
+    whole layer by causal pairs."""
+    import numpy as np
+    import synthetic
+    import oracle
+    Q, K, V = synthetic.make_attention_case()
+    L = Q.shape[1]
+    sample = np.sort(np.random.default_rng(0).choice(L, size=rows, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(Q, K, V, rho, causal=True, heads=[0], rows=sample)
+    t = time.perf_counter() - t0
+    pairs_sample = float(np.sum(sample + 1))
+    k = oracle.k_of(rho, Q.shape[2])
+    flops = 2.0 * pairs_sample * (k + V.shape[2])
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.host_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle attention of head 0 for {rows} of {L} query rows (column norms and TopK of the "
+                      f"whole head, reduced scores of the sampled rows, causal softmax, value product; {t:.2f} s), "
+                      "rate over those rows' causal pairs",
+            "seconds_measured": t}
+
+
 def cpu_baseline_wq(runner, rho):
     """The oracle's whole 8-bit-weight decode (decode, select, product) on this host."""
     import oracle
@@ -438,8 +528,11 @@ def main(argv=None):
     wl = WORKLOADS[args.workload]
     is_mlp = wl.get("mlp", False)
     is_wq = "wq" in wl
+    is_attn = wl.get("attn", False)
     if is_mlp:
         runner = MLPRunner(torch, rmm, args.copies)
+    elif is_attn:
+        runner = AttnRunner(torch, rmm, args.copies)
     elif is_wq:
         runner = WQRunner(torch, rmm, wl["wq"], args.copies)
     else:
@@ -456,11 +549,17 @@ def main(argv=None):
 
     sweep = []
     if not args.no_sweep:
-        runner.dense(0)
-        dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
-        log(f"dense torch.matmul: {dense_ms * 1e3:.1f} us/step")
+        try:
+            runner.dense(0)
+            torch.cuda.synchronize()
+        except RuntimeError as e:  # e.g. no fused attention kernel for this GPU in this torch build
+            log(f"dense comparison unavailable: {e}")
+            dense_ms = None
+        else:
+            dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
+            log(f"dense {'fused attention' if is_attn else 'torch.matmul'}: {dense_ms * 1e3:.1f} us/step")
         for r in wl["sweep"]:
-            for full in ((False, True) if r == 1.0 and not is_mlp and not is_wq else (False,)):
+            for full in ((False, True) if r == 1.0 and not (is_mlp or is_wq or is_attn) else (False,)):
                 t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
                                runner.copies, graph)
                 ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
@@ -477,7 +576,15 @@ def main(argv=None):
     log("per-kernel us per step: " + ", ".join(f"{kk}={v[0] * v[1] * 1e3:.1f}" + (f" ({v[1]:g} launches)" if v[1] != 1 else "")
                                            for kk, v in kt.items() if v[1]))
     stream = runner.plan(rho)["gemm"] == "stream"
-    if runner.n == 1:
+    if is_attn:
+        # the fused attention kernel: reduced scores and value product on the matrix cores
+        dom = "gemm"
+        gemm_ms = kt["gemm"][0]
+        achieved = runner.flops(rho) / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "attn_fwd", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": runner.flops(rho),
+                "kernel_ms": gemm_ms}
+    elif runner.n == 1:
         dom, bound = "gemv", "hbm"
         gemv_ms = kt["gemv"][0]
         if is_wq:  # kept 8-bit rows + a + column scales + fp32 partial row
@@ -519,7 +626,10 @@ def main(argv=None):
     roof["per_kernel_ms"] = {kk: v[0] for kk, v in kt.items() if v[1]}
 
     cpu = None
-    if rank == 0 and not args.no_cpu_baseline and is_wq:
+    if rank == 0 and not args.no_cpu_baseline and is_attn:
+        cpu = cpu_baseline_attn(runner, rho)
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+    elif rank == 0 and not args.no_cpu_baseline and is_wq:
         cpu = cpu_baseline_wq(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
     elif rank == 0 and not args.no_cpu_baseline and not is_mlp:  # the fp64 block needs every row of h: no bounded sample

@@ -284,6 +284,33 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
  * outside the above, RMM_ERR_WORKSPACE for a short workspace.
  */
 enum { RMM_WQ_FP8_E4M3 = 0, RMM_WQ_INT8 = 1 };
+
+/*
+ * Attention with reduced scores and the softmax fused (Sec. 3.2,
+ * "Attention"): for each query head h,
+ *   I_h = TopK(||Q_h[:, j]||_2, k = rmm_k(rho, dh))   (feature selection on Q)
+ *   O_h = softmax(alpha * Q_h[:, I_h] K_g[:, I_h]^T + M) V_g
+ * with alpha = 1/sqrt(dh) (the full head dimension), g = h / (H / Hkv) the
+ * grouped-query key/value head, and M the causal mask when causal = 1 (query
+ * i, the (Lk - Lq + i)-th position, sees keys 0 .. Lk - Lq + i).  The scores
+ * never reach HBM.
+ *
+ * q: H x Lq x dh, k: Hkv x Lk x dh, v: Hkv x Lk x dv, out: H x Lq x dv, all
+ * bf16, contiguous, 16-byte aligned; dh <= 128 and a multiple of 8, dv = 128,
+ * H a multiple of Hkv, Lq <= Lk when causal.  idx_out (H x k int32, each row
+ * ascending) may be NULL.  The softmax runs in fp32 (running maximum and sum,
+ * exponentials in base 2), the probabilities enter the value product rounded
+ * to bf16, accumulation is fp32 and O is rounded to nearest-even bf16.  The
+ * caller owns every buffer; workspace: rmm_attention_workspace_size bytes,
+ * 256-byte aligned (SIZE_MAX there: invalid or unsupported sizes).  Returns
+ * RMM_ERR_INVALID_ARG for null pointers, bad sizes, causal with Lq > Lk or
+ * overlapping buffers, RMM_ERR_UNSUPPORTED for sizes or alignments outside
+ * the above, RMM_ERR_WORKSPACE for a short workspace.
+ */
+size_t rmm_attention_workspace_size(int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t dh, double rho);
+rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t H, int64_t Hkv, int64_t Lq,
+                           int64_t Lk, int64_t dh, int64_t dv, double rho, int32_t causal, void *out, int32_t *idx_out,
+                           void *workspace, size_t ws_bytes, hipStream_t stream);
 size_t rmm_decode_wq_workspace_size(int64_t d, int64_t m, double rho);
 rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const float *scale, int64_t d, int64_t m,
                            int64_t ldb, double rho, float alpha, void *y, int32_t *idx_out, void *workspace,

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
-    "matmul_indexed", "plan_info", "gated_weights", "gated_mlp", "decode_wq", "WQ_FORMATS",
+    "matmul_indexed", "plan_info", "gated_weights", "gated_mlp", "decode_wq", "WQ_FORMATS", "attention",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -123,6 +123,10 @@ def load():
     L.rmm_decode_wq_workspace_size.restype = sz
     L.rmm_decode_wq.argtypes = [vp, vp, i32, vp, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, vp, vp, sz, vp]
     L.rmm_decode_wq.restype = ctypes.c_int
+    L.rmm_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_double]
+    L.rmm_attention_workspace_size.restype = sz
+    L.rmm_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_double, i32, vp, vp, vp, sz, vp]
+    L.rmm_attention.restype = ctypes.c_int
     L.rmm_plan_info.argtypes = [ctypes.POINTER(Desc), ctypes.c_double, ctypes.POINTER(i32)]
     L.rmm_plan_info.restype = ctypes.c_int
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
@@ -380,6 +384,41 @@ def gated_weights(Wg, Wu, transposed: bool = False):
     _check(load().rmm_gated_weights(Wg.data_ptr(), Wu.data_ptr(), d, m, 1 if transposed else 0, out.data_ptr(),
                                     _stream(Wg)), "rmm_gated_weights")
     return out
+
+
+def attention(q, k, v, rho: float, *, causal: bool = True, out=None, idx_out=None, workspace=None):
+    """Attention with reduced scores, softmax fused (rmm_attention).
+
+    q: bf16 (H, Lq, dh); k: bf16 (Hkv, Lk, dh); v: bf16 (Hkv, Lk, 128).
+    Returns (O, idx): O bf16 (H, Lq, 128), idx int32 (H, k) the dimensions
+    each query head keeps."""
+    torch = _torch()
+    _require_gpu(q, k, v)
+    L = load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or {q.dtype, k.dtype, v.dtype} != {torch.bfloat16}:
+        raise ValueError("expected bf16 q (H, Lq, dh), k (Hkv, Lk, dh), v (Hkv, Lk, dv)")
+    H, Lq, dh = q.shape
+    Hkv, Lk, dv = v.shape
+    if k.shape != (Hkv, Lk, dh):
+        raise ValueError("k must be (Hkv, Lk, dh) matching q and v")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("operands must be contiguous")
+    need = L.rmm_attention_workspace_size(H, Hkv, Lq, Lk, dh, float(rho))
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(2, "rmm_attention_workspace_size")
+    kk = int(L.rmm_k(float(rho), dh))
+    if out is None:
+        out = torch.empty((H, Lq, dv), dtype=torch.bfloat16, device=q.device)
+    if idx_out is None:
+        idx_out = torch.empty((H, kk), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        ws, wsb = _workspace(need, q.device)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    st = L.rmm_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), H, Hkv, Lq, Lk, dh, dv, float(rho),
+                         1 if causal else 0, out.data_ptr(), idx_out.data_ptr(), ws.data_ptr(), wsb, _stream(q))
+    _check(st, "rmm_attention")
+    return out, idx_out
 
 
 WQ_FORMATS = {"fp8": 0, "int8": 1}

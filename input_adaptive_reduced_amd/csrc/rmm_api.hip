@@ -542,6 +542,112 @@ rmm_status_t rmm_gated_mlp(const void *x, const void *Wgu, const void *Wd, int64
     return RMM_OK;
 }
 
+namespace {
+struct AttnPlan {
+    int64_t k, kpad, qrows, krows;
+    ColnormPlan cp;
+    size_t off_part, off_s, off_idx, off_q, off_k, total;
+};
+
+rmm_status_t attn_plan(int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t dh, double rho, AttnPlan &p) {
+    memset(&p, 0, sizeof(p));
+    if (H < 1 || Hkv < 1 || Lq < 1 || Lk < 1 || dh < 1 || H % Hkv) return RMM_ERR_INVALID_ARG;
+    p.k = k_of(rho, dh);
+    if (p.k < 1) return RMM_ERR_INVALID_ARG;
+    if (dh > 128 || dh % 8 || H > 65535) return RMM_ERR_UNSUPPORTED;
+    p.kpad = p.k <= 64 ? 64 : 128;
+    p.qrows = (Lq + 31) / 32 * 32;
+    p.krows = (Lk + 31) / 32 * 32;
+    if (p.qrows * p.kpad * 2 >= kMaxBufferBytes || p.krows * p.kpad * 2 >= kMaxBufferBytes ||
+        Lk * 128 * 2 >= kMaxBufferBytes || Lq * dh * 2 >= kMaxBufferBytes || Lk * dh * 2 >= kMaxBufferBytes)
+        return RMM_ERR_UNSUPPORTED;
+    p.cp = colnorm_plan(RMM_BF16, Lq, dh, H);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    p.off_part = take((size_t)p.cp.chunks * dh * H * 4);
+    p.off_s = take((size_t)dh * H * 4);
+    p.off_idx = take((size_t)p.kpad * H * 4);
+    p.off_q = take((size_t)H * p.qrows * p.kpad * 2);
+    p.off_k = take((size_t)H * p.krows * p.kpad * 2);
+    p.total = off;
+    return RMM_OK;
+}
+}  // namespace
+
+size_t rmm_attention_workspace_size(int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t dh, double rho) {
+    AttnPlan p;
+    return attn_plan(H, Hkv, Lq, Lk, dh, rho, p) == RMM_OK ? p.total : SIZE_MAX;
+}
+
+rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t H, int64_t Hkv, int64_t Lq,
+                           int64_t Lk, int64_t dh, int64_t dv, double rho, int32_t causal, void *out, int32_t *idx_out,
+                           void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !out || (causal != 0 && causal != 1)) return RMM_ERR_INVALID_ARG;
+    AttnPlan p;
+    rmm_status_t st = attn_plan(H, Hkv, Lq, Lk, dh, rho, p);
+    if (st != RMM_OK) return st;
+    if (causal && Lq > Lk) return RMM_ERR_INVALID_ARG;
+    if (dv != 128 || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RMM_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < p.total) return RMM_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return RMM_ERR_INVALID_ARG;
+    const int64_t qb = H * Lq * dh * 2, kb = Hkv * Lk * dh * 2, vb = Hkv * Lk * dv * 2, ob = H * Lq * dv * 2;
+    char *ws = static_cast<char *>(workspace);
+    const int64_t wb = (int64_t)p.total;
+    if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, vb) || overlaps(ws, wb, q, qb) ||
+        overlaps(ws, wb, k, kb) || overlaps(ws, wb, v, vb) || overlaps(ws, wb, out, ob) ||
+        (idx_out && (overlaps(idx_out, H * p.k * 4, out, ob) || overlaps(idx_out, H * p.k * 4, ws, wb) ||
+                     overlaps(idx_out, H * p.k * 4, q, qb) || overlaps(idx_out, H * p.k * 4, k, kb) ||
+                     overlaps(idx_out, H * p.k * 4, v, vb))))
+        return RMM_ERR_INVALID_ARG;
+    float *part = reinterpret_cast<float *>(ws + p.off_part);
+    float *s = reinterpret_cast<float *>(ws + p.off_s);
+    int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);
+    uint16_t *Qp = reinterpret_cast<uint16_t *>(ws + p.off_q);
+    uint16_t *Kp = reinterpret_cast<uint16_t *>(ws + p.off_k);
+    // the dimensions each query head keeps: TopK of its columns' norms (one per head)
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(q, RMM_BF16, Lq, dh, dh, H, Lq * dh, p.cp, part, stream));
+    if (norm_select_ok(p.cp.chunks, dh)) {
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_norm_select(part, p.cp.chunks, dh, H, p.k, idx_out, p.k, pidx, p.kpad, stream));
+    } else {
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, dh, H, s, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_select(s, nullptr, RMM_F32, 0, H, dh, p.k, idx_out, p.k, pidx, p.kpad, nullptr, stream));
+    }
+    // Q_h[:, I_h] and, per query head, K_g[:, I_h] in MFMA operand blocks
+    RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(q, RMM_BF16, Lq, dh, dh, Lq * dh, 1, pidx, p.kpad, p.kpad, Qp,
+                                            p.qrows * p.kpad, H, 1, stream));
+    RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(k, RMM_BF16, Lk, dh, dh, Lk * dh, H / Hkv, pidx, p.kpad, p.kpad, Kp,
+                                            p.krows * p.kpad, H, 1, stream));
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = Qp;
+    a.q_stride = p.qrows * p.kpad;
+    a.q_bytes = p.qrows * p.kpad * 2;
+    a.K = Kp;
+    a.k_stride = p.krows * p.kpad;
+    a.k_bytes = p.krows * p.kpad * 2;
+    a.V = static_cast<const uint16_t *>(v);
+    a.ldv = dv;
+    a.v_stride = Lk * dv;
+    a.v_bytes = Lk * dv * 2;
+    a.O = static_cast<uint16_t *>(out);
+    a.ldo = dv;
+    a.o_stride = Lq * dv;
+    a.H = (int)H;
+    a.group = (int)(H / Hkv);
+    a.Lq = (int)Lq;
+    a.Lk = (int)Lk;
+    a.causal = causal;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+    RMM_LAUNCH(RMM_KERNEL_GEMM, launch_attention_fwd(a, (int)p.kpad, stream));
+    return RMM_OK;
+}
+
 size_t rmm_decode_wq_workspace_size(int64_t d, int64_t m, double rho) {
     const int64_t k = k_of(rho, d);
     if (k < 1 || d > kFusedSelectMaxD || m < 16 || m % 16) return SIZE_MAX;

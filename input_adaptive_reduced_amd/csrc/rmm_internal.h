@@ -189,6 +189,26 @@ struct GenericArgs {
 hipError_t launch_gemm_generic(const GenericArgs &g, hipStream_t stream);
 
 // Decode: y = alpha * sum_t aval[t] * B[idx[t], :] (split over t, then reduce).
+// Attention with reduced scores and the softmax fused (attention.hip).  Q
+// and K packed per query head in MFMA operand blocks (launch_pack layout 1,
+// kq = 64 or 128 entries per row), V row-major (Lk x 128 per key/value head,
+// ldv apart), O row-major (Lq x 128 per query head, ldo apart).  *_stride
+// are per-head element strides, *_bytes the bytes readable from each head's
+// base (< 2^31).  scale_log2 = alpha * log2(e).
+struct AttnArgs {
+    const uint16_t *Q;
+    int64_t q_stride, q_bytes;
+    const uint16_t *K;
+    int64_t k_stride, k_bytes;
+    const uint16_t *V;
+    int64_t ldv, v_stride, v_bytes;
+    uint16_t *O;
+    int64_t ldo, o_stride;
+    int H, group, Lq, Lk, causal;
+    float scale_log2;
+};
+hipError_t launch_attention_fwd(const AttnArgs &a, int kq, hipStream_t stream);
+
 int gemv_splits(int64_t m, int64_t k);
 // Gathered GEMV over 8-bit weights (fmt 0: OCP FP8 E4M3, 1: int8) with one
 // fp32 scale per column: part[split][c] = scale[c] * sum over the split's

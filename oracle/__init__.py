@@ -21,6 +21,10 @@ LLM Inference":
   P_h[:, T] V_g[T, :] with g the GQA key/value head of query head h
   (Sec. 3.2, "Attention", and eq. 2 of App. D.1); no renormalisation of the
   kept weights (reading: the paragraph writes the product over T alone).
+* ``attention`` -- attention with reduced scores (Sec. 3.2, "Attention"):
+  per query head the dimensions I_h from Q_h's column norms, scores
+  alpha Q_h[:, I_h] K_g[:, I_h]^T, the causal mask, a row softmax (fp64,
+  maximum subtracted) and the product with V_g.
 * ``fp8_e4m3_value``, ``int8_value``, ``decode_wq`` -- single-row decode over
   8-bit weights with per-column scales (W8A16; App. B.6 combines RMM with
   INT8 weight quantization): I = TopK(|a_j|, k), y = scale * a[I] q[I, :],
@@ -215,6 +219,37 @@ def attention_pv(P: np.ndarray, V: np.ndarray, rho: float, heads: Optional[Seque
         raise ValueError("P must be (H_q, L_q, L_k) and V (H_kv, L_k, d_v) with H_kv dividing H_q")
     group = hq // hkv
     return [rmm(P[h], V[h // group], rho, 1.0, rows, threads) for h in (range(hq) if heads is None else heads)]
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, rho: float, causal: bool = True,
+              heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
+              threads: Optional[int] = None):
+    """softmax(alpha Q_h[:, I] K_g[:, I]^T + M) V_g per query head (Sec. 3.2,
+    "Attention"), alpha = 1/sqrt(d_h), I from Q_h's column norms, M = -inf on
+    keys after the query's position (queries are the last L_q of L_k
+    positions) when ``causal``.  Q (H, Lq, dh), K (Hkv, Lk, dh), V (Hkv, Lk,
+    dv).  Returns a list of (idx, O) per requested head, O for the requested
+    rows (all by default), fp64."""
+    hq, Lq, dh = Q.shape
+    hkv, Lk, _ = K.shape
+    if hq % hkv or V.shape[:2] != (hkv, Lk):
+        raise ValueError("Q (H, Lq, dh), K (Hkv, Lk, dh), V (Hkv, Lk, dv) with Hkv dividing H")
+    group = hq // hkv
+    alpha = 1.0 / np.sqrt(dh)
+    rows_arr = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = []
+    for h in (range(hq) if heads is None else heads):
+        g = h // group
+        Kt = np.ascontiguousarray(np.asarray(K[g], dtype=np.float64).T)
+        res = rmm(Q[h], Kt, rho, alpha, rows_arr, threads)   # the reduced scores of the requested rows
+        S = res.Y
+        if causal:
+            S = np.where(np.arange(Lk)[None, :] > (rows_arr + (Lk - Lq))[:, None], -np.inf, S)
+        S = S - S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=1, keepdims=True)
+        out.append((res.idx, P @ np.asarray(V[g], dtype=np.float64)))
+    return out
 
 
 def fp8_e4m3_value(codes: np.ndarray) -> np.ndarray:

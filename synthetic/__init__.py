@@ -46,6 +46,7 @@ __all__ = [
     "make_decode_case",
     "attention_weights",
     "quantize_columns",
+    "make_attention_case",
     "make_wq_decode_case",
     "make_pv_case",
     "CONFIGS",
@@ -357,6 +358,21 @@ def make_wq_decode_case(fmt: str, scale: Optional[dict] = None) -> WQCase:
     dec = make_decode_case(base)
     codes, sc = quantize_columns(base.B, fmt)
     return WQCase(dec.A, codes, sc, fmt, (0.8, 1.0))
+
+
+def make_attention_case(scale: Optional[dict] = None, seed: int = 8):
+    """Q and K of the QK^T case (c4: per-(head, dim) log-normal scales) and V
+    (H_kv x L x 128) ~ N(0, 1) in bf16 from its own seed; ``scale`` as for c4
+    (heads, kv_heads, L, dh) plus dv.  Returns (Q, K, V) float32 arrays."""
+    s = dict(scale or {})
+    dv = s.pop("dv", 128)
+    c = make_case("c4", s)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hkv, L = c.B.shape[0], c.B.shape[1]
+    V = np.empty((hkv, L, dv), dtype=np.float32)
+    for g in range(hkv):
+        V[g] = _store(rng.standard_normal((L, dv)), "bf16")
+    return c.A, c.B, V
 
 
 def make_decode_case(case: Case, seed: int = 55) -> Case:
