@@ -66,7 +66,7 @@ __device__ __forceinline__ uint4 *attn_stage(uint4 *a0, uint4 *a1, uint4 *a2) {
 }
 
 template <int KS>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnArgs g) {
+__global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs g) {
     constexpr int KB = 64;                // keys per block
     constexpr int KBUF = 2 * KS * 64;     // uint4 per K stage: 2 row groups x KS operand blocks of 1 KB
     constexpr int VCH = 16;               // 16-byte chunks per V row (128 columns)
