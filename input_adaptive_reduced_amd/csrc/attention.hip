@@ -88,7 +88,9 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs
     int t = blockIdx.x;
     if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // each XCD takes a contiguous run of tiles
     const int h = t / qtiles;
-    const int q0 = (t - h * qtiles) * 128;
+    int qt = t - h * qtiles;
+    if (g.causal) qt = qtiles - 1 - qt;  // a causal tile's keys grow with its position: longest first
+    const int q0 = qt * 128;
     const int qi = q0 + 32 * w + (lane & 31);  // this lane's query
     const int off = g.Lk - g.Lq;                // queries are the last Lq positions
 
