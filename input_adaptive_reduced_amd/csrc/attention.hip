@@ -58,15 +58,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nrec, 0x00020000);
 }
 
-template <int S>
+// stage S of NS (2 or 3) LDS stages
+template <int NS, int S>
 __device__ __forceinline__ uint4 *attn_stage(uint4 *a0, uint4 *a1, uint4 *a2) {
-    if constexpr (S % 3 == 0) return a0;
-    else if constexpr (S % 3 == 1) return a1;
+    if constexpr (S % NS == 0) return a0;
+    else if constexpr (S % NS == 1) return a1;
     else return a2;
 }
 
+// KS = kq / 16.  kq = 64: three stages, two blocks ahead (72 KB); kq = 128:
+// two stages, one block ahead (64 KB), so that two workgroups share a CU in
+// both cases.
 template <int KS>
-__global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs g) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
+    constexpr int NS = KS == 4 ? 3 : 2;   // LDS stages
     constexpr int KB = 64;                // keys per block
     constexpr int KBUF = 2 * KS * 64;     // uint4 per K stage: 2 row groups x KS operand blocks of 1 KB
     constexpr int VCH = 16;               // 16-byte chunks per V row (128 columns)
@@ -76,10 +81,10 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs
     static_assert(NL < 16, "vmcnt immediate");
     __shared__ uint4 sK0[KBUF];
     __shared__ uint4 sK1[KBUF];
-    __shared__ uint4 sK2[KBUF];
+    __shared__ uint4 sK2[NS == 3 ? KBUF : 1];
     __shared__ uint4 sV0[VBUF];
     __shared__ uint4 sV1[VBUF];
-    __shared__ uint4 sV2[VBUF];
+    __shared__ uint4 sV2[NS == 3 ? VBUF : 1];
     typedef __attribute__((address_space(3))) void lds_t;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hsel = lane >> 5;
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs
 
     const int kend = g.causal ? min(g.Lk, q0 + 128 + off) : g.Lk;
     const int nblk = (kend + KB - 1) / KB;
-    const int npad = (nblk + 2) / 3 * 3;
+    const int npad = (nblk + NS - 1) / NS * NS;
 
     auto issue = [&](int blk, uint4 *dK, uint4 *dV) __attribute__((always_inline)) {
         const bool real = blk < nblk;
@@ -220,22 +225,26 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 1) void attn_fwd_kernel(AttnArgs
             }
     };
 
+    // three stages: block e landed once only block e+1's loads are younger;
+    // two stages: block e+1 is issued only after the barrier, so wait for all
     auto block = [&](int e, auto Sc) __attribute__((always_inline)) {
         constexpr int S = decltype(Sc)::value;
-        __builtin_amdgcn_s_waitcnt(0x0f70 | NL);  // vmcnt(NL): block e landed, e+1 in flight
+        if constexpr (NS == 3) __builtin_amdgcn_s_waitcnt(0x0f70 | NL);  // vmcnt(NL)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);                          // vmcnt(0)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(min(e + 2, npad), attn_stage<S + 2>(sK0, sK1, sK2), attn_stage<S + 2>(sV0, sV1, sV2));
-        compute(e, attn_stage<S>(sK0, sK1, sK2), attn_stage<S>(sV0, sV1, sV2));
+        issue(min(e + NS - 1, npad), attn_stage<NS, S + NS - 1>(sK0, sK1, sK2),
+              attn_stage<NS, S + NS - 1>(sV0, sV1, sV2));
+        compute(e, attn_stage<NS, S>(sK0, sK1, sK2), attn_stage<NS, S>(sV0, sV1, sV2));
     };
 
     if (npad > 0) {
         issue(0, sK0, sV0);
-        issue(1, sK1, sV1);
-        for (int e = 0; e < npad; e += 3) {
+        if constexpr (NS == 3) issue(1, sK1, sV1);
+        for (int e = 0; e < npad; e += NS) {
             block(e, std::integral_constant<int, 0>{});
             block(e + 1, std::integral_constant<int, 1>{});
-            block(e + 2, std::integral_constant<int, 2>{});
+            if constexpr (NS == 3) block(e + 2, std::integral_constant<int, 2>{});
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load outlives the workgroup
