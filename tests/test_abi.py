@@ -135,3 +135,41 @@ def test_plan_info_on_host(lib):
     ds = r.Desc()
     lib.rmm_desc_init(ctypes.byref(ds), r.BF16, 64, 256, 128)
     assert lib.rmm_plan_info(ctypes.byref(ds), 0.5, None) == 1          # NULL output
+
+
+def test_attention_and_decode_wq_host_checks(lib):
+    """Workspace sizing and argument checks of rmm_attention and rmm_decode_wq
+    are host-only: they return before any GPU call (fake, aligned pointers)."""
+    SZ_MAX = ctypes.c_size_t(-1).value
+    ws_a = lib.rmm_attention_workspace_size
+    assert ws_a(32, 8, 4096, 4096, 128, 0.5) not in (0, SZ_MAX)
+    assert ws_a(32, 8, 4096, 4096, 128, 0.5) < ws_a(32, 8, 4096, 4096, 128, 0.8)   # 64 vs 128 kept columns
+    assert ws_a(32, 6, 64, 64, 128, 0.5) == SZ_MAX        # H not a multiple of Hkv
+    assert ws_a(4, 4, 64, 64, 136, 0.5) == SZ_MAX         # dh > 128
+    assert ws_a(4, 4, 64, 64, 100, 0.5) == SZ_MAX         # dh % 8 != 0
+    assert ws_a(4, 4, 64, 64, 128, 0.0) == SZ_MAX         # invalid rho
+    P = ctypes.c_void_p
+    q, k, v, o, w = P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x100000)
+    need = ws_a(2, 1, 64, 64, 128, 0.5)
+    att = lib.rmm_attention
+    assert att(None, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, o, None, w, need, None) == 1   # null q
+    assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 2, o, None, w, need, None) == 1      # causal not 0/1
+    assert att(q, k, v, 2, 1, 96, 64, 128, 128, 0.5, 1, o, None, w, need, None) == 1      # causal, Lq > Lk
+    assert att(q, k, v, 2, 1, 64, 64, 128, 64, 0.5, 1, o, None, w, need, None) == 2       # dv != 128
+    assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, P(0x40008), None, w, need, None) == 2  # misaligned out
+    assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, o, None, w, need - 1, None) == 3  # short workspace
+    assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, o, None, P(0x100010), need, None) == 1  # unaligned ws
+    assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, P(0x10000 + 256), None, w, need, None) == 1  # out over q
+    ws_d = lib.rmm_decode_wq_workspace_size
+    assert ws_d(8192, 28672, 0.8) not in (0, SZ_MAX)
+    assert ws_d(8192, 40, 0.8) == SZ_MAX                  # m % 16 != 0
+    assert ws_d(20000, 1024, 0.8) == SZ_MAX               # beyond the fused selection
+    a, bq, sc, y = P(0x10000), P(0x200000), P(0x30000), P(0x40000)
+    need = ws_d(1024, 256, 0.5)
+    dec = lib.rmm_decode_wq
+    assert dec(a, bq, 2, sc, 1024, 256, 256, 0.5, 1.0, y, None, w, need, None) == 1     # unknown format
+    assert dec(a, bq, 0, sc, 1024, 256, 128, 0.5, 1.0, y, None, w, need, None) == 1     # ldb < m
+    assert dec(a, bq, 0, sc, 1024, 256, 264, 0.5, 1.0, y, None, w, need, None) == 2     # ldb % 16 != 0
+    assert dec(a, P(0x200008), 0, sc, 1024, 256, 256, 0.5, 1.0, y, None, w, need, None) == 2  # misaligned codes
+    assert dec(a, bq, 0, sc, 1024, 256, 256, 0.5, 1.0, y, None, w, need - 1, None) == 3  # short workspace
+    assert dec(a, bq, 0, sc, 1024, 256, 256, 0.5, 1.0, P(0x200000 + 512), None, w, need, None) == 1  # y over codes
