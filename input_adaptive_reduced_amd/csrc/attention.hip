@@ -160,15 +160,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ss], s[kb], 0, 0, 0);
             }
         }
-        // s[kb][r]: key key0 + 32 kb + 8 (r / 4) + 4 hsel + r % 4 for query qi
+        // s[kb][r]: key key0 + 32 kb + 8 (r / 4) + 4 hsel + r % 4 for query qi; only blocks
+        // reaching past Lk or past the wave's first query need the mask (a wave-uniform test)
+        const bool masked = key0 + KB > g.Lk || (g.causal && key0 + KB - 1 > q0 + 32 * w + off);
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hsel + (r & 3);
                 float v = s[kb][r] * g.scale_log2;
-                if (key >= g.Lk || (g.causal && key > qi + off)) v = -INFINITY;
+                if (masked) {
+                    const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                    if (key >= g.Lk || (g.causal && key > qi + off)) v = -INFINITY;
+                }
                 s[kb][r] = v;
                 mx = fmaxf(mx, v);
             }
@@ -192,10 +196,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
                 }
         ls += __shfl_xor(ls, 32);
         l = l * fac + ls;
+        if (__ballot(fac != 1.f)) {  // some row's maximum moved: rescale its running output
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[j][e] *= fac;
+                for (int e = 0; e < 16; ++e) o[j][e] *= fac;
+        }
         // O^T += V^T P^T: P slot k of lane group hsel in step (kb, st) is key
         // 32 kb + 16 st + 8 (k / 4) + 4 hsel + k % 4 of the block
         const int gq = lane >> 4, li = lane & 15;
