@@ -164,22 +164,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
         // reaching past Lk or past the wave's first query need the mask (a wave-uniform test)
         const bool masked = key0 + KB > g.Lk || (g.causal && key0 + KB - 1 > q0 + 32 * w + off);
         float mx = -INFINITY;
+        if (masked) {
+            const int lim = g.causal ? min(g.Lk - 1, qi + off) : g.Lk - 1;  // last key this query sees
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float v = s[kb][r] * g.scale_log2;
-                if (masked) {
+                for (int r = 0; r < 16; ++r) {
                     const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                    if (key >= g.Lk || (g.causal && key > qi + off)) v = -INFINITY;
+                    s[kb][r] = key > lim ? -INFINITY : s[kb][r] * g.scale_log2;
+                    mx = fmaxf(mx, s[kb][r]);
                 }
-                s[kb][r] = v;
-                mx = fmaxf(mx, v);
-            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] *= g.scale_log2;
+                    mx = fmaxf(mx, s[kb][r]);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(m, mx);
         const float mref = mn == -INFINITY ? 0.f : mn;
-        const float fac = exp2f(m - mref);
+        // raw v_exp_f32: arguments are <= 0, and results below 2^-126 (flushed to zero)
+        // vanish against the row maximum's 1 in both the bf16 weights and the row sum
+        const float fac = __builtin_amdgcn_exp2f(m - mref);
         m = mn;
         float ls = 0.f;
         uint32_t pk[2][2][4];  // [half][k16 step][pair]
@@ -189,8 +198,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p0 = exp2f(s[kb][8 * st + 2 * i] - mref);
-                    const float p1 = exp2f(s[kb][8 * st + 2 * i + 1] - mref);
+                    const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i] - mref);
+                    const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * st + 2 * i + 1] - mref);
                     ls += p0 + p1;
                     pk[kb][st][i] = pack_bf16x2(p0, p1);
                 }
