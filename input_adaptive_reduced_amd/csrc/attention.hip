@@ -8,9 +8,10 @@
 // keeps a running row maximum and row sum (online softmax) while it walks the
 // keys, so HBM sees Q_I, K_I and V once and O once.
 //
-// Inputs: Q_I and K_I packed per query head in MFMA operand blocks (1 KB per
-// 32 rows x 16 kept dims; rows padded to 32 with zeros, dims to kq = 64 or
-// 128 with zeros), V row-major (L_k x 128 per key/value head).
+// Inputs: Q as given (each lane gathers its row's kept columns once), K_I
+// packed per query head in MFMA operand blocks (1 KB per 32 rows x 16 kept
+// dims; rows padded to 32 with zeros, dims to kq = 64 or 128 with zeros), V
+// row-major (L_k x 128 per key/value head).
 //
 // Workgroup: 128 queries of one head, four waves of 32.  Each wave keeps its
 // Q fragments in registers for the whole key loop.  Per 64-key block the K
@@ -99,19 +100,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
     const int qi = q0 + 32 * w + (lane & 31);  // this lane's query
     const int off = g.Lk - g.Lq;                // queries are the last Lq positions
 
-    const __amdgpu_buffer_rsrc_t rQ = attn_rsrc(g.Q + (int64_t)h * g.q_stride, g.q_bytes);
     const __amdgpu_buffer_rsrc_t rK = attn_rsrc(g.K + (int64_t)h * g.k_stride, g.k_bytes);
     const __amdgpu_buffer_rsrc_t rV = attn_rsrc(g.V + (int64_t)(h / g.group) * g.v_stride, g.v_bytes);
     const uint32_t ldv2 = (uint32_t)(g.ldv * 2);
 
-    // Q fragments of this wave's 32 rows (operand block (row group, s) at (R * KS + s) KB)
+    // Q fragments of this lane's row, gathered through the kept-column list once per
+    // workgroup: slot (s, k) of lane group hsel is column idx[16 s + 8 hsel + k]
+    // (zero past k and for rows past Lq)
     abf16x8_t qf[KS];
     {
-        const int R = (q0 >> 5) + w;
+        const int32_t *kid = g.idx + (int64_t)h * g.ld_idx + 8 * hsel;
+        const uint16_t *qrow = g.Q + ((int64_t)h * g.Lq + min(qi, g.Lq - 1)) * g.dh;
+        const bool row_ok = qi < g.Lq;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const uint32_t o = (uint32_t)((R * KS + s) * 1024 + lane * 16);
-            qf[s] = attn_bf16x8(__builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, o, 0, 0)));
+            uint32_t pk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c0 = kid[16 * s + 2 * i], c1 = kid[16 * s + 2 * i + 1];
+                const uint32_t v0 = row_ok && c0 >= 0 ? qrow[c0] : 0u;
+                const uint32_t v1 = row_ok && c1 >= 0 ? qrow[c1] : 0u;
+                pk[i] = v0 | (v1 << 16);
+            }
+            qf[s] = attn_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
         }
     }
 

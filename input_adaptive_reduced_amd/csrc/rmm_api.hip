@@ -546,7 +546,7 @@ namespace {
 struct AttnPlan {
     int64_t k, kpad, qrows, krows;
     ColnormPlan cp;
-    size_t off_part, off_s, off_idx, off_q, off_k, total;
+    size_t off_part, off_s, off_idx, off_k, total;
 };
 
 rmm_status_t attn_plan(int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t dh, double rho, AttnPlan &p) {
@@ -571,7 +571,6 @@ rmm_status_t attn_plan(int64_t H, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d
     p.off_part = take((size_t)p.cp.chunks * dh * H * 4);
     p.off_s = take((size_t)dh * H * 4);
     p.off_idx = take((size_t)p.kpad * H * 4);
-    p.off_q = take((size_t)H * p.qrows * p.kpad * 2);
     p.off_k = take((size_t)H * p.krows * p.kpad * 2);
     p.total = off;
     return RMM_OK;
@@ -606,7 +605,6 @@ rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t 
     float *part = reinterpret_cast<float *>(ws + p.off_part);
     float *s = reinterpret_cast<float *>(ws + p.off_s);
     int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);
-    uint16_t *Qp = reinterpret_cast<uint16_t *>(ws + p.off_q);
     uint16_t *Kp = reinterpret_cast<uint16_t *>(ws + p.off_k);
     // the dimensions each query head keeps: TopK of its columns' norms (one per head)
     RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(q, RMM_BF16, Lq, dh, dh, H, Lq * dh, p.cp, part, stream));
@@ -618,16 +616,15 @@ rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t 
         RMM_LAUNCH(RMM_KERNEL_SELECT,
                    launch_select(s, nullptr, RMM_F32, 0, H, dh, p.k, idx_out, p.k, pidx, p.kpad, nullptr, stream));
     }
-    // Q_h[:, I_h] and, per query head, K_g[:, I_h] in MFMA operand blocks
-    RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(q, RMM_BF16, Lq, dh, dh, Lq * dh, 1, pidx, p.kpad, p.kpad, Qp,
-                                            p.qrows * p.kpad, H, 1, stream));
+    // per query head K_g[:, I_h] in MFMA operand blocks (Q's kept columns are gathered in the kernel)
     RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(k, RMM_BF16, Lk, dh, dh, Lk * dh, H / Hkv, pidx, p.kpad, p.kpad, Kp,
                                             p.krows * p.kpad, H, 1, stream));
     AttnArgs a;
     memset(&a, 0, sizeof(a));
-    a.Q = Qp;
-    a.q_stride = p.qrows * p.kpad;
-    a.q_bytes = p.qrows * p.kpad * 2;
+    a.Q = static_cast<const uint16_t *>(q);
+    a.idx = pidx;
+    a.ld_idx = p.kpad;
+    a.dh = dh;
     a.K = Kp;
     a.k_stride = p.krows * p.kpad;
     a.k_bytes = p.krows * p.kpad * 2;

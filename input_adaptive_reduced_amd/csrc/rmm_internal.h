@@ -189,15 +189,16 @@ struct GenericArgs {
 hipError_t launch_gemm_generic(const GenericArgs &g, hipStream_t stream);
 
 // Decode: y = alpha * sum_t aval[t] * B[idx[t], :] (split over t, then reduce).
-// Attention with reduced scores and the softmax fused (attention.hip).  Q
-// and K packed per query head in MFMA operand blocks (launch_pack layout 1,
-// kq = 64 or 128 entries per row), V row-major (Lk x 128 per key/value head,
+// Attention with reduced scores and the softmax fused (attention.hip).  K
+// packed per query head in MFMA operand blocks (launch_pack layout 1, kq = 64
+// or 128 entries per row), Q as given, V row-major (Lk x 128 per key/value head,
 // ldv apart), O row-major (Lq x 128 per query head, ldo apart).  *_stride
 // are per-head element strides, *_bytes the bytes readable from each head's
 // base (< 2^31).  scale_log2 = alpha * log2(e).
 struct AttnArgs {
-    const uint16_t *Q;
-    int64_t q_stride, q_bytes;
+    const uint16_t *Q;     // H x Lq x dh row-major (the kept columns are gathered in the kernel)
+    const int32_t *idx;    // kept columns per head, ld_idx apart, -1 past k
+    int64_t ld_idx, dh;
     const uint16_t *K;
     int64_t k_stride, k_bytes;
     const uint16_t *V;
