@@ -1273,7 +1273,10 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
 
     const int ar = 32 * w + (lane & 31);  // this lane's staged A row
     const int hsel = lane >> 5;
-    auto compute = [&](int e, const uint4 *cP, const uint4 *cV) {
+    // column p of staged row ar sits at byte ((p >> 3) ^ (ar & 7)) * 16 + (p & 7) * 2 of the row,
+    // which is 2p ^ rsw: the swizzle only flips bits 4-6
+    const uint32_t rsw = (uint32_t)(ar & 7) << 4;
+    auto compute = [&](int e, const uint4 *cP, const uint4 *cV) __attribute__((always_inline)) {
         const int u = sWin[e], cnt = (int)sBeg[e + 1] - (int)sBeg[e];
         const char *prow = reinterpret_cast<const char *>(cP) + ar * (PCH * 16);
         for (int ks = 0; ks * 16 < cnt; ++ks) {
@@ -1286,9 +1289,8 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
 #pragma unroll
                 for (int z = 0; z < 2; ++z) {
                     const int j = ks * 16 + hsel * 8 + 2 * h + z;
-                    const int p = (int)(word >> (8 * (2 * (h & 1) + z))) & (W - 1);
-                    const uint16_t x =
-                        *reinterpret_cast<const uint16_t *>(prow + ((((p >> 3) ^ (ar & 7)) << 4) | ((p & 7) << 1)));
+                    const uint32_t p = (word >> (8 * (2 * (h & 1) + z))) & (W - 1);
+                    const uint16_t x = *reinterpret_cast<const uint16_t *>(prow + ((p << 1) ^ rsw));
                     v2[z] = j < cnt ? (uint32_t)x : 0u;
                 }
                 pk[h] = v2[0] | (v2[1] << 16);
