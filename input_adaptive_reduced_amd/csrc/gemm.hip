@@ -1279,7 +1279,9 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
     auto compute = [&](int e, const uint4 *cP, const uint4 *cV) __attribute__((always_inline)) {
         const int u = sWin[e], cnt = (int)sBeg[e + 1] - (int)sBeg[e];
         const char *prow = reinterpret_cast<const char *>(cP) + ar * (PCH * 16);
-        for (int ks = 0; ks * 16 < cnt; ++ks) {
+        // one k16 step; only a window's last, partial step masks slots past its count
+        auto kstep = [&](int ks, auto Mc) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(Mc)::value;
             const uint2 pp = *reinterpret_cast<const uint2 *>(sPos + u * W + ks * 16 + hsel * 8);
             uint32_t pk[4];
 #pragma unroll
@@ -1288,10 +1290,9 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
                 uint32_t v2[2];
 #pragma unroll
                 for (int z = 0; z < 2; ++z) {
-                    const int j = ks * 16 + hsel * 8 + 2 * h + z;
                     const uint32_t p = (word >> (8 * (2 * (h & 1) + z))) & (W - 1);
-                    const uint16_t x = *reinterpret_cast<const uint16_t *>(prow + ((p << 1) ^ rsw));
-                    v2[z] = j < cnt ? (uint32_t)x : 0u;
+                    const uint32_t x = *reinterpret_cast<const uint16_t *>(prow + ((p << 1) ^ rsw));
+                    v2[z] = !MASK || ks * 16 + hsel * 8 + 2 * h + z < cnt ? x : 0u;
                 }
                 pk[h] = v2[0] | (v2[1] << 16);
             }
@@ -1315,7 +1316,10 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
                 // operands swapped: lane l holds output row l % 32
                 acc[jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb.v, fa, acc[jn], 0, 0, 0);
             }
-        }
+        };
+        int ks = 0;
+        for (; (ks + 1) * 16 <= cnt; ++ks) kstep(ks, std::false_type{});
+        if (ks * 16 < cnt) kstep(ks, std::true_type{});
     };
 
     // window e: its loads landed once only window e+1's six are younger
