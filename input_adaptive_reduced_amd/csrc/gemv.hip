@@ -185,10 +185,12 @@ __global__ __launch_bounds__(512) void gemv_wq_partial_kernel(const uint8_t *__r
 }  // namespace
 
 int gemv_wq_splits(int64_t m, int64_t k) {
-    // as gemv_splits, for 1024-column workgroups
+    // about 1024 workgroups of 1024 columns, at least 256 kept rows per split
+    // (an 8-bit row is half a bf16 row: longer splits amortise each
+    // workgroup's list copy and LDS sum)
     const int64_t blocks = (m + kGemvWqCols - 1) / kGemvWqCols;
-    int64_t s = (2048 + blocks - 1) / blocks;
-    const int64_t max_s = (k + 127) / 128;
+    int64_t s = (1024 + blocks - 1) / blocks;
+    const int64_t max_s = (k + 255) / 256;
     if (s > max_s) s = max_s;
     const int64_t min_s = (k + kGemvMaxRows - 1) / kGemvMaxRows;
     if (s < min_s) s = min_s;
