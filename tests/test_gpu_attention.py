@@ -117,3 +117,22 @@ def test_attention_rejects_unsupported(rmm, torch):
     v64 = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rmm.RMMError):
         rmm.attention(q, torch.zeros((1, 64, 128), dtype=torch.bfloat16, device="cuda"), v64, 0.5)  # dv != 128
+
+
+def test_attention_repeatable_and_null_index_output(rmm, torch):
+    """Two calls give bit-identical outputs, and the C entry point accepts a
+    NULL kept-dimension output (the same O)."""
+    import ctypes
+    Q, K, V = case(dict(heads=4, kv_heads=2, L=256, dh=128), 0.5)
+    q, k, v = to_device(Q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    O1, i1 = rmm.attention(q, k, v, 0.5, causal=True)
+    O2, i2 = rmm.attention(q, k, v, 0.5, causal=True)
+    L = rmm.load()
+    need = L.rmm_attention_workspace_size(4, 2, 256, 256, 128, 0.5)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    O3 = torch.empty_like(O1)
+    st = L.rmm_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), 4, 2, 256, 256, 128, 128, 0.5, 1, O3.data_ptr(),
+                         None, ws.data_ptr(), need, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(O1, O2) and torch.equal(i1, i2) and torch.equal(O1, O3)

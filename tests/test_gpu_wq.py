@@ -106,3 +106,23 @@ def test_unsupported_shapes(rmm, torch):
     with pytest.raises(ValueError):
         rmm.decode_wq(a, torch.zeros((64, 48), dtype=torch.uint8, device="cuda"),
                       torch.ones(48, dtype=torch.float32, device="cuda"), 0.5, "fp4")
+
+
+def test_repeatable_and_null_index_output(rmm, torch):
+    """Two calls give bit-identical outputs, and the C entry point accepts a
+    NULL kept-row output (the same y)."""
+    import ctypes
+    a, codes, scale = small_case(11, 2048, 1024, "fp8")
+    ad = to_device(a, "bf16")
+    Bq, sc = torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda()
+    y1, i1 = rmm.decode_wq(ad, Bq, sc, 0.6, "fp8")
+    y2, i2 = rmm.decode_wq(ad, Bq, sc, 0.6, "fp8")
+    L = rmm.load()
+    need = L.rmm_decode_wq_workspace_size(2048, 1024, 0.6)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y3 = torch.empty_like(y1)
+    st = L.rmm_decode_wq(ad.data_ptr(), Bq.data_ptr(), 0, sc.data_ptr(), 2048, 1024, 1024, 0.6, 1.0, y3.data_ptr(),
+                         None, ws.data_ptr(), need, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(y1, y2) and torch.equal(i1, i2) and torch.equal(y1, y3)
