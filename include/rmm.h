@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
     RMM_OK = 0,
     RMM_ERR_INVALID_ARG = 1, /* a size, pointer, stride or rho is invalid */
-    RMM_ERR_UNSUPPORTED = 2, /* valid request this build cannot run */
+    RMM_ERR_UNSUPPORTED = 2, /* valid request the library cannot run */
     RMM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
     RMM_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } rmm_status_t;
