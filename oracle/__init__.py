@@ -29,6 +29,10 @@ LLM Inference":
   8-bit weights with per-column scales (W8A16; App. B.6 combines RMM with
   INT8 weight quantization): I = TopK(|a_j|, k), y = scale * a[I] q[I, :],
   with the codes decoded from the OCP FP8 E4M3 definition or as int8.
+* ``dequantize``, ``reduced_product_wq`` -- the reduced product of an n-row
+  activation block with 8-bit weights (codes and one fp32 scale per column,
+  the W8A16 combination of App. B.6): the four steps of ``rmm`` on A and the
+  dequantized weights value(q) * scale.
 * ``diagnostics`` -- retained energy (App. B.4 / eq. 16), the Prop. 1 bound
   (eq. 12), the Cor. 1 bound (eq. 14) and the relative bound (eq. 17).
 * ``gated_mlp`` -- the gated MLP block with RMM on its three projections
@@ -275,12 +279,33 @@ def decode_wq(a: np.ndarray, codes: np.ndarray, fmt: str, scale: np.ndarray, rho
     """Single-row decode over 8-bit weights: the n = 1 case of ``rmm`` (the
     scores are |a_j|) with B[t, c] = value(q[t, c]) * scale[c]; returns the
     selection and y = alpha * a[I] B[I, :] (1 x m, fp64)."""
+    a2 = np.asarray(a, dtype=np.float64).reshape(1, -1)
+    return rmm(a2, dequantize(codes, fmt, scale), rho, alpha, None, threads)
+
+
+def dequantize(codes: np.ndarray, fmt: str, scale: np.ndarray) -> np.ndarray:
+    """The weights that 8-bit codes with one fp32 scale per column stand for:
+    B[t, c] = value(q[t, c]) * scale[c], fp64 (``fmt`` "fp8" = OCP E4M3,
+    "int8" = two's complement)."""
     values = fp8_e4m3_value(codes) if fmt == "fp8" else int8_value(codes) if fmt == "int8" else None
     if values is None:
         raise ValueError("fmt must be 'fp8' or 'int8'")
-    a2 = np.asarray(a, dtype=np.float64).reshape(1, -1)
-    B = values * np.asarray(scale, dtype=np.float64)[None, :]
-    return rmm(a2, B, rho, alpha, None, threads)
+    return values * np.asarray(scale, dtype=np.float64)[None, :]
+
+
+def reduced_product_wq(A: np.ndarray, codes: np.ndarray, fmt: str, scale: np.ndarray, rho: float,
+                       alpha: float = 1.0, rows: Optional[Sequence[int]] = None,
+                       threads: Optional[int] = None) -> Result:
+    """RMM with weights stored as 8-bit codes and per-column fp32 scales
+    (weight-only quantization, W8A16; App. B.6 runs RMM on INT8-quantized
+    weights): the four steps of ``rmm`` on A (n x d) and the dequantized
+    weights B = value(q) * scale (``dequantize``).  The selection depends on
+    A only (Sec. 3.2), so it is the same as over unquantized weights; the
+    product is alpha * A[:, I] B[I, :] by the triple loop, fp64."""
+    B = dequantize(codes, fmt, scale)
+    if np.shape(A)[1] != B.shape[0]:
+        raise ValueError("A's columns must match the code rows")
+    return rmm(A, B, rho, alpha, rows, threads)
 
 
 def diagnostics(A: np.ndarray, B: np.ndarray, idx: np.ndarray) -> dict:

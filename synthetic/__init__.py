@@ -48,6 +48,7 @@ __all__ = [
     "quantize_columns",
     "make_attention_case",
     "make_wq_decode_case",
+    "make_wq_case",
     "make_pv_case",
     "CONFIGS",
     "sha256_of",
@@ -358,6 +359,26 @@ def make_wq_decode_case(fmt: str, scale: Optional[dict] = None) -> WQCase:
     dec = make_decode_case(base)
     codes, sc = quantize_columns(base.B, fmt)
     return WQCase(dec.A, codes, sc, fmt, (0.8, 1.0))
+
+
+@dataclasses.dataclass
+class WQGemmCase:
+    """An activation block times 8-bit weights: A (n x d bf16 values), codes
+    (d x m uint8), scale (m fp32), fmt."""
+    A: np.ndarray
+    codes: np.ndarray
+    scale: np.ndarray
+    fmt: str
+    rhos: tuple
+
+
+def make_wq_case(fmt: str, scale: Optional[dict] = None) -> WQGemmCase:
+    """The 70B up projection (A 4096 x 8192 from the c5 recipe, B 8192 x 28672
+    ~ N(0, 1/8192)) with B quantized per column to ``fmt``; ``scale``
+    overrides n, d, m of the underlying case (same draw order)."""
+    base = make_case("c5", scale)
+    codes, sc = quantize_columns(base.B, fmt)
+    return WQGemmCase(base.A, codes, sc, fmt, (0.5, 0.8, 1.0))
 
 
 def make_attention_case(scale: Optional[dict] = None, seed: int = 8):
