@@ -2,24 +2,35 @@
 """Throughput of the reduced-matrix-multiplication path on one MI355X.
 
 A step is one whole rmm_matmul -- column norms, TopK, gather, reduced product
--- on the Llama-3.1-8B-shaped projection A (4096 x 4096, bf16) x B
-(4096 x 4096, bf16) at rho = 0.8 (k = 3277), the retention ratio of the
-paper's latency experiments.  ``value`` is 2 n k m / t per step in TFLOP/s
-with every input resident in HBM: the steps rotate over enough distinct
-(A, B) pairs that the working set exceeds the 256 MB Infinity Cache.
+-- on the largest layer product: the Llama-3.1-70B-shaped MLP up projection
+A (4096 x 8192, bf16) x B (8192 x 28672, bf16) at rho = 0.8 (k = 6554), the
+retention ratio of the paper's latency experiments.  ``value`` is 2 n k m / t
+per step in TFLOP/s with every input resident in HBM: the steps rotate over
+enough distinct (A, B) pairs that the working set exceeds the 256 MB Infinity
+Cache.  Other workloads (the 8B projections, attention, decode, the gated
+MLP block) are selected with --workload.
 
 The same JSON line carries
-  * ``sweep``: the path at rho = 0.5, 0.7, 0.8, 1.0 (and rho = 1 with the
+  * ``median_ms_per_step``: the median of per-step event times from a second
+    pass of the same K steps (``ms_per_step`` is the mean of the bracketed
+    pass that ``value`` comes from);
+  * ``sweep``: the path at each rho of the workload (and rho = 1 with the
     full path forced) with the dense bf16 torch.matmul (hipBLASLt) time and
     the speedup over it;
   * ``roofline``: the reduced-product GEMM kernel (the dominant kernel),
     timed per launch with HIP events recorded around it on its own stream,
-    against the bf16 MFMA peak; ``traffic`` comes from committed rocprofv3
-    counters when they were taken on the current kernel source, else null;
+    against the bf16 MFMA datasheet peak and against the matrix-core
+    throughput measured on this GPU in the same run (``measured_peak``);
+    ``traffic`` comes from committed rocprofv3 counters when they were taken
+    on the current kernel source, else null;
+  * ``clocks``: shader and memory clocks sampled from sysfs during the timed
+    pass (null where the files cannot be read);
+  * ``inputs_sha256``: digest of the bf16 input bytes;
   * ``cpu_baseline``: the CPU oracle timed on this host on a bounded sample
-    (full norms and selection, a sample of output rows, extrapolated).
+    (full norms and selection, a sample of output rows, extrapolated), and
+    ``parity``: the GPU's kept set and sampled output rows against it.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 """
 from __future__ import annotations
 
@@ -45,7 +56,7 @@ WORKLOADS = {
                label="Llama-3.1-8B-shaped projection: A 4096x4096 bf16 x B 4096x4096 bf16"),
     "c3": dict(case="c3", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0),
                label="Llama-3.1-8B-shaped MLP down projection: A 2048x14336 bf16 x B 14336x4096 bf16"),
-    "c5": dict(case="c5", rho=0.8, sweep=(0.8, 1.0),
+    "c5": dict(case="c5", rho=0.8, sweep=(0.5, 0.7, 0.8, 1.0),
                label="Llama-3.1-70B-shaped MLP up projection: A 4096x8192 bf16 x B 8192x28672 bf16"),
     "c5-decode": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), decode=True,
                       label="70B up projection decode: a 1x8192 bf16 x B 8192x28672 bf16"),
@@ -116,6 +127,7 @@ class Runner:
             return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
 
         A0, B0 = up(case.A), up(case.B)
+        self.sha256 = synthetic.sha256_of(synthetic.as_bf16_bits(case.A), synthetic.as_bf16_bits(case.B))
         per_set = A0.numel() * 2 + B0.numel() * 2
         if copies is None:
             copies = max(2, min(16, math.ceil(2 * MALL_BYTES / per_set)))
@@ -355,7 +367,7 @@ class MLPRunner:
         torch.matmul(h, self.Wd[i], out=self.Y[i])
 
 
-def time_steps(torch, fn, steps, warmup, copies, graph):
+def time_steps(torch, fn, steps, warmup, copies, graph, clocks=None, median=False):
     """Mean ms per step over `steps` calls of fn(i) rotating over copies.
 
     With graphs, each input set's step is captured once (after one eager call
@@ -385,12 +397,109 @@ def time_steps(torch, fn, steps, warmup, copies, graph):
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
+    with (clocks if clocks is not None else _Null()):
+        start.record()
+        for i in range(steps):
+            run(i)
+        stop.record()
+        torch.cuda.synchronize()
+    mean = start.elapsed_time(stop) / steps
+    if median:
+        return mean, step_median(torch, fn, steps, copies, run)
+    return mean
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def step_median(torch, fn, steps, copies, graph_runs=None):
+    """Median ms per step from events recorded between consecutive steps (a
+    separate pass: the event records sit between the steps)."""
+    run = graph_runs if graph_runs is not None else (lambda i: fn(i % copies))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
     for i in range(steps):
         run(i)
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+
+
+class ClockSampler:
+    """Polls the GPU's current shader and memory clock levels from sysfs
+    (pp_dpm_sclk / pp_dpm_mclk of the PCI device torch reports) on a
+    background thread while a region runs; the readings are MHz values of
+    the level marked current."""
+
+    def __init__(self, torch):
+        self.paths = None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+            paths = {k: os.path.join(dev, f"pp_dpm_{k}") for k in ("sclk", "mclk")}
+            if all(os.access(v, os.R_OK) for v in paths.values()):
+                self.paths = paths
+                self.device = dev
+                with open(paths["sclk"]) as f:  # the driver's level table, as read before the region
+                    self.table = " | ".join(ln.strip() for ln in f if ln.strip())
+        except Exception:  # noqa: BLE001  (no sysfs, no PCI id: report null)
+            self.paths = None
+        self.samples = {"sclk": [], "mclk": []}
+        self._stop = None
+
+    @staticmethod
+    def _current(path):
+        with open(path) as f:
+            for ln in f:
+                if ln.rstrip().endswith("*"):
+                    tok = ln.split(":", 1)[1].strip().split()[0]
+                    return float(tok.lower().replace("mhz", ""))
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.paths:
+            self._stop = threading.Event()
+
+            def poll():
+                while not self._stop.is_set():
+                    for k, p in self.paths.items():
+                        try:
+                            v = self._current(p)
+                        except (OSError, ValueError, IndexError):
+                            v = None
+                        if v is not None:
+                            self.samples[k].append(v)
+                    self._stop.wait(0.002)
+
+            self._thread = threading.Thread(target=poll, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.paths or not self.samples["sclk"]:
+            return None
+        out = {"source": self.device + "/pp_dpm_{sclk,mclk} (the DPM level the driver marks current)",
+               "samples": len(self.samples["sclk"]), "sclk_levels": getattr(self, "table", None)}
+        for k, v in self.samples.items():
+            if v:
+                v = sorted(v)
+                out[f"{k}_mhz_median"] = v[len(v) // 2]
+                out[f"{k}_mhz_min"] = v[0]
+                out[f"{k}_mhz_max"] = v[-1]
+        return out
 
 
 def kernel_times(torch, rmm, runner, rho, steps, copies):
@@ -405,9 +514,13 @@ def kernel_times(torch, rmm, runner, rho, steps, copies):
     return {kname: (ms / cnt if cnt else 0.0, cnt / steps) for kname, (ms, cnt) in rec.items()}
 
 
-def cpu_baseline(runner, rho, budget_s=12.0):
+def cpu_baseline(runner, rho, budget_s=12.0, gpu=None):
     """The oracle as it stands, on this host's cores: full norms and selection,
-    the product on a sample of output rows, extrapolated to the whole job."""
+    the product on a sample of output rows, extrapolated to the whole job.
+
+    ``gpu`` (optional) is (idx, Y) of the GPU's own call on the same inputs
+    (batch entry 0): its kept set is compared with the oracle's in full and
+    its sampled rows with the oracle's rows (``parity`` in the result)."""
     import numpy as np
     import oracle
     threads = oracle.host_threads()
@@ -437,7 +550,20 @@ def cpu_baseline(runner, rho, budget_s=12.0):
     per_matrix = t_sel + t_rows * n / rows
     total = per_matrix * runner.batch
     value = 2.0 * runner.batch * n * k * m / total / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    parity = None
+    if gpu is not None:
+        g_idx, g_Y = gpu
+        cmp_rows = sample[::max(1, sample.size // 256)][:256]  # spread over the sample
+        Y_ref = oracle.reduced_product(A64, B64, idx, 1.0, rows=cmp_rows, threads=threads)
+        Y_got = g_Y[cmp_rows].astype(np.float64)
+        order = np.sort(s)[::-1]
+        parity = {"idx_exact": bool(np.array_equal(g_idx, idx)),
+                  "rel_frobenius": float(np.linalg.norm(Y_got - Y_ref) / np.linalg.norm(Y_ref)),
+                  "rows_compared": int(cmp_rows.size), "tolerance": 1e-2,
+                  "boundary_rel_gap": float((order[k - 1] - order[k]) / order[k - 1]) if k < d else None,
+                  "what": "GPU kept set vs the oracle's fp64 full-sort TopK (all of it); GPU output rows vs the "
+                          "oracle's fp64 triple-loop rows (relative Frobenius error over the compared rows)"}
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "parity": parity,
             "sample": (f"fp64 oracle: full column norms + full-sort TopK of one {n}x{d} matrix "
                        f"({t_sel:.2f} s) and the reduced product for {rows} of {n} output rows "
                        f"({t_rows:.2f} s)" +
@@ -488,7 +614,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=None, help="input sets rotated over (default: > 2x MALL)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -497,6 +623,9 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB a few times (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings) and exit")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="only run the matrix-core ceiling probe and print its TFLOP/s")
+    ap.add_argument("--no-mfma-ceiling", action="store_true", help="skip the matrix-core ceiling probe")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -525,6 +654,11 @@ def main(argv=None):
                           "launches": 5}), flush=True)
         return 0
 
+    if args.calibrate_mfma:
+        cal = rmm.calibrate_mfma()
+        print(json.dumps({"calibration": "bf16 matrix-core ceiling", **cal}), flush=True)
+        return 0
+
     wl = WORKLOADS[args.workload]
     is_mlp = wl.get("mlp", False)
     is_wq = "wq" in wl
@@ -542,10 +676,13 @@ def main(argv=None):
     graph = not args.no_graph
     log(f"workload {args.workload}: {wl['label']}; copies={runner.copies} graph={graph}")
 
-    ms = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph)
+    clocks = ClockSampler(torch)
+    ms, med = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph,
+                         clocks=clocks, median=True)
     value = runner.flops(rho) / (ms * 1e-3) / 1e12
     k = rmm.k_of(rho, runner.d)
-    log(f"rho={rho} k={k}: {ms * 1e3:.1f} us/step, {value:.1f} TFLOP/s")
+    log(f"rho={rho} k={k}: {ms * 1e3:.1f} us/step (median {med * 1e3:.1f}), {value:.1f} TFLOP/s; "
+        f"clocks {clocks.summary()}")
 
     sweep = []
     if not args.no_sweep:
@@ -624,6 +761,18 @@ def main(argv=None):
                 "algorithmic_flops": runner.flops(rho), "kernel_ms": gemm_ms}
     roof["traffic"] = load_traffic(dom, args.workload)
     roof["per_kernel_ms"] = {kk: v[0] for kk, v in kt.items() if v[1]}
+    if roof["bound"] == "mfma" and not args.no_mfma_ceiling:
+        cal = rmm.calibrate_mfma()
+        ceiling = sorted(cal["tflops"])[len(cal["tflops"]) // 2]
+        roof["measured_peak"] = ceiling
+        roof["frac_of_measured_peak"] = roof["achieved"] / ceiling
+        roof["measured_peak_shader_mhz"] = sorted(cal["shader_mhz"])[len(cal["shader_mhz"]) // 2]
+        roof["measured_peak_how"] = ("median of %d back-to-back launches of the matrix-core probe "
+                                     "(rmm_calibrate_mfma: %d workgroups x 4 waves, eight independent "
+                                     "v_mfma_f32_32x32x16_bf16 chains, no memory traffic); shader clock read "
+                                     "in the probe's waves from the cycle counter against the 100 MHz counter"
+                                     % (len(cal["tflops"]), cal["workgroups"]))
+        log(f"matrix-core ceiling measured: {ceiling:.0f} TFLOP/s; GEMM at {roof['frac_of_measured_peak']:.3f} of it")
 
     cpu = None
     if rank == 0 and not args.no_cpu_baseline and is_attn:
@@ -633,8 +782,14 @@ def main(argv=None):
         cpu = cpu_baseline_wq(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
     elif rank == 0 and not args.no_cpu_baseline and not is_mlp:  # the fp64 block needs every row of h: no bounded sample
-        cpu = cpu_baseline(runner, rho)
-        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        # the GPU's own result on input copy 0, for the parity check against the oracle's
+        key = (rho, False)
+        runner.call(0, rho)
+        torch.cuda.synchronize()
+        g_idx = runner.idx[key].view(runner.batch, -1)[0].cpu().numpy()
+        g_Y = (runner.Y[0][0] if runner.batched else runner.Y[0]).float().cpu().numpy()
+        cpu = cpu_baseline(runner, rho, gpu=(g_idx, g_Y))
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads; parity {cpu['parity']}")
 
     line = {
         "metric": METRIC,
@@ -644,6 +799,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "median_ms_per_step": med,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -653,6 +809,9 @@ def main(argv=None):
                    "n": runner.n, "d": runner.d, "m": runner.m, "batch": runner.batch, "rho": rho, "k": k,
                    "input_copies_rotated": runner.copies, "hip_graph": graph},
         "roofline": roof,
+        "clocks": clocks.summary(),
+        "inputs_sha256": getattr(runner, "sha256", None),
+        "parity": cpu.pop("parity", None) if cpu else None,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }

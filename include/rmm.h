@@ -88,6 +88,13 @@ int32_t rmm_version(void);
  *            not matter
  * Errors: RMM_ERR_INVALID_ARG for n < 1, d < 1, lda < d, NULL A or s_out, or
  * an unknown dtype; RMM_ERR_WORKSPACE for a short workspace.
+ * Summation order: each entry point adds the squares of a column in a fixed
+ * order, but rmm_colnorm and rmm_matmul (and rmm_gated_mlp) split the rows
+ * into different chunks, so their fp32 norms can differ in the last bits.
+ * rmm_select(rmm_colnorm(A)) therefore keeps the same set as rmm_matmul's
+ * idx_out whenever the k-th and (k+1)-th largest norms differ by more than
+ * fp32 rounding (relative ~1e-6); closer than that, each call is still
+ * deterministic, but the two may break the near-tie differently.
  */
 size_t rmm_colnorm_workspace_size(rmm_dtype_t dt, int64_t n, int64_t d);
 rmm_status_t rmm_colnorm(const void *A, rmm_dtype_t dt, int64_t n, int64_t d, int64_t lda,
@@ -339,6 +346,25 @@ enum {
 };
 rmm_status_t rmm_timing_enable(int32_t enable, int32_t capacity);
 rmm_status_t rmm_timing_collect(double *ms, int64_t *count);
+
+/*
+ * Matrix-core ceiling probe for measurement tools: enqueues one kernel of
+ * `workgroups` workgroups of four waves; each wave issues `iters` rounds of
+ * eight independent v_mfma_f32_32x32x16_bf16 (no memory traffic), so the
+ * launch performs workgroups * 4 * iters * 8 * 32768 flops.  Timing it
+ * (events around the launch) gives the bf16 matrix throughput the chip
+ * sustains at the clock it holds under that load, to set beside the
+ * datasheet peak.  out: device, out_len >= workgroups * 256 floats (one
+ * checksum per thread, written so the work cannot be elided).  clk: device,
+ * 2 * workgroups uint64 or NULL; when given, entry 2w receives the shader
+ * clock cycles and entry 2w + 1 the ticks of the constant 100 MHz counter
+ * that the first wave of workgroup w spent in its loop (clock under this
+ * load = cycles / ticks * 100 MHz).
+ * Errors: RMM_ERR_INVALID_ARG for NULL out, workgroups outside [1, 2^20],
+ * iters < 1 or a short out; RMM_ERR_HIP when the launch fails.
+ */
+rmm_status_t rmm_calibrate_mfma(int64_t workgroups, int32_t iters, float *out, int64_t out_len, uint64_t *clk,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

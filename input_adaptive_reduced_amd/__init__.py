@@ -23,6 +23,7 @@ __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
     "matmul_indexed", "plan_info", "gated_weights", "gated_mlp", "decode_wq", "WQ_FORMATS", "attention",
+    "check_out", "calibrate_mfma",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -132,6 +133,7 @@ def load():
     L.rmm_timing_enable.argtypes, L.rmm_timing_enable.restype = [i32, i32], ctypes.c_int
     L.rmm_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.rmm_timing_collect.restype = ctypes.c_int
+    L.rmm_calibrate_mfma.argtypes, L.rmm_calibrate_mfma.restype = [i64, i32, vp, i64, vp, vp], ctypes.c_int
     _lib = L
     return L
 
@@ -191,6 +193,35 @@ def _workspace(nbytes: int, device):
     return torch.empty(int(nbytes), dtype=torch.uint8, device=device), int(nbytes)
 
 
+def _ptr(t):
+    """Device address of an optional tensor (None -> NULL)."""
+    return None if t is None else t.data_ptr()
+
+
+def check_out(t, shape, dtype, device, name: str):
+    """Raise ValueError unless ``t`` can receive an output of ``shape`` and
+    ``dtype`` on ``device``: exact shape and dtype, contiguous, same device.
+    The library writes through the raw pointer, so a smaller or strided
+    tensor would be written past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+
+
+def _user_workspace(workspace, need: int, device):
+    """The caller's workspace (uint8-sized bytes on ``device``) or a new one."""
+    if workspace is None:
+        return _workspace(need, device)
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def colnorm(A) -> "torch.Tensor":
     """s_j = ||A[:, j]||_2 (fp32) of a 2-D bf16/fp32 tensor with unit column stride."""
     torch = _torch()
@@ -202,8 +233,8 @@ def colnorm(A) -> "torch.Tensor":
     dt = _dtype_code(A)
     s = torch.empty(d, dtype=torch.float32, device=A.device)
     ws, wsb = _workspace(L.rmm_colnorm_workspace_size(dt, n, d), A.device)
-    _check(L.rmm_colnorm(A.data_ptr(), dt, n, d, A.stride(0), s.data_ptr(),
-                         None if ws is None else ws.data_ptr(), wsb, _stream(A)), "rmm_colnorm")
+    _check(L.rmm_colnorm(A.data_ptr(), dt, n, d, A.stride(0), s.data_ptr(), _ptr(ws), wsb, _stream(A)),
+           "rmm_colnorm")
     return s
 
 
@@ -299,23 +330,23 @@ def matmul(A, B, rho: float, *, transB: bool = False, b_group: int = 1, alpha: f
         raise RMMError(1, f"rho={rho!r}")
     if out is None:
         out = torch.empty(shape, dtype=A.dtype, device=A.device)
-    elif tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1:
-        raise ValueError("out has the wrong shape, dtype or layout")
+    elif (tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1 or out.device != A.device
+          or (A.dim() == 3 and out.stride(0) < shape[1] * out.stride(1))):
+        # rows may be padded (ldy = out.stride(-2)); every element must be addressable
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    idx_shape = (ds.batch, k) if A.dim() == 3 else (k,)
     if idx_out is None and return_idx:
-        idx_out = torch.empty((ds.batch, k) if A.dim() == 3 else (k,), dtype=torch.int32, device=A.device)
-    if idx_out is not None and (idx_out.dtype != torch.int32 or not idx_out.is_contiguous()
-                                or idx_out.numel() != ds.batch * k):
-        raise ValueError("idx_out must be a contiguous int32 tensor with batch*k elements")
+        idx_out = torch.empty(idx_shape, dtype=torch.int32, device=A.device)
+    elif idx_out is not None:
+        # any contiguous int32 tensor of batch*k elements (e.g. flat) will do
+        check_out(idx_out, tuple(idx_out.shape) if idx_out.numel() == ds.batch * k else idx_shape, torch.int32,
+                  A.device, "idx_out")
     need = L.rmm_workspace_size(ctypes.byref(ds), float(rho))
     if need == ctypes.c_size_t(-1).value:
         raise RMMError(1, "rmm_workspace_size")
-    if workspace is None:
-        ws, wsb = _workspace(need, A.device)
-    else:
-        ws, wsb = workspace, workspace.numel() * workspace.element_size()
-    st = L.rmm_matmul(ctypes.byref(ds), A.data_ptr(), B.data_ptr(), float(rho), out.data_ptr(),
-                      None if idx_out is None else idx_out.data_ptr(),
-                      None if ws is None else ws.data_ptr(), wsb, _stream(A))
+    ws, wsb = _user_workspace(workspace, need, A.device)
+    st = L.rmm_matmul(ctypes.byref(ds), A.data_ptr(), B.data_ptr(), float(rho), out.data_ptr(), _ptr(idx_out),
+                      _ptr(ws), wsb, _stream(A))
     _check(st, "rmm_matmul")
     return out, idx_out
 
@@ -331,6 +362,35 @@ def timing_collect() -> dict:
     cnt = (ctypes.c_int64 * n)()
     _check(load().rmm_timing_collect(ms, cnt), "rmm_timing_collect")
     return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n)}
+
+
+def calibrate_mfma(workgroups: int = 2048, iters: int = 4096, repeats: int = 5) -> dict:
+    """Sustained bf16 matrix-core throughput of this GPU (rmm_calibrate_mfma):
+    the probe kernel launched ``repeats`` times back to back on the current
+    stream, each launch timed with events.  Returns the TFLOP/s of every
+    launch, the flops per launch and the shader clock (MHz) the probe's
+    waves measured during each launch (median over workgroups)."""
+    torch = _torch()
+    L = load()
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    clk = torch.empty((repeats, workgroups, 2), dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(repeats + 1)]
+    flops = float(workgroups) * 4 * iters * 8 * 2 * 32 * 32 * 16
+    _check(L.rmm_calibrate_mfma(workgroups, iters, out.data_ptr(), out.numel(), None, sp),
+           "rmm_calibrate_mfma")  # untimed first launch
+    ev[0].record(stream)
+    for r in range(repeats):
+        _check(L.rmm_calibrate_mfma(workgroups, iters, out.data_ptr(), out.numel(), clk[r].data_ptr(), sp),
+               "rmm_calibrate_mfma")
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[r].elapsed_time(ev[r + 1]) for r in range(repeats)]
+    c = clk.cpu().double()
+    mhz = (c[:, :, 0] / c[:, :, 1].clamp(min=1) * 100.0).median(dim=1).values.tolist()
+    return {"flops_per_launch": flops, "ms": ms, "tflops": [flops / (t * 1e-3) / 1e12 for t in ms],
+            "shader_mhz": mhz, "workgroups": workgroups, "iters": iters}
 
 
 def matmul_indexed(A, B, idx, *, transB: bool = False, b_group: int = 1, alpha: float = 1.0, out=None,
@@ -353,17 +413,15 @@ def matmul_indexed(A, B, idx, *, transB: bool = False, b_group: int = 1, alpha: 
     k = int(idx.shape[-1])
     if out is None:
         out = torch.empty(shape, dtype=A.dtype, device=A.device)
-    elif tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1:
-        raise ValueError("out has the wrong shape, dtype or layout")
+    elif (tuple(out.shape) != shape or out.dtype != A.dtype or out.stride(-1) != 1 or out.device != A.device
+          or (A.dim() == 3 and out.stride(0) < shape[1] * out.stride(1))):
+        raise ValueError("out has the wrong shape, dtype, layout or device")
     need = L.rmm_workspace_size_indexed(ctypes.byref(ds), k)
     if need == ctypes.c_size_t(-1).value:
         raise RMMError(1, "rmm_workspace_size_indexed")
-    if workspace is None:
-        ws, wsb = _workspace(need, A.device)
-    else:
-        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    ws, wsb = _user_workspace(workspace, need, A.device)
     st = L.rmm_matmul_indexed(ctypes.byref(ds), A.data_ptr(), B.data_ptr(), idx.data_ptr(), k, out.data_ptr(),
-                              None if ws is None else ws.data_ptr(), wsb, _stream(A))
+                              _ptr(ws), wsb, _stream(A))
     _check(st, "rmm_matmul_indexed")
     return out
 
@@ -407,16 +465,19 @@ def attention(q, k, v, rho: float, *, causal: bool = True, out=None, idx_out=Non
     if need == ctypes.c_size_t(-1).value:
         raise RMMError(2, "rmm_attention_workspace_size")
     kk = int(L.rmm_k(float(rho), dh))
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must live on one device")
     if out is None:
         out = torch.empty((H, Lq, dv), dtype=torch.bfloat16, device=q.device)
+    else:
+        check_out(out, (H, Lq, dv), torch.bfloat16, q.device, "out")
     if idx_out is None:
         idx_out = torch.empty((H, kk), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        ws, wsb = _workspace(need, q.device)
     else:
-        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+        check_out(idx_out, (H, kk), torch.int32, q.device, "idx_out")
+    ws, wsb = _user_workspace(workspace, need, q.device)
     st = L.rmm_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), H, Hkv, Lq, Lk, dh, dv, float(rho),
-                         1 if causal else 0, out.data_ptr(), idx_out.data_ptr(), ws.data_ptr(), wsb, _stream(q))
+                         1 if causal else 0, out.data_ptr(), idx_out.data_ptr(), _ptr(ws), wsb, _stream(q))
     _check(st, "rmm_attention")
     return out, idx_out
 
@@ -449,16 +510,19 @@ def decode_wq(a, Bq, scale, rho: float, fmt: str = "fp8", *, alpha: float = 1.0,
     if need == ctypes.c_size_t(-1).value:
         raise RMMError(2, "rmm_decode_wq_workspace_size")
     k = int(L.rmm_k(float(rho), d))
+    if Bq.device != a.device or scale.device != a.device:
+        raise ValueError("a, Bq and scale must live on one device")
     if out is None:
         out = torch.empty(a.shape[:-1] + (m,), dtype=torch.bfloat16, device=a.device)
+    else:
+        check_out(out, a.shape[:-1] + (m,), torch.bfloat16, a.device, "out")
     if idx_out is None:
         idx_out = torch.empty(k, dtype=torch.int32, device=a.device)
-    if workspace is None:
-        ws, wsb = _workspace(need, a.device)
     else:
-        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+        check_out(idx_out, (k,), torch.int32, a.device, "idx_out")
+    ws, wsb = _user_workspace(workspace, need, a.device)
     st = L.rmm_decode_wq(a.data_ptr(), Bq.data_ptr(), WQ_FORMATS[fmt], scale.data_ptr(), d, m, Bq.stride(0),
-                         float(rho), float(alpha), out.data_ptr(), idx_out.data_ptr(), ws.data_ptr(), wsb, _stream(a))
+                         float(rho), float(alpha), out.data_ptr(), idx_out.data_ptr(), _ptr(ws), wsb, _stream(a))
     _check(st, "rmm_decode_wq")
     return out, idx_out
 
@@ -481,17 +545,17 @@ def gated_mlp(x, Wgu, Wd, rho_in: float, rho_h: float, *, out=None, return_h: bo
     if need == ctypes.c_size_t(-1).value:
         raise RMMError(2, "rmm_gated_mlp_workspace_size")
     k_in, k_h = int(L.rmm_k(float(rho_in), d)), int(L.rmm_k(float(rho_h), m))
+    if Wgu.device != x.device or Wd.device != x.device:
+        raise ValueError("x, Wgu and Wd must live on one device")
     if out is None:
         out = torch.empty((n, d), dtype=torch.bfloat16, device=x.device)
+    else:
+        check_out(out, (n, d), torch.bfloat16, x.device, "out")
     idx_in = torch.empty(k_in, dtype=torch.int32, device=x.device)
     idx_h = torch.empty(k_h, dtype=torch.int32, device=x.device)
     h = torch.empty((n, m), dtype=torch.bfloat16, device=x.device) if return_h else None
-    if workspace is None:
-        ws, wsb = _workspace(need, x.device)
-    else:
-        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    ws, wsb = _user_workspace(workspace, need, x.device)
     st = L.rmm_gated_mlp(x.data_ptr(), Wgu.data_ptr(), Wd.data_ptr(), n, d, m, float(rho_in), float(rho_h),
-                         out.data_ptr(), None if h is None else h.data_ptr(), idx_in.data_ptr(), idx_h.data_ptr(),
-                         ws.data_ptr(), wsb, _stream(x))
+                         out.data_ptr(), _ptr(h), idx_in.data_ptr(), idx_h.data_ptr(), _ptr(ws), wsb, _stream(x))
     _check(st, "rmm_gated_mlp")
     return (out, idx_in, idx_h, h) if return_h else (out, idx_in, idx_h)

@@ -755,8 +755,27 @@ __global__ __launch_bounds__(BS) void select_kernel(const void *__restrict__ src
         static_assert(E % PER == 0, "");
 #pragma unroll
         for (int q = 0; q < E / PER; ++q) {
-            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         r, (uint32_t)(j0 + q * PER) * ESZ, 0, 0));
+            const int p0 = j0 + q * PER;
+            uint4 v;
+            if (p0 + PER <= d || p0 >= d) {
+                v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)p0 * ESZ, 0, 0));
+            } else {
+                // the piece that holds column d-1 and runs past d: element loads, so that
+                // the range check (bytes from d * ESZ on read as zero) never cuts a piece
+                uint32_t e[PER];
+#pragma unroll
+                for (int h = 0; h < PER; ++h) {
+                    const uint32_t off = (uint32_t)(p0 + h) * ESZ;
+                    if constexpr (ROW_BF16)
+                        e[h] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+                    else
+                        e[h] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+                }
+                if constexpr (ROW_BF16)
+                    v = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+                else
+                    v = make_uint4(e[0], e[1], e[2], e[3]);
+            }
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {

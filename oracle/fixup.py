@@ -10,6 +10,10 @@ error): the dropped columns that sit inside the gap are multiplied by 0.99
 (then re-rounded to the storage precision) and the norms recomputed, until
 every boundary passes.
 
+``enforce_gap_mlp`` does the same for the intermediate h of the gated MLP
+block, whose columns are computed: it scales columns of the up-projection
+weight, which scales the matching columns of h.
+
 The norms come from this package's own fp64 ``colnorm``.  A single row
 (n = 1, decode) needs no fix-up: there s_j = |a_j| is exact in both
 precisions and both sides break exact ties toward the lower index.
@@ -76,3 +80,50 @@ def enforce_gap_batched(A: np.ndarray, ks: Iterable[int], dtype: str, rel_gap: f
         out[b], t = enforce_gap(A[b], ks, dtype, rel_gap)
         touched += t
     return out, touched
+
+
+def enforce_gap_mlp(x: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, rho_in: float, ks_h: Iterable[int],
+                    rel_gap: float = 1e-3, max_iter: int = 200) -> Tuple[np.ndarray, int]:
+    """Open the TopK boundary gaps of the gated block's intermediate h.
+
+    h = bf16(SiLU(x_I Wg_I) * (x_I Wu_I)) is computed, so its column norms
+    cannot be spaced by nudging x.  Column c of h is proportional to column c
+    of the up product x_I Wu_I, so scaling Wu[:, c] by 0.99 (re-rounded to
+    bf16) lowers h's column c by about 1%.  Returns (Wu', touched) such that
+    the oracle's h (this package's ``colnorm``, ``topk`` and
+    ``reduced_product``, the same steps as ``gated_mlp``) has, for every k in
+    ``ks_h``, a relative gap of at least ``rel_gap`` between its k-th and
+    (k+1)-th largest column norms.  x and Wg are left as they are.
+
+    This only prepares inputs, so the two products use numpy's fp64 matmul
+    instead of the oracle's triple loop (many times faster on a large
+    block): the sums differ from the oracle's in the last fp64 bits, which
+    moves a bf16 rounding of h, and so a norm, by far less than the gap.
+    """
+    from . import k_of, round_bf16, silu, topk
+
+    x = np.asarray(x, dtype=np.float32)
+    Wu = np.array(Wu, dtype=np.float32, copy=True)
+    d, m = Wu.shape
+    k_in = k_of(rho_in, d)
+    idx_in = topk(colnorm(x), k_in)
+    xi = np.ascontiguousarray(x[:, idx_in], dtype=np.float64)
+    sg = silu(xi @ np.asarray(Wg, dtype=np.float64)[idx_in])
+    u = xi @ Wu[idx_in].astype(np.float64)
+    ks = sorted({int(k) for k in ks_h if 0 < int(k) < m})
+    touched = 0
+    for _ in range(max_iter):
+        s = colnorm(round_bf16(sg * u))
+        order = np.lexsort((np.arange(m), -s))
+        bad = []
+        for k in ks:
+            ok, inside = _boundary_ok(s, order, k, rel_gap)
+            if not ok:
+                bad.append(inside)
+        if not bad:
+            return Wu, touched
+        cols = np.unique(np.concatenate(bad))
+        Wu[:, cols] = round_to_bf16(Wu[:, cols] * np.float32(0.99))
+        u[:, cols] = xi @ Wu[np.ix_(idx_in, cols)].astype(np.float64)
+        touched += cols.size
+    raise RuntimeError("gap fix-up of h did not converge")

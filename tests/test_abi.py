@@ -173,3 +173,27 @@ def test_attention_and_decode_wq_host_checks(lib):
     assert dec(a, P(0x200008), 0, sc, 1024, 256, 256, 0.5, 1.0, y, None, w, need, None) == 2  # misaligned codes
     assert dec(a, bq, 0, sc, 1024, 256, 256, 0.5, 1.0, y, None, w, need - 1, None) == 3  # short workspace
     assert dec(a, bq, 0, sc, 1024, 256, 256, 0.5, 1.0, P(0x200000 + 512), None, w, need, None) == 1  # y over codes
+
+
+def test_binding_refuses_wrong_outputs_before_any_launch():
+    """The binding validates caller-supplied outputs before it calls the
+    library: a tensor of the wrong shape, dtype, layout or device raises
+    ValueError (the library would write through the raw pointer)."""
+    torch = pytest.importorskip("torch")
+    import input_adaptive_reduced_amd as rmm
+
+    meta = torch.device("meta")
+    good = torch.empty((4, 128, 128), dtype=torch.bfloat16, device=meta)
+    rmm.check_out(good, (4, 128, 128), torch.bfloat16, meta, "out")
+    bad = [
+        (torch.empty((4, 127, 128), dtype=torch.bfloat16, device=meta), "shape"),
+        (torch.empty((4, 128, 128), dtype=torch.float32, device=meta), "float32"),
+        (torch.empty((4, 128, 256), dtype=torch.bfloat16, device=meta)[:, :, :128], "contiguous"),
+        (torch.empty((4, 128, 128), dtype=torch.bfloat16), "live on"),
+    ]
+    for t, what in bad:
+        with pytest.raises(ValueError, match=what):
+            rmm.check_out(t, (4, 128, 128), torch.bfloat16, meta, "out")
+    # idx outputs: an int32 tensor one element short is refused
+    with pytest.raises(ValueError, match="shape"):
+        rmm.check_out(torch.empty(63, dtype=torch.int32, device=meta), (64,), torch.int32, meta, "idx_out")

@@ -5,9 +5,14 @@ and relative Frobenius tolerance of ``gpu_util.assert_close``.  Inputs are the
 seeded synthetic workloads, with the TopK boundary gaps opened by
 ``oracle.fixup`` so that fp32 (GPU) and fp64 (oracle) norms rank alike.
 
-Small instances cover every output element and span several tiles plus a
-ragged tail; the full-size workloads (the shapes the benchmark times, in the
-same launch configuration) compare every index and a sample of output rows.
+Every linear case compares every output element (small instances spanning
+several tiles plus a ragged tail; the 256x256 kernels with ragged tiles and
+split K; the full-size projections c2 at every rho and c3 at rho = 0.8, in
+the launch configuration the benchmark times) except c5, whose whole oracle
+product (770 G fp64 multiply-adds, twice over with the error bound's |A||B|)
+would take minutes: it compares every index and about 200 output rows: 192
+seeded random rows plus the first and last rows of every third 256-row tile.  c3 at the other rho
+and the attention cases compare sampled rows as well.
 """
 import math
 
@@ -110,22 +115,41 @@ RAGGED = [
                          ids=[f"{k}{'-splitk' if s else ''}-d{c['d']}-rho{r}{'-full' if f else ''}"
                               for c, r, k, s, f in RAGGED])
 def test_ragged_large_tiles(rmm, scale, rho, kernel, split, full):
-    # sampled rows include the last rows of the ragged final row block
+    # every output element, including the ragged last row and column tiles
+    # and, with split K, every split's partial sums through the reduce
     torch = pytest.importorskip("torch")
     case, A, B64 = linear_case("c2", scale, rhos=(rho,))
-    n = A.shape[0]
-    rows = sorted(set(sample_rows(n, 12, seed=5)) | {n - 1, n - 2, n - 17, n - 33})
     Am = torch.empty(A.shape, dtype=torch.bfloat16, device="meta")
     Bm = torch.empty(case.B.shape, dtype=torch.bfloat16, device="meta")
     info = rmm.plan_info(Am, Bm, rho, full_path=full)
     assert info["gemm"] == kernel and (info["splits"] > 1) == split, info
-    check_linear(rmm, case, A, B64, rho, rows=rows, full_path=full)
+    check_linear(rmm, case, A, B64, rho, rows=None, full_path=full)
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
-def test_full_size_linear(rmm, name):
+def plan_of(rmm, case, rho):
+    torch = pytest.importorskip("torch")
+    Am = torch.empty(case.A.shape, dtype=torch.bfloat16, device="meta")
+    Bm = torch.empty(case.B.shape, dtype=torch.bfloat16, device="meta")
+    return rmm.plan_info(Am, Bm, rho)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_linear_every_row(rmm, name):
+    """The 8B-shaped projections at full size, every element of Y: c2 at
+    rho = 0.5, 0.7, 0.8, 1.0 (the A^T route; rho = 1 takes the shortcut) and
+    c3 at rho = 0.8 (the A^T route with split K); c3's other rho on rows."""
     case, A, B64 = linear_case(name)
-    rows = sample_rows(A.shape[0], 12, seed=7)
+    for rho in case.rhos:
+        if rho < 1.0:
+            assert plan_of(rmm, case, rho)["gemm"] == "tdma"
+        every = name == "c2" or rho == 0.8
+        check_linear(rmm, case, A, B64, rho, rows=None if every else sample_rows(A.shape[0], 12, seed=7))
+
+
+def test_full_size_linear_c5(rmm):
+    case, A, B64 = linear_case("c5")
+    n = A.shape[0]
+    rows = sorted(set(sample_rows(n, 192, seed=7)) | {n - 2})
     for rho in case.rhos:
         check_linear(rmm, case, A, B64, rho, rows=rows)
 
@@ -223,6 +247,34 @@ def test_decode(rmm, scale):
         Y_ref = oracle.reduced_product(a, B64, ref_idx)
         absprod = oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx)
         assert_close(to_host(Y), Y_ref, absprod, k, "bf16", f"decode rho={rho}")
+
+
+@pytest.mark.parametrize("d", [1001, 1004])
+def test_decode_row_length_not_a_multiple_of_eight(rmm, d):
+    """The decode route with d % 8 != 0 (row padded to a multiple of 8): the
+    selection reads the row's last 16-byte piece element by element, so the
+    last columns keep their values and the padding (huge values here, which
+    would win the TopK if read) is never scored."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(d)
+    m, ld = 64, 1008
+    a = synthetic.round_to_bf16((rng.standard_normal((1, d)) * np.exp(rng.standard_normal(d))).astype(np.float32))
+    a[0, -3:] = np.float32(64.0)  # the last columns must be kept
+    B = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
+    padded = np.full((1, ld), 3.0e4, np.float32)
+    padded[:, :d] = a
+    Ad = to_device(synthetic.round_to_bf16(padded), "bf16")[:, :d]
+    Bd = to_device(B, "bf16")
+    assert rmm.plan_info(Ad, Bd, 0.6)["route"] == "decode"
+    B64 = B.astype(np.float64)
+    for rho in (0.6, 1.0):
+        k = oracle.k_of(rho, d)
+        ref_idx = oracle.topk(np.abs(a[0]).astype(np.float64), k)
+        Y, idx = rmm.matmul(Ad, Bd, rho)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), rho
+        assert_close(to_host(Y), oracle.reduced_product(a, B64, ref_idx),
+                     oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx), k, "bf16", f"d={d} rho={rho}")
 
 
 def test_decode_exact_ties(rmm):

@@ -98,6 +98,28 @@ def test_full_size_decode(rmm, torch, fmt):
         check(rmm, torch, c.a, c.codes, c.scale, fmt, rho)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("d", [1001, 1004])
+def test_row_length_not_a_multiple_of_eight(rmm, torch, fmt, d):
+    """d % 8 != 0: the row's last 16-byte piece is read element by element;
+    the values stored after the row (huge, they would win the TopK if read)
+    are never scored."""
+    a, codes, scale = small_case(d, d, 64, fmt)
+    a[-2:] = np.float32(64.0)
+    trap = np.full(d + 15, 3.0e4, np.float32)
+    trap[:d] = a
+    ad = to_device(synthetic.round_to_bf16(trap), "bf16")[:d]
+    for rho in (0.6, 1.0):
+        y, idx = rmm.decode_wq(ad, torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda(), rho, fmt)
+        torch.cuda.synchronize()
+        ref = oracle.decode_wq(a, codes, fmt, scale, rho)
+        assert np.array_equal(idx.cpu().numpy(), ref.idx)
+        val = oracle.fp8_e4m3_value(codes) if fmt == "fp8" else oracle.int8_value(codes)
+        W = val * scale.astype(np.float64)[None, :]
+        absprod = oracle.reduced_product(np.abs(a).reshape(1, -1), np.abs(W), ref.idx)
+        assert_close(to_host(y).reshape(1, -1), ref.Y, absprod, ref.k, "bf16", f"{fmt} d={d} rho={rho}")
+
+
 def test_unsupported_shapes(rmm, torch):
     a = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rmm.RMMError):

@@ -36,6 +36,13 @@ def test_rmm_wrapper_and_diagnostics(oracle_mod):
     assert abs(dg["retained_energy"] - 294 / 324) < 1e-15
     assert abs(dg["prop1"] - (math.sqrt(10) + 12 * math.sqrt(2))) < 1e-13
     assert abs(dg["cor1"] - math.sqrt(30) * math.sqrt(20)) < 1e-12  # ||A_drop||_F^2 = 1+25+4, ||B_drop||_F^2 = 10+8+2
+    # eq. (17): eps_A, eps_B and the relative bound, worked by hand in the golden file
+    assert abs(dg["eps_A"] - 5 / 54) < 1e-15
+    assert abs(dg["eps_B"] - 20 / 27) < 1e-15
+    assert abs(dg["rel17"] - 10 / (27 * math.sqrt(2))) < 1e-15
+    assert abs(dg["normA_F"] - 18) < 1e-13 and abs(dg["normB_F"] - math.sqrt(27)) < 1e-13
+    rel_err = math.sqrt(g["rho05_error"]["frobenius_squared"]) / (dg["normA_F"] * dg["normB_F"])
+    assert rel_err <= dg["rel17"]
 
 
 def test_repeatable_and_thread_count_independent(oracle_mod):
@@ -87,3 +94,22 @@ def test_round_to_bf16_ties_to_even():
     assert r[2] == 1.0 + 2 ** -6       # halfway between 1+2^-7 and 1+2^-6: even is 1+2^-6
     assert r[3] == -2.5
     assert np.isfinite(r[4])
+
+
+def test_gap_fixup_of_the_gated_block(oracle_mod):
+    """After enforce_gap_mlp every requested boundary of the oracle's own h
+    (gated_mlp's h) has a relative gap of at least 1e-3, and only Wu changed."""
+    import synthetic
+    from oracle.fixup import enforce_gap_mlp
+
+    c = synthetic.make_mlp_case(dict(n=128, d=256, m=512), seed=3)
+    ks = [oracle_mod.k_of(r, 512) for r in (0.5, 0.7)]
+    Wu2, touched = enforce_gap_mlp(c.x, c.Wg, c.Wu, 0.8, ks)
+    assert touched > 0
+    assert np.array_equal(synthetic.round_to_bf16(Wu2), Wu2)
+    changed = np.any(Wu2 != c.Wu, axis=0)
+    assert 0 < changed.sum() < 512
+    res = oracle_mod.gated_mlp(c.x, c.Wg, Wu2, c.Wd, 0.8, 0.5)
+    s = np.sort(oracle_mod.colnorm(res.h))[::-1]
+    for k in ks:
+        assert (s[k - 1] - s[k]) / s[k - 1] >= 1e-3
