@@ -203,6 +203,29 @@ rmm_status_t rmm_matmul(const rmm_desc_t *desc, const void *A, const void *B, do
                         int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rmm_matmul for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same four steps, kernels and results, bit for bit, but with no workspace
+ * argument.  Its scratch memory is a fixed array of
+ * RMM_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * until the process ends; the call itself allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine).
+ *   desc, A, B, rho, Y, idx_out, stream   as for rmm_matmul
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or different host threads without ordering) race
+ * and give undefined results; calls ordered on one stream are safe.  The
+ * array keeps whatever the last call left there; nothing in it needs to
+ * start at zero.
+ * Errors: as for rmm_matmul, plus RMM_ERR_WORKSPACE when
+ * rmm_workspace_size(desc, rho) (for these pointers' alignment) exceeds
+ * RMM_NOALLOC_SCRATCH_BYTES, detected before anything is launched, and
+ * RMM_ERR_HIP when the array's device address cannot be looked up.
+ */
+#define RMM_NOALLOC_SCRATCH_BYTES (64u << 20)
+rmm_status_t rmm_matmul_noalloc(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,
+                                int32_t *idx_out, hipStream_t stream);
+
+/*
  * The reduced product over a caller-supplied kept set: steps 3-4 of
  * rmm_matmul with I given instead of selected.  This is the static variant
  * of the selection (Sec. 4, "Baselines": one subset of feature dimensions

@@ -689,6 +689,63 @@ rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const flo
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- entry point without allocations
+// rmm_matmul_noalloc takes its workspace from this array instead of the
+// caller: one copy per GPU, alive until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in, so its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[RMM_NOALLOC_SCRATCH_BYTES];
+
+namespace rmm {
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of the current device's scratch array (resolved on the
+// first call on that device).
+rmm_status_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_error = e;
+        return RMM_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kScratchDevices) return RMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_error = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return RMM_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RMM_OK;
+}
+}  // namespace
+}  // namespace rmm
+
+extern "C" rmm_status_t rmm_matmul_noalloc(const rmm_desc_t *desc, const void *A, const void *B, double rho, void *Y,
+                                           int32_t *idx_out, hipStream_t stream) {
+    int64_t extA, extB, extY;
+    rmm_status_t st = check_desc(desc, extA, extB, extY);
+    if (st != RMM_OK) return st;
+    if (!A || !B || !Y) return RMM_ERR_INVALID_ARG;
+    const int64_t k = k_of(rho, desc->d);
+    if (k < 1) return RMM_ERR_INVALID_ARG;
+    // the plan for these very pointers (their alignment picks the route) must fit the array
+    if (make_plan(desc, k, A, B, Y).total > (size_t)RMM_NOALLOC_SCRATCH_BYTES) return RMM_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != RMM_OK) return st;
+    return run_matmul(desc, A, B, k, nullptr, Y, idx_out, ws, (size_t)RMM_NOALLOC_SCRATCH_BYTES, stream, extA, extB,
+                      extY);
+}
+
 namespace rmm {
 
 namespace {
