@@ -71,6 +71,12 @@ WORKLOADS = {
     "c5-decode-int8": dict(case="c5", rho=0.8, sweep=(0.8, 1.0), wq="int8",
                            label="70B up projection decode over int8 weights with per-column scales: "
                                  "a 1x8192 bf16 x B 8192x28672 int8"),
+    "c5-fp8": dict(case="c5", rho=0.8, sweep=(0.5, 0.8, 1.0), wqgemm="fp8",
+                   label="70B up projection over FP8 E4M3 weights with per-column scales: A 4096x8192 bf16 x "
+                         "B 8192x28672 fp8"),
+    "c5-int8": dict(case="c5", rho=0.8, sweep=(0.5, 0.8, 1.0), wqgemm="int8",
+                    label="70B up projection over int8 weights with per-column scales: A 4096x8192 bf16 x "
+                          "B 8192x28672 int8"),
     "attn": dict(case="attn", rho=0.5, sweep=(0.5, 0.8, 1.0), attn=True,
                  label="causal attention with reduced scores, softmax fused: Q 32x4096x128, K/V 8 GQA heads "
                        "x4096x128 bf16"),
@@ -240,6 +246,62 @@ class WQRunner:
     def dense(self, i):
         # one weight copy: the dense GEMV streams all 470 MB of it, twice the MALL
         self.torch.matmul(self.a[i].view(1, -1), self.B16, out=self.Yd)
+
+
+class WQGemmRunner:
+    """The reduced product over 8-bit weights (rmm_matmul_wq) on the 70B up
+    projection; the dense comparison is the bf16 product over the unquantized
+    weights (hipBLASLt through torch.matmul)."""
+
+    def __init__(self, torch, rmm, fmt, copies):
+        import numpy as np
+        import synthetic
+        self.torch, self.rmm, self.fmt = torch, rmm, fmt
+        dev = torch.device("cuda:0")
+        base = synthetic.make_case("c5")
+        codes, scale = synthetic.quantize_columns(base.B, fmt)
+        self.A_host, self.codes_host, self.scale_host = base.A, codes, scale
+        self.sha256 = synthetic.sha256_of(synthetic.as_bf16_bits(base.A), codes, scale)
+
+        def up(x):
+            bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
+            return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+        A0, q0, s0 = up(base.A), torch.from_numpy(codes).to(dev), torch.from_numpy(scale).to(dev)
+        self.n, self.d = base.A.shape
+        self.m = codes.shape[1]
+        if copies is None:
+            copies = max(2, min(16, math.ceil(2 * MALL_BYTES / (A0.numel() * 2 + q0.numel()))))
+        self.copies = copies
+        self.A = [A0] + [A0.clone() for _ in range(copies - 1)]
+        self.Bq = [q0] + [q0.clone() for _ in range(copies - 1)]
+        self.scale = [s0] + [s0.clone() for _ in range(copies - 1)]
+        self.B16 = up(base.B)  # one copy: 470 MB, above the MALL on its own
+        self.batch, self.batched = 1, False
+        self.Y = [torch.empty((self.n, self.m), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+        self.ws, self.idx = {}, {}
+
+    def flops(self, rho):
+        return 2.0 * self.n * self.rmm.k_of(rho, self.d) * self.m
+
+    def call(self, i, rho, full_path=False):
+        import ctypes
+        torch, rmm = self.torch, self.rmm
+        key = (rho, False)
+        if key not in self.ws:
+            need = rmm.load().rmm_matmul_wq_workspace_size(self.n, self.d, self.m, rho)
+            if need == ctypes.c_size_t(-1).value:
+                raise rmm.RMMError(2, "rmm_matmul_wq_workspace_size")
+            self.ws[key] = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            self.idx[key] = torch.empty(rmm.k_of(rho, self.d), dtype=torch.int32, device="cuda:0")
+        rmm.matmul_wq(self.A[i], self.Bq[i], self.scale[i], rho, self.fmt, out=self.Y[i], idx_out=self.idx[key],
+                      workspace=self.ws[key])
+
+    def plan(self, rho):
+        return {"route": "mfma", "gemm": "tdma_" + self.fmt, "splits": 1}
+
+    def dense(self, i):
+        self.torch.matmul(self.A[i], self.B16, out=self.Y[i])
 
 
 class AttnRunner:
@@ -572,6 +634,49 @@ def cpu_baseline(runner, rho, budget_s=12.0, gpu=None):
             "seconds_measured": t_sel + t_rows + t_probe}
 
 
+def cpu_baseline_wqgemm(runner, rho, gpu, budget_s=12.0):
+    """The oracle's reduced product over 8-bit weights on this host: the
+    per-matrix part (codes decoded and scaled, norms, full-sort TopK) timed
+    whole, the triple-loop product on a sample of output rows, extrapolated
+    to all rows; plus the GPU's kept set and rows against it."""
+    import numpy as np
+    import oracle
+    threads = oracle.host_threads()
+    A, codes, scale = runner.A_host, runner.codes_host, runner.scale_host
+    n = A.shape[0]
+    t0 = time.perf_counter()
+    B = oracle.dequantize(codes, runner.fmt, scale)
+    sel = oracle.rmm(A, None, rho)
+    t_mat = time.perf_counter() - t0
+    k = sel.k
+    probe = max(threads, 8)
+    t0 = time.perf_counter()
+    oracle.reduced_product(A, B, sel.idx, 1.0, rows=list(range(probe)), threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(n, max(probe, probe * budget_s / max(t_probe, 1e-6))))
+    rows = max(threads, rows // threads * threads)
+    sample = np.sort(np.random.default_rng(0).choice(n, size=rows, replace=False))
+    t0 = time.perf_counter()
+    Y_ref = oracle.reduced_product(A, B, sel.idx, 1.0, rows=sample, threads=threads)
+    t_rows = time.perf_counter() - t0
+    total = t_mat + t_rows * n / rows
+    value = 2.0 * n * k * runner.m / total / 1e12
+    g_idx, g_Y = gpu
+    Y_got = g_Y[sample].astype(np.float64)
+    order = np.sort(sel.s)[::-1]
+    parity = {"idx_exact": bool(np.array_equal(g_idx, sel.idx)),
+              "rel_frobenius": float(np.linalg.norm(Y_got - Y_ref) / np.linalg.norm(Y_ref)),
+              "rows_compared": int(rows), "tolerance": 1e-2,
+              "boundary_rel_gap": float((order[k - 1] - order[k]) / order[k - 1]) if k < order.size else None,
+              "what": "GPU kept set vs the oracle's fp64 full-sort TopK; GPU output rows vs the oracle's fp64 "
+                      "rows over the dequantized weights"}
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "parity": parity,
+            "sample": f"fp64 oracle over {runner.fmt} weights: codes decoded and scaled, norms and full-sort TopK of "
+                      f"the {n}x{A.shape[1]} block ({t_mat:.2f} s), the product for {rows} of {n} rows "
+                      f"({t_rows:.2f} s), extrapolated to all rows",
+            "seconds_measured": t_mat + t_probe + t_rows}
+
+
 def cpu_baseline_attn(runner, rho, rows=256):
     """The oracle's attention for one head on a row sample (norms, TopK and
     the reduced scores of those rows, softmax, value product), scaled to the
@@ -663,7 +768,10 @@ def main(argv=None):
     is_mlp = wl.get("mlp", False)
     is_wq = "wq" in wl
     is_attn = wl.get("attn", False)
-    if is_mlp:
+    is_wqgemm = "wqgemm" in wl
+    if is_wqgemm:
+        runner = WQGemmRunner(torch, rmm, wl["wqgemm"], args.copies)
+    elif is_mlp:
         runner = MLPRunner(torch, rmm, args.copies)
     elif is_attn:
         runner = AttnRunner(torch, rmm, args.copies)
@@ -696,7 +804,7 @@ def main(argv=None):
             dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
             log(f"dense {'fused attention' if is_attn else 'torch.matmul'}: {dense_ms * 1e3:.1f} us/step")
         for r in wl["sweep"]:
-            for full in ((False, True) if r == 1.0 and not (is_mlp or is_wq or is_attn) else (False,)):
+            for full in ((False, True) if r == 1.0 and not (is_mlp or is_wq or is_attn or is_wqgemm) else (False,)):
                 t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
                                runner.copies, graph)
                 ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
@@ -778,6 +886,12 @@ def main(argv=None):
     if rank == 0 and not args.no_cpu_baseline and is_attn:
         cpu = cpu_baseline_attn(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+    elif rank == 0 and not args.no_cpu_baseline and is_wqgemm:
+        key = (rho, False)
+        runner.call(0, rho)
+        torch.cuda.synchronize()
+        cpu = cpu_baseline_wqgemm(runner, rho, (runner.idx[key].cpu().numpy(), runner.Y[0].float().cpu().numpy()))
+        log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads; parity {cpu['parity']}")
     elif rank == 0 and not args.no_cpu_baseline and is_wq:
         cpu = cpu_baseline_wq(runner, rho)
         log(f"cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")

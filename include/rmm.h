@@ -347,6 +347,33 @@ rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const flo
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The reduced product over 8-bit weights for any number of rows (weight-only
+ * quantization, W8A16): RMM on an activation block A and weights stored as
+ * 8-bit codes with one fp32 scale per output column, the combination App.
+ * B.6 evaluates on INT8-quantized Llama models and App. B.7 leaves to fused
+ * quantized kernels.
+ *   I = TopK(||A[:, j]||_2, k = rmm_k(rho, d))   (Sec. 3.2: from A alone)
+ *   Y[i, c] = alpha * scale[c] * sum_{t<k} A[i, I_t] * q[I_t, c]
+ * A: n x d bf16 row-major, leading dimension lda.  Bq: d x m codes, rows ldb
+ * bytes apart, fmt RMM_WQ_FP8_E4M3 or RMM_WQ_INT8 (as for rmm_decode_wq).
+ * scale: m fp32.  Y: n x m bf16, leading dimension ldy.  idx_out (k int32,
+ * ascending) may be NULL.  Every code is exact in bf16, so the kept rows are
+ * widened to bf16 inside the kernel and contracted on bf16 MFMA with fp32
+ * accumulation; scale[c] and alpha multiply the fp32 sum once and Y is
+ * rounded to nearest-even (bit-reproducible: fixed summation order).
+ * n = 1 runs rmm_decode_wq (the same result definition, |a_j| scores).
+ * Supported for n > 1: n, d, lda, ldy multiples of 8; m and ldb multiples
+ * of 16; d < 65535; A, Bq, Y and scale 16-byte aligned; A (and its
+ * transpose) and Bq under 2^31 bytes; otherwise RMM_ERR_UNSUPPORTED (the
+ * size query returns SIZE_MAX).  workspace: rmm_matmul_wq_workspace_size
+ * bytes, 256-byte aligned.  Errors otherwise as for rmm_decode_wq.
+ */
+size_t rmm_matmul_wq_workspace_size(int64_t n, int64_t d, int64_t m, double rho);
+rmm_status_t rmm_matmul_wq(const void *A, int64_t n, int64_t d, int64_t lda, const void *Bq, int32_t fmt,
+                           const float *scale, int64_t m, int64_t ldb, double rho, float alpha, void *Y, int64_t ldy,
+                           int32_t *idx_out, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Optional per-kernel timing for measurement tools.  While enabled, every
  * kernel rmm_matmul enqueues is bracketed by a pair of HIP events recorded
  * on the call's stream (at most `capacity` pairs are kept; later kernels are

@@ -23,7 +23,7 @@ __all__ = [
     "RMMError", "lib_path", "load", "k_of", "status_string", "version", "colnorm", "select", "matmul",
     "workspace_size", "timing_enable", "timing_collect", "KERNEL_KINDS", "F32", "BF16", "FLAG_FULL_PATH",
     "matmul_indexed", "plan_info", "gated_weights", "gated_mlp", "decode_wq", "WQ_FORMATS", "attention",
-    "check_out", "calibrate_mfma",
+    "check_out", "calibrate_mfma", "matmul_wq",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +124,11 @@ def load():
     L.rmm_decode_wq_workspace_size.restype = sz
     L.rmm_decode_wq.argtypes = [vp, vp, i32, vp, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, vp, vp, sz, vp]
     L.rmm_decode_wq.restype = ctypes.c_int
+    L.rmm_matmul_wq_workspace_size.argtypes = [i64, i64, i64, ctypes.c_double]
+    L.rmm_matmul_wq_workspace_size.restype = sz
+    L.rmm_matmul_wq.argtypes = [vp, i64, i64, i64, vp, i32, vp, i64, i64, ctypes.c_double, ctypes.c_float, vp, i64,
+                                vp, vp, sz, vp]
+    L.rmm_matmul_wq.restype = ctypes.c_int
     L.rmm_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_double]
     L.rmm_attention_workspace_size.restype = sz
     L.rmm_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_double, i32, vp, vp, vp, sz, vp]
@@ -524,6 +529,50 @@ def decode_wq(a, Bq, scale, rho: float, fmt: str = "fp8", *, alpha: float = 1.0,
     st = L.rmm_decode_wq(a.data_ptr(), Bq.data_ptr(), WQ_FORMATS[fmt], scale.data_ptr(), d, m, Bq.stride(0),
                          float(rho), float(alpha), out.data_ptr(), idx_out.data_ptr(), _ptr(ws), wsb, _stream(a))
     _check(st, "rmm_decode_wq")
+    return out, idx_out
+
+
+def matmul_wq(A, Bq, scale, rho: float, fmt: str = "fp8", *, alpha: float = 1.0, out=None, idx_out=None,
+              workspace=None):
+    """Y = alpha * A[:, I] (value(Bq) * scale)[I, :] with I = TopK(||A[:, j]||, ceil(rho d))
+    (rmm_matmul_wq: 8-bit weights with one fp32 scale per column, any n).
+
+    A: bf16 (n, d) with unit column stride; Bq: (d, m) 8-bit codes (uint8,
+    int8 or float8_e4m3fn storage; ``fmt`` "fp8" = OCP E4M3, "int8") with
+    unit column stride; scale: fp32 (m,).  Returns (Y, idx): Y bf16 (n, m),
+    idx int32 (k,) ascending."""
+    torch = _torch()
+    _require_gpu(A, Bq, scale)
+    L = load()
+    if fmt not in WQ_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(WQ_FORMATS)}")
+    if A.dtype != torch.bfloat16 or A.dim() != 2 or A.stride(1) != 1:
+        raise ValueError("A must be a bf16 matrix with unit column stride")
+    n, d = A.shape
+    if Bq.element_size() != 1 or Bq.dim() != 2 or Bq.shape[0] != d or Bq.stride(1) != 1:
+        raise ValueError("Bq must be (d, m) 8-bit codes with unit column stride")
+    m = Bq.shape[1]
+    if scale.dtype != torch.float32 or scale.numel() != m or not scale.is_contiguous():
+        raise ValueError("scale must be m contiguous fp32 values")
+    if Bq.device != A.device or scale.device != A.device:
+        raise ValueError("A, Bq and scale must live on one device")
+    need = L.rmm_matmul_wq_workspace_size(n, d, m, float(rho))
+    if need == ctypes.c_size_t(-1).value:
+        raise RMMError(2, "rmm_matmul_wq_workspace_size")
+    k = int(L.rmm_k(float(rho), d))
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.bfloat16, device=A.device)
+    elif tuple(out.shape) != (n, m) or out.dtype != torch.bfloat16 or out.stride(1) != 1 or out.device != A.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    if idx_out is None:
+        idx_out = torch.empty(k, dtype=torch.int32, device=A.device)
+    else:
+        check_out(idx_out, (k,), torch.int32, A.device, "idx_out")
+    ws, wsb = _user_workspace(workspace, need, A.device)
+    st = L.rmm_matmul_wq(A.data_ptr(), n, d, A.stride(0), Bq.data_ptr(), WQ_FORMATS[fmt], scale.data_ptr(), m,
+                         Bq.stride(0), float(rho), float(alpha), out.data_ptr(), out.stride(0), idx_out.data_ptr(),
+                         _ptr(ws), wsb, _stream(A))
+    _check(st, "rmm_matmul_wq")
     return out, idx_out
 
 

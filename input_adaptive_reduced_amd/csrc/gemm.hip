@@ -43,6 +43,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 constexpr int BK = 64;  // K step: 64 bf16 = eight 16-byte chunks per LDS row
 constexpr int kBdmaListRows = 16384;  // u16 list entries gemm_bdma_kernel keeps in LDS
 constexpr int kTdmaListRows = 8192;   // u16 list entries gemm_tdma_kernel keeps in LDS
+constexpr int kTdmaListRowsQ = 32768; // the same with 8-bit B (its stages take half the LDS)
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
@@ -378,45 +379,103 @@ __global__ __launch_bounds__(WM *WN * 64, 1) void gemm_bf16_kernel(GemmArgs g) {
 // c ^ (r % 16)) so every global store is a full 16-byte piece and each
 // 16-lane group writes 256 contiguous bytes of a row.  The caller has made
 // sure no wave still reads operands from `stage`.
-template <bool SPLIT>
+// Output of a 256x256 tile: lane l of wave (wm, wn) holds, for each
+// (i, j, q), four consecutive columns n0 + 128 wn + 32 j + 8 q + 4 (l / 32)
+// of row m0 + 128 wm + 32 i + l % 32.  With SPLIT the fp32 partials go to
+// part[split] (alpha is applied by the reduce); otherwise the tile is
+// rounded to bf16, staged in LDS and written in 16-byte row pieces.  With
+// SCALED (8-bit weights) every column c is multiplied by colscale[c] too:
+// the scale of the dequantized weight column, applied once to the fp32 sum.
+template <bool SPLIT, bool SCALED = false>
 __device__ __forceinline__ void store_tile_256(const GemmArgs &g, const f32x16_t (&acc)[4][4], uint4 *stage,
                                                int64_t m0, int64_t n0, int64_t b, int split, int wm, int wn,
                                                int lane) {
     constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+    // factors of the four columns of (j, q): alpha (not with SPLIT) times the column scales
+    auto factors = [&](int j, int q, float (&f)[4]) {
+        const float a = SPLIT ? 1.f : g.alpha;
+        if constexpr (SCALED) {
+            const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+            const float4 v = col < g.m ? *reinterpret_cast<const float4 *>(g.colscale + col)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+            f[0] = a * v.x;
+            f[1] = a * v.y;
+            f[2] = a * v.z;
+            f[3] = a * v.w;
+        } else {
+            f[0] = f[1] = f[2] = f[3] = a;
+        }
+    };
     if constexpr (SPLIT) {
         (void)stage;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
-            if (row >= g.n) continue;
+        if constexpr (SCALED) {
+            // scale loads per (j, q), reused over the four row blocks
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
                     if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
-                    *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m + col) =
-                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    float f[4];
+                    factors(j, q, f);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+                        if (row >= g.n) continue;
+                        *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m + col) =
+                            make_float4(f[0] * acc[i][j][4 * q], f[1] * acc[i][j][4 * q + 1],
+                                        f[2] * acc[i][j][4 * q + 2], f[3] * acc[i][j][4 * q + 3]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int64_t row = m0 + wm * WTM + i * 32 + (lane & 31);
+                if (row >= g.n) continue;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t col = n0 + wn * WTN + j * 32 + q * 8 + (lane >> 5) * 4;
+                        if (col >= g.m) continue;  // m % 8 == 0: the four columns are all in or all out
+                        *reinterpret_cast<float4 *>(g.part + (((int64_t)split * g.batch + b) * g.n + row) * g.m +
+                                                    col) =
+                            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                        acc[i][j][4 * q + 3]);
+                    }
                 }
             }
         }
     } else {
         constexpr int CPW = WTN / 8;
         char *st = reinterpret_cast<char *>(stage);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        auto stage_one = [&](int i, int j, int q, const float (&f)[4]) {
             const int r = i * 32 + (lane & 31);
+            const int c4 = j * 8 + q * 2 + (lane >> 5);
+            const uint32_t lo = pack_bf16x2(f[0] * acc[i][j][4 * q], f[1] * acc[i][j][4 * q + 1]);
+            const uint32_t hi = pack_bf16x2(f[2] * acc[i][j][4 * q + 2], f[3] * acc[i][j][4 * q + 3]);
+            const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
+            *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
+        };
+        if constexpr (SCALED) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int c4 = j * 8 + q * 2 + (lane >> 5);
-                    const uint32_t lo = pack_bf16x2(g.alpha * acc[i][j][4 * q], g.alpha * acc[i][j][4 * q + 1]);
-                    const uint32_t hi = pack_bf16x2(g.alpha * acc[i][j][4 * q + 2], g.alpha * acc[i][j][4 * q + 3]);
-                    const int chunk = (c4 >> 1) ^ (r & (CPW - 1));
-                    *reinterpret_cast<uint2 *>(st + (r * CPW + chunk) * 16 + (c4 & 1) * 8) = make_uint2(lo, hi);
+                    float f[4];
+                    factors(j, q, f);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) stage_one(i, j, q, f);
                 }
-            }
+        } else {
+            const float f[4] = {g.alpha, g.alpha, g.alpha, g.alpha};
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) stage_one(i, j, q, f);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staging writes are done
         __builtin_amdgcn_wave_barrier();
@@ -918,6 +977,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
     store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
+// Eight 8-bit weight codes (k-consecutive, as ds_read_b64_tr_b8 delivers
+// them for one column) widened to the bf16 MFMA operand.  Both formats are
+// exact in bf16: an E4M3 value has at most 4 significant bits and an
+// exponent in [-9, 8]; an int8 value at most 8 significant bits.  FP8 uses
+// gfx950's packed conversion (scale 1); int8 converts each sign-extended
+// byte to fp32 and packs pairs (round-to-nearest-even, exact here).
+template <int BQ>
+__device__ __forceinline__ bf16x8_t codes_to_bf16x8(uint32_t lo, uint32_t hi) {
+    if constexpr (BQ == 1) {
+        const rmm_bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+        const rmm_bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+        const rmm_bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+        const rmm_bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+        return as_bf16x8(make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)));
+    } else {
+        const int32_t x = (int32_t)lo, y = (int32_t)hi;
+        return as_bf16x8(make_uint4(
+            pack_bf16x2((float)(int8_t)x, (float)(int8_t)(x >> 8)), pack_bf16x2((float)(int8_t)(x >> 16), (float)(x >> 24)),
+            pack_bf16x2((float)(int8_t)y, (float)(int8_t)(y >> 8)), pack_bf16x2((float)(int8_t)(y >> 16), (float)(y >> 24))));
+    }
+}
+
 // Reduced product with both operands gathered by rows through LDS: A^T
 // (the activation block transposed, d x n, written by the column-norm pass)
 // supplies rows A^T[I_t, :] exactly as B supplies rows B[I_t, :], so neither
@@ -944,17 +1026,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
 // such rows read as zero).  Per K step it is as fast as the A-direct kernel
 // on a 4096 x 4096 x 4096 projection and 2-4% faster than gemm_bdma_kernel
 // on a 2048 x 14336 x 4096 one, without the pack pass either needs.
-template <bool SPLIT, int EPI>
+template <bool SPLIT, int EPI, int BQ = 0>
 __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
+    static_assert(BQ == 0 || EPI == 0, "8-bit weights with the plain epilogue only");
     constexpr int BM = 256, BN = 256, WTM = 128, WTN = 128;
     constexpr int FM = 4, FN = 4;
     constexpr int CPR = 32;
     constexpr int BUF = BK * CPR;  // uint4 per stage (32 KB)
+    // 8-bit B: 64 rows x 256 codes per stage (16 KB); the list then takes the
+    // LDS left (64 KB), which also stages waves 2 and 3 in the epilogue.
+    // Separate arrays, so the compiler can tell the LDS-DMA writes of one
+    // stage from the reads of another and need not wait between them.
+    constexpr int BUFB = BQ ? BUF / 2 : BUF;
     __shared__ uint4 sA0[BUF];
     __shared__ uint4 sA1[BUF];
-    __shared__ uint4 sB0[BUF];
-    __shared__ uint4 sB1[BUF];
-    __shared__ __align__(16) uint16_t sIdx[kTdmaListRows];
+    __shared__ uint4 sB0[BUFB];
+    __shared__ uint4 sB1[BUFB];
+    __shared__ __align__(16) uint16_t sIdx[BQ ? kTdmaListRowsQ : kTdmaListRows];
     typedef __attribute__((address_space(3))) void lds_t;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
@@ -974,7 +1062,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     const int kt1 = min(KT, kt0 + per);
     const int kte = kt0 + (max(kt1 - kt0, 0) + 1) / 2 * 2;
     const uint32_t lda2 = (uint32_t)(g.lda * 2), ma2 = (uint32_t)(m0 * 2);
-    const uint32_t ldb2 = (uint32_t)(g.ldb * 2), nb2 = (uint32_t)(n0 * 2);
+    constexpr uint32_t BE = BQ ? 1u : 2u;  // bytes per B element
+    const uint32_t ldb2 = (uint32_t)(g.ldb * BE), nb2 = (uint32_t)(n0 * BE);
     const int hsel = lane >> 5, pos = lane & 31;
 
     auto load_rows = [&](int kt, uint32_t (&o)[8]) {
@@ -1016,6 +1105,47 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
             f[j] = u.v;
         }
     };
+    // 8-bit B: a stage holds the step's 64 kept rows x 256 codes (16 KB), the
+    // 16-byte chunk c of row k at c ^ (k & 7).  A wave fills 16 rows with four
+    // LDS-DMA loads of 1 KB (four rows each: lane l fetches chunk
+    // (l & 15) ^ (k & 7) of row 4i + l / 16 of its 16).
+    auto load_rows_q = [&](int kt, uint32_t (&o)[4]) {
+        const int t0 = (kt - kt0) * BK + 16 * w;
+        const uint4 v0 = *reinterpret_cast<const uint4 *>(sIdx + t0);
+        const uint4 v1 = *reinterpret_cast<const uint4 *>(sIdx + t0 + 8);
+        const int gg = lane >> 4;  // entry 4i + gg of the wave's 16
+        const uint32_t sh = (gg & 1) ? 16u : 0u;
+        o[0] = ((gg >> 1) ? v0.y : v0.x) >> sh & 0xffffu;
+        o[1] = ((gg >> 1) ? v0.w : v0.z) >> sh & 0xffffu;
+        o[2] = ((gg >> 1) ? v1.y : v1.x) >> sh & 0xffffu;
+        o[3] = ((gg >> 1) ? v1.w : v1.z) >> sh & 0xffffu;
+    };
+    auto dma_q = [&](uint4 *dst, const uint32_t (&r4)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kr = 16 * w + 4 * i + (lane >> 4);
+            const uint32_t c = (uint32_t)((lane & 15) ^ (kr & 7));
+            const uint32_t row = r4[i];
+            const uint32_t off = (row * ldb2 + nb2 + c * 16u) | (row == 0xffffu ? kOob : 0u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_t *)&dst[(16 * w + 4 * i) * 16], 16, off, 0, 0, 0);
+        }
+    };
+    // B fragments of sub-step ks from an 8-bit stage: one transposed 8-byte
+    // read per fragment (lane i of a 16-lane group addresses row i / 2, eight
+    // columns 8 (i & 1) of the group's 16; lane j then holds column j's eight
+    // codes), the raw codes kept for codes_to_bf16x8
+    auto read_q = [&](const uint4 *stg, int ks, int base, uint2 (&f)[4]) {
+        const int gq = lane >> 4, li = lane & 15;
+        const int k = ks * 16 + 8 * (gq >> 1) + (li >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = base + j * 32 + 16 * (gq & 1) + 8 * (li & 1);
+            const char *p = reinterpret_cast<const char *>(stg) + k * 256 + (((col >> 4) ^ (k & 7)) << 4) + (col & 15);
+            typedef int v2i_t __attribute__((ext_vector_type(2)));
+            const v2i_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t *)p);
+            f[j] = make_uint2((uint32_t)v.x, (uint32_t)v.y);
+        }
+    };
     auto stA = [&](auto Sc) -> uint4 * {
         if constexpr (decltype(Sc)::value % 2 == 0) return sA0; else return sA1;
     };
@@ -1032,6 +1162,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     bf16x8_t fa[2][FM], fb[2][FN];
+    uint2 fq[2][FN];  // 8-bit B: raw codes of the fragments
     uint32_t rows[8];
 
     auto step = [&](int kt, auto Sc) {
@@ -1046,23 +1177,59 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) next[i] = rows[i];
         load_rows(kt + 2, rows);
+        uint32_t nextq[4];  // 8-bit B: rows of step kt+1 in the layout of dma_q
+        if constexpr (BQ != 0) load_rows_q(kt + 1, nextq);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks < 3) {
-                read_tr(cB, ks + 1, wn * WTN, fb[(ks + 1) & 1]);
+                if constexpr (BQ != 0)
+                    read_q(cB, ks + 1, wn * WTN, fq[(ks + 1) & 1]);
+                else
+                    read_tr(cB, ks + 1, wn * WTN, fb[(ks + 1) & 1]);
                 read_tr(cA, ks + 1, wm * WTM, fa[(ks + 1) & 1]);
             } else {
-                read_tr(oB, 0, wn * WTN, fb[0]);
+                if constexpr (BQ != 0)
+                    read_q(oB, 0, wn * WTN, fq[0]);
+                else
+                    read_tr(oB, 0, wn * WTN, fb[0]);
                 read_tr(oA, 0, wm * WTM, fa[0]);
             }
-            if (ks == 0) dma(rB, ldb2, nb2, dB, 0, 8, next);
+            if (ks == 0) {
+                if constexpr (BQ != 0)
+                    dma_q(dB, nextq);
+                else
+                    dma(rB, ldb2, nb2, dB, 0, 8, next);
+            }
             if (ks == 3) dma(rA, lda2, ma2, dA, 0, 8, rows);
+            if constexpr (BQ != 0) {
+                // fragment j widened just before its four MFMAs
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int j = 0; j < FN; ++j) {
+                    const bf16x8_t bj = codes_to_bf16x8<BQ>(fq[ks & 1][j].x, fq[ks & 1][j].y);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
-            if (ks == 0 || ks == 3) {
+                    for (int i = 0; i < FM; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bj, fa[ks & 1][i], acc[i][j], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+            }
+            if constexpr (BQ != 0) {
+                // per MFMA: the conversions of the next fragment, an LDS read, and in
+                // sub-steps 0 and 3 an LDS-DMA load (four of B in 0, eight of A in 3)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, BQ == 1 ? 1 : 3, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
+                    if (ks == 3 && q < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    if (ks == 0 && q < 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            } else if (ks == 0 || ks == 3) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -1097,13 +1264,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
         // steps kt0 (both operands) and kt0+1 (A; its B is loaded in step kt0's sub-step 0)
         load_rows(kt0, rows);
         dma(rA, lda2, ma2, sA0, 0, 8, rows);
-        dma(rB, ldb2, nb2, sB0, 0, 8, rows);
+        if constexpr (BQ != 0) {
+            uint32_t r4[4];
+            load_rows_q(kt0, r4);
+            dma_q(sB0, r4);
+        } else {
+            dma(rB, ldb2, nb2, sB0, 0, 8, rows);
+        }
         load_rows(kt0 + 1, rows);
         dma(rA, lda2, ma2, sA1, 0, 8, rows);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_tr(sB0, 0, wn * WTN, fb[0]);
+        if constexpr (BQ != 0)
+            read_q(sB0, 0, wn * WTN, fq[0]);
+        else
+            read_tr(sB0, 0, wn * WTN, fb[0]);
         read_tr(sA0, 0, wm * WTM, fa[0]);
         for (int kt = kt0; kt < kte; kt += 2) {
             step(kt, std::integral_constant<int, 0>{});
@@ -1112,11 +1288,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_s_waitcnt(0x0070);
     __syncthreads();
-    uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : w == 2 ? sB0 : sB1;
+    static_assert(BQ == 0 || kTdmaListRowsQ * 2 >= 2 * BUF * 16, "the list region stages two 32 KB tiles");
+    uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : BQ ? reinterpret_cast<uint4 *>(sIdx) + (w - 2) * BUF
+                                                    : w == 2 ? sB0 : sB1;
     if constexpr (EPI == 1)
         store_tile_swiglu(g, acc, stage, m0, n0 / 2 + wn * 64, tm, wm, lane);
     else
-        store_tile_256<SPLIT>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
+        store_tile_256<SPLIT, BQ != 0>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }
 
 // Reduced product with a narrow output (m <= 128) whose kept A columns are
@@ -1979,14 +2157,14 @@ static bool bdma_ok(int64_t kpad, int splits, int64_t d, int transB) {
 
 // The two-operand LDS-DMA kernel keeps the list of a split's K range (plus
 // the two steps loaded past it) in 16 KB.
-static bool tdma_ok(int64_t kpad, int splits, int64_t d) {
+static bool tdma_ok(int64_t kpad, int splits, int64_t d, int bq = 0) {
     if (d >= 0xffff) return false;
     const int64_t KT = kpad / BK;
     const int64_t per = std::min<int64_t>(((KT + splits - 1) / splits + 1) & ~1LL, KT);
-    return (per + 2) * BK <= kTdmaListRows;
+    return (per + 2) * BK <= (bq ? kTdmaListRowsQ : kTdmaListRows);
 }
 
-bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d) { return tdma_ok(kpad, splits, d); }
+bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d, int bq) { return tdma_ok(kpad, splits, d, bq); }
 
 GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d) {
     GemmConfig c = gemm_choose_tile(n, m, k, 1);
@@ -2084,10 +2262,25 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         return hipGetLastError();
     }
     if (c.tile == 5) {
-        if (a.bmode != 0 || a.batch != 1 || !tdma_ok(a.kpad, a.splits, 0)) return hipErrorInvalidValue;
+        if (a.bmode != 0 || a.batch != 1 || !tdma_ok(a.kpad, a.splits, 0, a.bq)) return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
         dim3 grid((unsigned)tiles, (unsigned)a.splits, 1);
-        if (a.epi == 1) {
+        if (a.bq != 0) {
+            // 8-bit B: rows of m codes (16-byte pieces), one fp32 scale per column
+            if (a.epi != 0 || a.bq > 2 || !a.colscale || a.m % 16 || a.ldb % 16 || ((uintptr_t)a.colscale & 15))
+                return hipErrorInvalidValue;
+            if (a.bq == 1) {
+                if (a.splits > 1)
+                    gemm_tdma_kernel<true, 0, 1><<<grid, 256, 0, stream>>>(a);
+                else
+                    gemm_tdma_kernel<false, 0, 1><<<grid, 256, 0, stream>>>(a);
+            } else {
+                if (a.splits > 1)
+                    gemm_tdma_kernel<true, 0, 2><<<grid, 256, 0, stream>>>(a);
+                else
+                    gemm_tdma_kernel<false, 0, 2><<<grid, 256, 0, stream>>>(a);
+            }
+        } else if (a.epi == 1) {
             // SwiGLU needs whole sums: one K range; the interleaved operand is 2 x (outputs) wide
             if (a.splits != 1 || a.m % 64 != 0 || (a.Y && a.ldy < a.m / 2) || (a.Yt && (!a.npart || a.n % 8)) ||
                 (!a.Y && !a.Yt))

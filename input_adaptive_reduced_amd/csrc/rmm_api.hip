@@ -689,6 +689,130 @@ rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const flo
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- reduced product over 8-bit weights
+namespace rmm {
+namespace {
+struct WqPlan {
+    int64_t k, kpad;
+    ColnormPlan cp;
+    GemmConfig gc;
+    size_t off_part, off_s, off_idx, off_At, off_gpart, total;
+};
+
+// n > 1: the transposing norm pass, the selection, then the two-operand GEMM
+// over rows of A^T and 8-bit rows of B (one K range per split).
+rmm_status_t wq_plan(int64_t n, int64_t d, int64_t m, double rho, WqPlan &p) {
+    memset(&p, 0, sizeof(p));
+    if (n < 2 || d < 1 || m < 1) return RMM_ERR_INVALID_ARG;
+    p.k = k_of(rho, d);
+    if (p.k < 1) return RMM_ERR_INVALID_ARG;
+    if (n % 8 || d % 8 || m % 16 || d >= 0xffff || n > INT32_MAX / 2 || m > INT32_MAX / 2 ||
+        n * d * 2 >= kMaxBufferBytes)
+        return RMM_ERR_UNSUPPORTED;
+    p.kpad = (p.k + 127) / 128 * 128;
+    p.gc = gemm_choose_transposed(n, m, p.k, d);
+    if (p.gc.tile != 5) {
+        // few tiles or few K steps: the same kernel, its K range split as the chooser asks
+        p.gc.tile = 5;
+        if (p.gc.splits < 1) p.gc.splits = 1;
+    }
+    while (!gemm_tdma_fits(p.kpad, p.gc.splits, d, 1) && p.gc.splits < 64) ++p.gc.splits;
+    if (!gemm_tdma_fits(p.kpad, p.gc.splits, d, 1)) return RMM_ERR_UNSUPPORTED;
+    p.cp = colnorm_transpose_plan(n, d);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    p.off_part = take((size_t)p.cp.chunks * d * 4);
+    p.off_s = take((size_t)d * 4);
+    p.off_idx = take((size_t)p.kpad * 4);
+    p.off_At = take((size_t)d * n * 2);
+    if (p.gc.splits > 1) p.off_gpart = take((size_t)p.gc.splits * n * m * 4);
+    p.total = off;
+    return RMM_OK;
+}
+}  // namespace
+}  // namespace rmm
+
+extern "C" size_t rmm_matmul_wq_workspace_size(int64_t n, int64_t d, int64_t m, double rho) {
+    if (n == 1) return rmm_decode_wq_workspace_size(d, m, rho);
+    WqPlan p;
+    return wq_plan(n, d, m, rho, p) == RMM_OK ? p.total : SIZE_MAX;
+}
+
+extern "C" rmm_status_t rmm_matmul_wq(const void *A, int64_t n, int64_t d, int64_t lda, const void *Bq, int32_t fmt,
+                                      const float *scale, int64_t m, int64_t ldb, double rho, float alpha, void *Y,
+                                      int64_t ldy, int32_t *idx_out, void *workspace, size_t ws_bytes,
+                                      hipStream_t stream) {
+    if (!A || !Bq || !scale || !Y || (fmt != RMM_WQ_FP8_E4M3 && fmt != RMM_WQ_INT8) || n < 1 || d < 1 || m < 1 ||
+        lda < d || ldb < m || ldy < m || !isfinite(alpha))
+        return RMM_ERR_INVALID_ARG;
+    if (n == 1)  // a single row: the decode route (ranking |a_j|, the gathered 8-bit GEMV)
+        return rmm_decode_wq(A, Bq, fmt, scale, d, m, ldb, rho, alpha, Y, idx_out, workspace, ws_bytes, stream);
+    WqPlan p;
+    rmm_status_t st = wq_plan(n, d, m, rho, p);
+    if (st != RMM_OK) return st;
+    const int64_t ab = ((n - 1) * lda + d) * 2, bb = (d - 1) * ldb + m, sb = m * 4, yb = ((n - 1) * ldy + m) * 2;
+    if (lda % 8 || ldy % 8 || ldb % 16 || !aligned16(A) || !aligned16(Bq) || !aligned16(Y) || !aligned16(scale) ||
+        ab >= kMaxBufferBytes || bb >= kMaxBufferBytes)
+        return RMM_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < p.total) return RMM_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return RMM_ERR_INVALID_ARG;
+    char *ws = static_cast<char *>(workspace);
+    const int64_t wb = (int64_t)p.total;
+    if (overlaps(Y, yb, A, ab) || overlaps(Y, yb, Bq, bb) || overlaps(Y, yb, scale, sb) || overlaps(ws, wb, A, ab) ||
+        overlaps(ws, wb, Bq, bb) || overlaps(ws, wb, scale, sb) || overlaps(ws, wb, Y, yb) ||
+        (idx_out && (overlaps(idx_out, p.k * 4, Y, yb) || overlaps(idx_out, p.k * 4, ws, wb) ||
+                     overlaps(idx_out, p.k * 4, A, ab) || overlaps(idx_out, p.k * 4, Bq, bb))))
+        return RMM_ERR_INVALID_ARG;
+    float *part = reinterpret_cast<float *>(ws + p.off_part);
+    float *s = reinterpret_cast<float *>(ws + p.off_s);
+    int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);
+    uint16_t *At = reinterpret_cast<uint16_t *>(ws + p.off_At);
+    // steps 1-2 on A alone (the set does not depend on the weights), A^T for the row gathers
+    RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_transpose(A, n, d, lda, p.cp, At, n, part, stream));
+    if (norm_select_ok(p.cp.chunks, d)) {
+        RMM_LAUNCH(RMM_KERNEL_SELECT, launch_norm_select(part, p.cp.chunks, d, 1, p.k, idx_out, p.k, pidx, p.kpad,
+                                                         stream));
+    } else {
+        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, d, 1, s, stream));
+        RMM_LAUNCH(RMM_KERNEL_SELECT,
+                   launch_select(s, nullptr, RMM_F32, 0, 1, d, p.k, idx_out, p.k, pidx, p.kpad, nullptr, stream));
+    }
+    // steps 3-4: kept rows of A^T and of the codes, widened to bf16 in the kernel, scaled per column
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.A = At;
+    g.lda = n;
+    g.a_bytes = d * n * 2;
+    g.B = static_cast<const uint16_t *>(Bq);
+    g.ldb = ldb;
+    g.b_bytes = bb;
+    g.group = 1;
+    g.bmode = 0;
+    g.idx = pidx;
+    g.ld_idx = p.kpad;
+    g.Y = static_cast<uint16_t *>(Y);
+    g.ldy = ldy;
+    g.n = n;
+    g.m = m;
+    g.k = p.k;
+    g.kpad = p.kpad;
+    g.batch = 1;
+    g.alpha = alpha;
+    g.splits = p.gc.splits;
+    g.part = p.gc.splits > 1 ? reinterpret_cast<float *>(ws + p.off_gpart) : nullptr;
+    g.bq = fmt == RMM_WQ_FP8_E4M3 ? 1 : 2;
+    g.colscale = scale;
+    RMM_LAUNCH(RMM_KERNEL_GEMM, launch_gemm_bf16(g, p.gc, stream));
+    if (p.gc.splits > 1)  // the partials already carry the column scales
+        RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(g.part, p.gc.splits, n, m, 1, alpha,
+                                                           static_cast<uint16_t *>(Y), ldy, 0, stream));
+    return RMM_OK;
+}
+
 // ---------------------------------------------------------------- entry point without allocations
 // rmm_matmul_noalloc takes its workspace from this array instead of the
 // caller: one copy per GPU, alive until the process ends.  In host code the

@@ -139,6 +139,9 @@ struct GemmArgs {
     int epi;             // tile 5 only: 0 = Y, 1 = SwiGLU of interleaved gate/up column blocks (see gemm.hip)
     uint16_t *Yt;        // epi 1: h^T (m/2 x n, rows n apart), or NULL
     float *npart;        // epi 1 with Yt: column sums of h^2 per 128-row chunk [chunk][m/2]
+    int bq;              // tile 5 only: B element format, 0 = bf16, 1 = OCP FP8 E4M3 codes, 2 = int8 codes
+                         // (8-bit B: ldb in bytes, rows of m codes; b_bytes in bytes)
+    const float *colscale;  // bq != 0: one fp32 scale per output column (Y = alpha * scale[c] * sum)
 };
 struct GemmConfig {
     int tile;    // 0: 256x256, 1: 128x128, 2: 256x256 with A in operand blocks (A-direct),
@@ -158,8 +161,9 @@ GemmConfig gemm_choose(int64_t n, int64_t m, int64_t k, int64_t batch, int64_t d
 // or tile -1 when the shape does not suit it.
 GemmConfig gemm_choose_transposed(int64_t n, int64_t m, int64_t k, int64_t d);
 // Whether tile 5 can run a K range of kpad padded entries in `splits` splits
-// (its kept-row list must fit in LDS) for contraction length d.
-bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d);
+// (its kept-row list must fit in LDS) for contraction length d; bq != 0: with
+// 8-bit B, whose smaller stages leave room for a longer list.
+bool gemm_tdma_fits(int64_t kpad, int splits, int64_t d, int bq = 0);
 hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t stream);
 // Gate and up weights of a gated MLP (d x m each; stored m x d, the nn.Linear
 // layout, when `transposed`) interleaved in 32-column blocks into one d x 2m
