@@ -11,9 +11,9 @@ Cache.  Other workloads (the 8B projections, attention, decode, the gated
 MLP block) are selected with --workload.
 
 The same JSON line carries
-  * ``median_ms_per_step``: the median of per-step event times from a second
-    pass of the same K steps (``ms_per_step`` is the mean of the bracketed
-    pass that ``value`` comes from);
+  * ``median_ms_per_step``: from a second pass of the same K steps, the
+    median over ten chunks of each chunk's mean ms per step (``ms_per_step``
+    is the mean of the bracketed pass that ``value`` comes from);
   * ``sweep``: the path at each rho of the workload (and rho = 1 with the
     full path forced) with the dense bf16 torch.matmul (hipBLASLt) time and
     the speedup over it;
@@ -479,18 +479,24 @@ class _Null:
         return False
 
 
-def step_median(torch, fn, steps, copies, graph_runs=None):
-    """Median ms per step from events recorded between consecutive steps (a
-    separate pass: the event records sit between the steps)."""
+def step_median(torch, fn, steps, copies, graph_runs=None, chunks=10):
+    """Median over ``chunks`` consecutive chunks of the K steps of the mean
+    ms per step in each chunk (a separate pass; events sit only between
+    chunks, so short steps are not inflated by per-step event records)."""
     run = graph_runs if graph_runs is not None else (lambda i: fn(i % copies))
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    chunks = max(1, min(chunks, steps))
+    sizes = [steps // chunks + (1 if c < steps % chunks else 0) for c in range(chunks)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(chunks + 1)]
     torch.cuda.synchronize()
     ev[0].record()
-    for i in range(steps):
-        run(i)
-        ev[i + 1].record()
+    i = 0
+    for c, n in enumerate(sizes):
+        for _ in range(n):
+            run(i)
+            i += 1
+        ev[c + 1].record()
     torch.cuda.synchronize()
-    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    t = sorted(ev[c].elapsed_time(ev[c + 1]) / n for c, n in enumerate(sizes))
     return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
 
 
@@ -784,14 +790,8 @@ def main(argv=None):
     graph = not args.no_graph
     log(f"workload {args.workload}: {wl['label']}; copies={runner.copies} graph={graph}")
 
-    clocks = ClockSampler(torch)
-    ms, med = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph,
-                         clocks=clocks, median=True)
-    value = runner.flops(rho) / (ms * 1e-3) / 1e12
-    k = rmm.k_of(rho, runner.d)
-    log(f"rho={rho} k={k}: {ms * 1e3:.1f} us/step (median {med * 1e3:.1f}), {value:.1f} TFLOP/s; "
-        f"clocks {clocks.summary()}")
-
+    # the dense comparison and the rho sweep run first: the headline below then starts
+    # from a GPU at its working clock, not from the cold-start transient
     sweep = []
     if not args.no_sweep:
         try:
@@ -816,6 +816,14 @@ def main(argv=None):
                 sweep.append(ent)
                 log(f"  rho={r}{' full' if full else ''}: {t * 1e3:.1f} us, {ent['tflops']:.1f} TFLOP/s"
                     + (f", x{ent['speedup_vs_dense']:.2f} vs dense" if dense_ms else ""))
+
+    clocks = ClockSampler(torch)
+    ms, med = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph,
+                         clocks=clocks, median=True)
+    value = runner.flops(rho) / (ms * 1e-3) / 1e12
+    k = rmm.k_of(rho, runner.d)
+    log(f"rho={rho} k={k}: {ms * 1e3:.1f} us/step (median {med * 1e3:.1f}), {value:.1f} TFLOP/s; "
+        f"clocks {clocks.summary()}")
 
     kt = kernel_times(torch, rmm, runner, rho, args.kernel_steps, runner.copies)
     log("per-kernel us per step: " + ", ".join(f"{kk}={v[0] * v[1] * 1e3:.1f}" + (f" ({v[1]:g} launches)" if v[1] != 1 else "")

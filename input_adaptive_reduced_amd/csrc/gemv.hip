@@ -182,7 +182,267 @@ __global__ __launch_bounds__(512) void gemv_wq_partial_kernel(const uint8_t *__r
     }
 }
 
+// ---------------------------------------------------------------- one-launch decode
+// The whole single-row step in one launch: every workgroup selects the kept
+// rows itself (the selection depends only on the d values of a, 16-32 KB
+// that every workgroup reads from the caches), then streams its own block
+// of columns over all kept rows, so no workgroup waits for another and no
+// partial sums leave the workgroup (no split over rows, no reduce launch).
+//
+// Selection: the key of index j is the magnitude of a_j's bf16 pattern
+// (bits 14..0), which orders like |a_j| (NaN above +Inf, -0 = +0).  A
+// 256-bin histogram of the top 8 key bits and a 128-bin histogram of the
+// low 7 bits inside the bin that holds the k-th largest give the exact
+// threshold T and the count of keys above it; every key above T is kept,
+// and of the keys equal to T the lowest-indexed ones up to k.  One block
+// scan of (above, equal) counts in index order places each kept index at
+// its ascending position: the LDS list (row, a value) is ascending, the
+// same set and order as the selection kernels produce.
+//
+// Stream: LPR lanes cover a 16-byte piece each of one kept row's column
+// block (256-byte pieces for bf16, 128-byte for 8-bit codes), so a wave
+// reads 64 / LPR rows per instruction with U instructions in flight; every
+// lane accumulates its EPL columns over its rows in a fixed order, and the
+// 64 row groups of the workgroup are added in a fixed order at the end:
+// bit-reproducible.  BQ: 0 = bf16 B, 1 = OCP FP8 E4M3 codes, 2 = int8 codes
+// (8-bit: y[c] also times scale[c]).
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedMaxKeys = 16384;  // d limit (keys per thread <= 16)
+
+template <int BQ, int LPR_>
+struct FusedShape {
+    static constexpr int EPL = BQ ? 16 : 8;   // columns per lane (one 16-byte load)
+    static constexpr int LPR = LPR_;          // lanes per row piece (16-byte pieces)
+    static constexpr int CB = EPL * LPR;      // columns per workgroup
+    static constexpr int RPI = 64 / LPR;      // rows per wave instruction
+};
+constexpr int kFusedLpr = 64;  // one 1 KB row piece per wave instruction
+
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+template <int BQ, int LPR>
+__global__ __launch_bounds__(1024) void decode_fused_kernel(const uint16_t *__restrict__ a, int d, int k,
+                                                            const char *__restrict__ B, int64_t row_bytes, int64_t m,
+                                                            const float *__restrict__ scale, float alpha,
+                                                            uint16_t *__restrict__ y, int32_t *__restrict__ idx_out,
+                                                            int rows_per_split, float *__restrict__ part) {
+    using S = FusedShape<BQ, LPR>;
+    constexpr int E = kFusedMaxKeys / kFusedThreads;
+    __shared__ int hist[256];
+    __shared__ int wsum[kFusedThreads / 64 + 1];
+    __shared__ int sinfo[4];
+    __shared__ uint16_t sidx[kFusedMaxKeys];
+    __shared__ float sval[kFusedMaxKeys];  // then the row-group sums (row groups x CB floats)
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+    // ---- keys: `per` consecutive indices per thread
+    const int per = (d + kFusedThreads - 1) / kFusedThreads;
+    const int j0 = tid * per;
+    uint32_t raw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) raw[e] = (e < per && j0 + e < d) ? (uint32_t)a[j0 + e] : 0x10000u;  // 0x10000: no key
+    for (int q = tid; q < 256; q += kFusedThreads) hist[q] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (raw[e] < 0x10000u) atomicAdd(&hist[(raw[e] & 0x7fffu) >> 7], 1);
+    __syncthreads();
+    if (w == 0) {
+        // bins in descending order, four per lane: the bin holding the k-th largest key
+        int c[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c[q] = hist[255 - 4 * lane - q];
+            sum += c[q];
+        }
+        const int incl = wave_incl_scan_i32(sum, lane);
+        int above = incl - sum;
+        if (above < k && k <= incl) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (above + c[q] >= k) {
+                    sinfo[0] = 255 - 4 * lane - q;
+                    sinfo[1] = above;
+                    break;
+                }
+                above += c[q];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)sinfo[0];
+    for (int q = tid; q < 128; q += kFusedThreads) hist[q] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (raw[e] < 0x10000u && ((raw[e] & 0x7fffu) >> 7) == b1) atomicAdd(&hist[raw[e] & 0x7fu], 1);
+    __syncthreads();
+    if (w == 0) {
+        const int above1 = sinfo[1];
+        int c[2], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            c[q] = hist[127 - 2 * lane - q];
+            sum += c[q];
+        }
+        const int incl = above1 + wave_incl_scan_i32(sum, lane);
+        int above = incl - sum;
+        if (above < k && k <= incl) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (above + c[q] >= k) {
+                    sinfo[2] = (int)((b1 << 7) | (uint32_t)(127 - 2 * lane - q));
+                    sinfo[3] = above;
+                    break;
+                }
+                above += c[q];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t T = (uint32_t)sinfo[2];
+    const int need_eq = k - sinfo[3];
+    // ---- ascending compaction: block scan of (keys above T) << 16 | (keys equal to T)
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (raw[e] >= 0x10000u) continue;
+        const uint32_t kk = raw[e] & 0x7fffu;
+        gt += kk > T;
+        eq += kk == T;
+    }
+    const int v = (gt << 16) | eq;
+    const int incl = wave_incl_scan_i32(v, lane);
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        const int t = lane < kFusedThreads / 64 ? wsum[lane] : 0;
+        const int u = wave_incl_scan_i32(t, lane);
+        if (lane < kFusedThreads / 64) wsum[lane] = u - t;
+    }
+    __syncthreads();
+    const int excl = wsum[w] + incl - v;
+    int gb = excl >> 16, eb = excl & 0xffff;
+    const bool write_idx = idx_out && blockIdx.x == 0 && blockIdx.y == 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (raw[e] >= 0x10000u) continue;
+        const uint32_t kk = raw[e] & 0x7fffu;
+        int t = -1;
+        if (kk > T) {
+            t = gb + min(eb, need_eq);
+            ++gb;
+        } else if (kk == T) {
+            if (eb < need_eq) t = gb + eb;
+            ++eb;
+        }
+        if (t >= 0) {
+            sidx[t] = (uint16_t)(j0 + e);
+            sval[t] = __uint_as_float(raw[e] << 16);
+            if (write_idx) idx_out[t] = j0 + e;
+        }
+    }
+    __syncthreads();
+
+    // ---- stream the workgroup's column block over every kept row
+    const int g = lane / S::LPR, cl = lane % S::LPR;
+    const int64_t c0 = (int64_t)blockIdx.x * S::CB + cl * S::EPL;
+    const bool col_ok = c0 < m;
+    const char *Bc = B + c0 * (BQ ? 1 : 2);
+    float acc[S::EPL];
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) acc[e] = 0.f;
+    constexpr int U = 8;                                   // loads in flight per lane
+    constexpr int ROUND = (kFusedThreads / 64) * S::RPI;  // rows per wave-round of the workgroup
+    const int t_lo = (int)blockIdx.y * rows_per_split, t_hi = min(k, t_lo + rows_per_split);
+    for (int tb = t_lo; tb < t_hi; tb += ROUND * U) {
+        uint4 vv[U];
+        float av[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u * ROUND + w * S::RPI + g;
+            const bool ok = t < t_hi && col_ok;
+            av[u] = ok ? sval[t] : 0.f;
+            vv[u] = ok ? *reinterpret_cast<const uint4 *>(Bc + (int64_t)sidx[t] * row_bytes) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (BQ == 0) {
+                fma8(acc, av[u], vv[u]);
+            } else {
+                fma4_q8<BQ - 1>(acc, av[u], vv[u].x);
+                fma4_q8<BQ - 1>(acc + 4, av[u], vv[u].y);
+                fma4_q8<BQ - 1>(acc + 8, av[u], vv[u].z);
+                fma4_q8<BQ - 1>(acc + 12, av[u], vv[u].w);
+            }
+        }
+    }
+    __syncthreads();  // every wave is done with the list: its LDS takes the row-group sums
+    float *red = sval;
+    const int rg = w * S::RPI + g;
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) red[rg * S::CB + cl * S::EPL + e] = acc[e];
+    __syncthreads();
+    constexpr int NRG = (kFusedThreads / 64) * S::RPI;  // row groups
+    static_assert(NRG * S::CB <= kFusedMaxKeys, "row-group sums fit in the list's LDS");
+    for (int c = tid; c < S::CB; c += kFusedThreads) {
+        const int64_t col = (int64_t)blockIdx.x * S::CB + c;
+        float sum = 0.f;
+        for (int r = 0; r < NRG; ++r) sum += red[r * S::CB + c];
+        if (col < m) {
+            if (part) {  // split rows: scaled partial sums, alpha applied by the reduce
+                part[(int64_t)blockIdx.y * m + col] = BQ ? sum * scale[col] : sum;
+            } else {
+                const float f = BQ ? alpha * scale[col] : alpha;
+                y[col] = f32_to_bf16(f * sum);
+            }
+        }
+    }
+}
+
 }  // namespace
+
+int64_t decode_fused_min_m() { return 28 * FusedShape<0, kFusedLpr>::CB; }
+
+int decode_fused_splits(int bq, int64_t m, int64_t k) {
+    // about one workgroup per CU (each selects once), whole column blocks
+    const int64_t cb = bq ? FusedShape<1, kFusedLpr>::CB : FusedShape<0, kFusedLpr>::CB;
+    const int64_t blocks = (m + cb - 1) / cb;
+    int64_t s = 256 / blocks;
+    const int64_t max_s = (k + 255) / 256;  // at least 256 kept rows per split
+    if (s > max_s) s = max_s;
+    return (int)(s < 1 ? 1 : s);
+}
+
+hipError_t launch_decode_fused(const uint16_t *a, int64_t d, int64_t k, const void *B, int bq, int64_t ldb, int64_t m,
+                               const float *scale, float alpha, uint16_t *y, int32_t *idx_out, int splits,
+                               float *part, hipStream_t stream) {
+    if (d < 1 || d > kFusedMaxKeys || k < 1 || k > d || m < 1 || bq < 0 || bq > 2 || (bq && !scale) ||
+        m % (bq ? 16 : 8) || ldb % (bq ? 16 : 8) || splits < 1 || (splits > 1 && !part))
+        return hipErrorInvalidValue;
+    const int64_t cb = bq ? FusedShape<1, kFusedLpr>::CB : FusedShape<0, kFusedLpr>::CB;
+    const dim3 grid((unsigned)((m + cb - 1) / cb), (unsigned)splits);
+    const int rps = (int)((k + splits - 1) / splits);
+    float *pp = splits > 1 ? part : nullptr;
+    const char *Bb = static_cast<const char *>(B);
+    if (bq == 0)
+        decode_fused_kernel<0, kFusedLpr><<<grid, kFusedThreads, 0, stream>>>(a, (int)d, (int)k, Bb, ldb * 2, m, scale,
+                                                                              alpha, y, idx_out, rps, pp);
+    else if (bq == 1)
+        decode_fused_kernel<1, kFusedLpr><<<grid, kFusedThreads, 0, stream>>>(a, (int)d, (int)k, Bb, ldb, m, scale,
+                                                                              alpha, y, idx_out, rps, pp);
+    else
+        decode_fused_kernel<2, kFusedLpr><<<grid, kFusedThreads, 0, stream>>>(a, (int)d, (int)k, Bb, ldb, m, scale,
+                                                                              alpha, y, idx_out, rps, pp);
+    return hipGetLastError();
+}
 
 int gemv_wq_splits(int64_t m, int64_t k) {
     // about 1024 workgroups of 1024 columns, at least 256 kept rows per split

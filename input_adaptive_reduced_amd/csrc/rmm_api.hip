@@ -94,6 +94,7 @@ struct Plan {
     bool shortcut;   // rho = 1 fast path: no norms or selection
     bool directA;    // MFMA reads A in place (no pack)
     bool transA;     // the norm pass writes A^T and the GEMM gathers its rows (no pack)
+    bool fused_decode;  // decode with the selection inside the GEMV (gsplits row splits)
     ColnormPlan cp;
     GemmConfig gc;
     int gsplits;
@@ -180,6 +181,14 @@ Plan make_plan(const rmm_desc_t *ds, int64_t k, const void *A, const void *B, co
     if (bf && ptr_ok && ld_ok && ds->n == 1 && !ds->transB && ds->batch == 1 && ds->d <= kFusedSelectMaxD) {
         p.route = ROUTE_DECODE;
         p.shortcut = false;  // the fused |a| selection also produces the kept values
+        // wide outputs: every GEMV workgroup selects from |a| itself (no select launch)
+        p.fused_decode = !given && ds->m >= decode_fused_min_m();
+        if (p.fused_decode) {
+            p.gsplits = decode_fused_splits(0, ds->m, k);
+            p.off_gpart = 0;
+            p.total = p.gsplits > 1 ? align_up((size_t)p.gsplits * ds->m * 4) : 0;
+            return p;
+        }
     } else if (bf && ptr_ok && ld_ok && mfma_extents_ok(ds, p.kpad)) {
         p.route = ROUTE_MFMA;
     } else {
@@ -648,6 +657,10 @@ rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t 
 size_t rmm_decode_wq_workspace_size(int64_t d, int64_t m, double rho) {
     const int64_t k = k_of(rho, d);
     if (k < 1 || d > kFusedSelectMaxD || m < 16 || m % 16) return SIZE_MAX;
+    if (m >= decode_fused_min_m()) {  // the selection inside the GEMV: only the split partials
+        const int s = decode_fused_splits(1, m, k);
+        return s > 1 ? align_up((size_t)s * m * 4) : 0;
+    }
     const int64_t kpad = (k + 127) / 128 * 128;
     const int splits = gemv_wq_splits(m, k);
     return align_up((size_t)kpad * 4) + align_up((size_t)k * 4) + align_up((size_t)splits * m * 4);
@@ -663,8 +676,8 @@ rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const flo
         ((uintptr_t)scale & 3))
         return RMM_ERR_UNSUPPORTED;
     const size_t need = rmm_decode_wq_workspace_size(d, m, rho);
-    if (!workspace || ws_bytes < need) return RMM_ERR_WORKSPACE;
-    if ((uintptr_t)workspace & 255) return RMM_ERR_INVALID_ARG;
+    if (need > 0 && (!workspace || ws_bytes < need)) return RMM_ERR_WORKSPACE;
+    if (need > 0 && ((uintptr_t)workspace & 255)) return RMM_ERR_INVALID_ARG;
     const int64_t ab = d * 2, bb = (d - 1) * ldb + m, sb = m * 4, yb = m * 2;
     char *ws = static_cast<char *>(workspace);
     if (overlaps(y, yb, a, ab) || overlaps(y, yb, Bq, bb) || overlaps(y, yb, scale, sb) ||
@@ -673,6 +686,18 @@ rmm_status_t rmm_decode_wq(const void *a, const void *Bq, int32_t fmt, const flo
         (idx_out && (overlaps(idx_out, k * 4, y, yb) || overlaps(idx_out, k * 4, ws, (int64_t)need) ||
                      overlaps(idx_out, k * 4, a, ab) || overlaps(idx_out, k * 4, Bq, bb))))
         return RMM_ERR_INVALID_ARG;
+    if (m >= decode_fused_min_m()) {
+        // the |a| selection inside every GEMV workgroup, then the split sum (if split)
+        const int fs = decode_fused_splits(1, m, k);
+        float *fpart = reinterpret_cast<float *>(ws);
+        RMM_LAUNCH(RMM_KERNEL_GEMV, launch_decode_fused(static_cast<const uint16_t *>(a), d, k, Bq,
+                                                        fmt == RMM_WQ_FP8_E4M3 ? 1 : 2, ldb, m, scale, alpha,
+                                                        static_cast<uint16_t *>(y), idx_out, fs, fpart, stream));
+        if (fs > 1)
+            RMM_LAUNCH(RMM_KERNEL_REDUCE,
+                       launch_splitk_reduce(fpart, fs, 1, m, 1, alpha, static_cast<uint16_t *>(y), m, 0, stream));
+        return RMM_OK;
+    }
     const int64_t kpad = (k + 127) / 128 * 128;
     const int splits = gemv_wq_splits(m, k);
     int32_t *pidx = reinterpret_cast<int32_t *>(ws);
@@ -901,6 +926,16 @@ rmm_status_t run_matmul(const rmm_desc_t *desc, const void *A, const void *B, in
     const int64_t n = ds.n, d = ds.d, m = ds.m, batch = ds.batch;
     int32_t *pidx = reinterpret_cast<int32_t *>(ws + p.off_idx);  // padded: kpad per row
 
+    if (p.fused_decode) {
+        float *gpart = reinterpret_cast<float *>(ws + p.off_gpart);
+        RMM_LAUNCH(RMM_KERNEL_GEMV, launch_decode_fused(static_cast<const uint16_t *>(A), d, k, B, 0, ds.ldb, m, nullptr,
+                                                        ds.alpha, static_cast<uint16_t *>(Y), idx_out, p.gsplits,
+                                                        gpart, stream));
+        if (p.gsplits > 1)
+            RMM_LAUNCH(RMM_KERNEL_REDUCE, launch_splitk_reduce(gpart, p.gsplits, 1, m, 1, ds.alpha,
+                                                               static_cast<uint16_t *>(Y), ds.ldy, 0, stream));
+        return RMM_OK;
+    }
     if (p.route == ROUTE_DECODE) {
         float *aval = reinterpret_cast<float *>(ws + p.off_aval);
         float *gpart = reinterpret_cast<float *>(ws + p.off_gpart);

@@ -215,6 +215,20 @@ struct AttnArgs {
 hipError_t launch_attention_fwd(const AttnArgs &a, int kq, hipStream_t stream);
 
 int gemv_splits(int64_t m, int64_t k);
+// Single-row decode with the selection inside the GEMV: every workgroup
+// selects from |a| itself (a bf16, d <= 16384), then streams one 512-column
+// (bf16 B, bq 0) or 1024-column (8-bit codes, bq 1 = FP8 E4M3, 2 = int8,
+// with per-column scale) block over one split of the kept rows; ldb in
+// elements.  splits == 1: y[c] = alpha (* scale[c]) * sum_t a[I_t] B[I_t, c]
+// rounded to bf16; otherwise part[split][c] (scaled, without alpha) for
+// launch_splitk_reduce.  idx_out (k int32, ascending) may be NULL.  Taken
+// for wide outputs (m >= decode_fused_min_m()), with decode_fused_splits
+// splits (about one workgroup per CU).
+int64_t decode_fused_min_m();
+int decode_fused_splits(int bq, int64_t m, int64_t k);
+hipError_t launch_decode_fused(const uint16_t *a, int64_t d, int64_t k, const void *B, int bq, int64_t ldb, int64_t m,
+                               const float *scale, float alpha, uint16_t *y, int32_t *idx_out, int splits,
+                               float *part, hipStream_t stream);
 // Gathered GEMV over 8-bit weights (fmt 0: OCP FP8 E4M3, 1: int8) with one
 // fp32 scale per column: part[split][c] = scale[c] * sum over the split's
 // kept rows of aval[t] * q[idx[t], c].  m and ldb multiples of 16, B 16-byte

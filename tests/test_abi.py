@@ -118,7 +118,8 @@ def test_plan_info_on_host(lib):
     assert info(r.BF16, 4100, 4096, 4096, 0.8) == (0, (1, 2, 1))       # n % 8 != 0: A packed, A-direct kernel
     assert info(r.BF16, 4096, 8192, 28672, 0.8) == (0, (1, 5, 1))      # c5
     assert info(r.BF16, 4096, 8192, 40960, 0.8) == (0, (1, 4, 1))      # wider output keeps the pack; LDS-DMA B
-    st, (route, gemm, splits) = info(r.BF16, 1, 8192, 28672, 0.8)     # decode: gathered GEMV
+    assert info(r.BF16, 1, 8192, 28672, 0.8) == (0, (2, -1, 4))       # wide decode: 56 column blocks x 4 row splits
+    st, (route, gemm, splits) = info(r.BF16, 1, 8192, 4096, 0.8)      # narrower decode: split gathered GEMV
     assert st == 0 and route == 2 and gemm == -1 and splits > 1
     assert info(r.BF16, 4096, 128, 4096, 0.5, transB=1, batch=32, group=4) == (0, (1, 3, 1))  # c4 scores
     # attention's P V (m = d_v): A's kept columns gathered inside the narrow-output kernel
@@ -161,7 +162,8 @@ def test_attention_and_decode_wq_host_checks(lib):
     assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, o, None, P(0x100010), need, None) == 1  # unaligned ws
     assert att(q, k, v, 2, 1, 64, 64, 128, 128, 0.5, 1, P(0x10000 + 256), None, w, need, None) == 1  # out over q
     ws_d = lib.rmm_decode_wq_workspace_size
-    assert ws_d(8192, 28672, 0.8) not in (0, SZ_MAX)
+    assert ws_d(8192, 28672, 0.8) == 9 * 28672 * 4        # wide outputs: selection in the GEMV, 9 row splits
+    assert ws_d(8192, 4096, 0.8) not in (0, SZ_MAX)       # narrower: select launch, split GEMV and reduce
     assert ws_d(8192, 40, 0.8) == SZ_MAX                  # m % 16 != 0
     assert ws_d(20000, 1024, 0.8) == SZ_MAX               # beyond the fused selection
     a, bq, sc, y = P(0x10000), P(0x200000), P(0x30000), P(0x40000)

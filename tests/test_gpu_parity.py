@@ -277,6 +277,62 @@ def test_decode_row_length_not_a_multiple_of_eight(rmm, d):
                      oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx), k, "bf16", f"d={d} rho={rho}")
 
 
+ONE_LAUNCH = [
+    # (d, m, rho): decodes wide enough (m >= 14336) for the selection inside the GEMV
+    (1001, 24584, 0.6),    # odd d; the last column block holds 8 columns
+    (16384, 24576, 0.5),   # the longest row the selection takes
+    (8192, 28672, 1.0),    # every row kept
+    (640, 24576, 1 / 640),  # one row kept
+]
+
+
+@pytest.mark.parametrize("d,m,rho", ONE_LAUNCH, ids=[f"d{c[0]}-m{c[1]}-rho{c[2]:.3g}" for c in ONE_LAUNCH])  # noqa
+def test_decode_selection_in_gemv(rmm, d, m, rho):
+    """Wide single-row decodes (m >= 14336): every GEMV workgroup selects
+    from |a| itself, then streams its column block over one split of the kept
+    rows (the split sum follows): kept set bit for bit, y within the bound,
+    repeat calls identical."""
+    import ctypes
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(d + m)
+    a = synthetic.round_to_bf16((rng.standard_normal((1, d)) * np.exp(rng.standard_normal(d))).astype(np.float32))
+    B = synthetic.round_to_bf16((rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32))
+    ld = (d + 7) // 8 * 8  # the decode route wants a 16-byte row pitch: pad the row, values after d unused
+    padded = np.full((1, ld), 3.0e4, np.float32)
+    padded[:, :d] = a
+    ad, Bd = to_device(synthetic.round_to_bf16(padded), "bf16")[:, :d], to_device(B, "bf16")
+    info = rmm.plan_info(ad, Bd, rho)
+    assert info["route"] == "decode", info
+    k = oracle.k_of(rho, d)
+    ref_idx = oracle.topk(np.abs(a[0]).astype(np.float64), k)
+    Y, idx = rmm.matmul(ad, Bd, rho, alpha=0.5)
+    Y2, _ = rmm.matmul(ad, Bd, rho, alpha=0.5, return_idx=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    assert torch.equal(Y, Y2)
+    B64 = B.astype(np.float64)
+    assert_close(to_host(Y), oracle.reduced_product(a, B64, ref_idx, 0.5),
+                 oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx, 0.5), k, "bf16", f"d={d} m={m}")
+
+
+def test_decode_selection_in_gemv_ties(rmm):
+    """Many equal |a_j| through the selection inside the GEMV: ties -> lower index."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(15)
+    d, m = 1000, 24576
+    a = synthetic.round_to_bf16(rng.choice([-2.0, -1.0, 0.5, 1.0, 2.0, -0.0], size=(1, d)).astype(np.float32))
+    B = synthetic.round_to_bf16(rng.standard_normal((d, m)).astype(np.float32))
+    ad, Bd, B64 = to_device(a, "bf16"), to_device(B, "bf16"), B.astype(np.float64)
+    for k in (1, 137, 500, 999, 1000):
+        rho = k / d
+        ref_idx = oracle.topk(np.abs(a[0]).astype(np.float64), k)
+        Y, idx = rmm.matmul(ad, Bd, rho)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), k
+        assert_close(to_host(Y), oracle.reduced_product(a, B64, ref_idx),
+                     oracle.reduced_product(np.abs(a), np.abs(B64), ref_idx), k, "bf16", f"ties k={k}")
+
+
 def test_decode_exact_ties(rmm):
     """n = 1 with many equal |a_j| (bf16 has few values): ties -> lower index."""
     torch = pytest.importorskip("torch")

@@ -120,6 +120,15 @@ def test_row_length_not_a_multiple_of_eight(rmm, torch, fmt, d):
         assert_close(to_host(y).reshape(1, -1), ref.Y, absprod, ref.k, "bf16", f"{fmt} d={d} rho={rho}")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("d,m,rho", [(1001, 24592, 0.6), (16384, 24576, 0.5), (640, 28672, 1.0)])
+def test_selection_in_gemv_decode(rmm, torch, fmt, d, m, rho):
+    """Wide 8-bit decodes (m >= 14336): every GEMV workgroup selects from |a|
+    itself (no select launch): kept set bit for bit, y within the bound."""
+    a, codes, scale = small_case(d * 7 + m, d, m, fmt)
+    check(rmm, torch, a, codes, scale, fmt, rho, alpha=0.5)
+
+
 def test_unsupported_shapes(rmm, torch):
     a = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rmm.RMMError):

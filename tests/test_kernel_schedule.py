@@ -17,8 +17,9 @@ gemm_tdma_kernel keeps two LDS stages per operand: each wave waits for all
 of its own LDS-DMA loads (vmcnt(0)) right before the workgroup barrier, and
 refills a stage only after that barrier, since only then has every wave
 read its last operands from it.  The test checks that in the compiled loop
-every barrier directly follows such a wait and that all 16 LDS-DMA loads of
-a step come after a barrier and before the next wait.  No GPU is used.
+every barrier directly follows such a wait and that all LDS-DMA loads of a
+step (16 with bf16 weights, 12 with 8-bit weights) come after a barrier and
+before the next wait.  No GPU is used.
 """
 import os
 import re
@@ -137,13 +138,20 @@ def loop_tokens(asm: str, kernel: str):
             yield "".join(seq)
 
 
-@pytest.mark.parametrize("inst", ["ILb0ELi0E", "ILb1ELi0E", "ILb0ELi1E"])  # (split K, epilogue)
-def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm, inst):
-    for split in (inst,):
-        loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernel" + split))
-        assert loops, "no K loop with a barrier found"
-        for seq in loops:
-            assert seq.count("B") == 2, seq  # two K steps per iteration, one barrier each
-            # rotate to start at a barrier: then B D^16 W B D^16 W
-            r = seq[seq.index("B"):] + seq[:seq.index("B")]
-            assert re.fullmatch(r"(BD{16}W){2}", r), seq
+TDMA = [
+    # (split K, epilogue, B format) instantiation, LDS-DMA loads per K step:
+    # bf16 B 8 + A 8; 8-bit B (FP8, int8) 4 + A 8
+    ("ILb0ELi0ELi0E", 16), ("ILb1ELi0ELi0E", 16), ("ILb0ELi1ELi0E", 16),
+    ("ILb0ELi0ELi1E", 12), ("ILb1ELi0ELi1E", 12), ("ILb0ELi0ELi2E", 12), ("ILb1ELi0ELi2E", 12),
+]
+
+
+@pytest.mark.parametrize("inst,loads", TDMA, ids=[t[0] for t in TDMA])
+def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm, inst, loads):
+    loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernel" + inst))
+    assert loops, "no K loop with a barrier found"
+    for seq in loops:
+        assert seq.count("B") == 2, seq  # two K steps per iteration, one barrier each
+        # rotate to start at a barrier: then B D^loads W B D^loads W
+        r = seq[seq.index("B"):] + seq[:seq.index("B")]
+        assert re.fullmatch(r"(BD{%d}W){2}" % loads, r), seq
