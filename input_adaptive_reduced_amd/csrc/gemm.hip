@@ -1045,7 +1045,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     __shared__ __align__(16) uint16_t sIdx[BQ ? kTdmaListRowsQ : kTdmaListRows];
     typedef __attribute__((address_space(3))) void lds_t;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+    // the wave index is uniform: from an SGPR, LDS-DMA destinations (M0) are scalar arithmetic
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 1,
+              wn = w & 1;
     const int tiles_m = (int)((g.n + BM - 1) / BM), tiles_n = (int)((g.m + BN - 1) / BN);
     int tm, tn;
     tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
