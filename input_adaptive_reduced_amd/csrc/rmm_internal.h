@@ -210,6 +210,7 @@ struct AttnArgs {
     uint16_t *O;
     int64_t ldo, o_stride;
     int H, group, Lq, Lk, causal;
+    int pair;  // causal query tiles paired per workgroup (set by launch_attention_fwd)
     float scale_log2;
 };
 hipError_t launch_attention_fwd(const AttnArgs &a, int kq, hipStream_t stream);

@@ -108,6 +108,16 @@ def test_attention_full_size(rmm, torch):
     check(rmm, torch, Q, K, V, 0.5, True, heads=[0, 13, 31], rows=sample_rows(4096, 10, seed=6, tile=128))
 
 
+@pytest.mark.parametrize("rho,Lq", [(0.5, None), (0.8, None), (0.5, 1100)], ids=["k64", "k128", "k64-Lq1100"])
+def test_attention_paired_tiles(rmm, torch, rho, Lq):
+    """More causal query tiles than two workgroups per CU hold (64 heads x 9
+    tiles): each workgroup takes a long and a short tile of one head, the
+    middle tile alone; every row of three heads, both kept widths, and queries
+    at the end of a longer context with a ragged last tile."""
+    Q, K, V = case(dict(heads=64, kv_heads=16, L=1152, dh=128), rho, Lq)
+    check(rmm, torch, Q, K, V, rho, True, heads=[0, 37, 63])
+
+
 def test_attention_rejects_unsupported(rmm, torch):
     q = torch.zeros((2, 64, 128), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 32, 128), dtype=torch.bfloat16, device="cuda")
