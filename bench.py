@@ -95,6 +95,86 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# rocprofv3 FETCH_SIZE reads half the bytes a streaming read moves on this chip and
+# WRITE_SIZE reads them exactly: factors from a 1 GiB device copy (``--calibrate-copy``)
+FETCH_SCALE, WRITE_SCALE = 1.9999496949451407, 1.0
+# the dominant kernel of each workload: (roofline key, kernel name fragment, source file)
+TRAFFIC_KERNELS = {
+    "c2": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c3": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c5": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c5-fp8": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c5-int8": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c4": ("gemm", "gemm_stream_kernel", "gemm.hip"),
+    "pv": ("gemm", "gemm_gcol_kernel", "gemm.hip"),
+    "attn": ("gemm", "attn_fwd", "attention.hip"),
+    "c5-decode": ("gemv", "decode_fused_kernel", "gemv.hip"),
+    "c5-decode-fp8": ("gemv", "decode_fused_kernel", "gemv.hip"),
+    "c5-decode-int8": ("gemv", "decode_fused_kernel", "gemv.hip"),
+}
+
+
+def short_kernel_name(name):
+    """``void rmm::(anonymous namespace)::k<4>(rmm::Args)`` -> ``k<4>``."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # the argument list: the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not name.startswith("(anonymous", i):
+            cut = i
+            break
+    name = name[:cut]
+    for ns in ("rmm::(anonymous namespace)::", "rmm::"):
+        name = name.replace(ns, "")
+    return name
+
+
+def record_traffic(workload, fetch_csv, write_csv):
+    """Average FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the rows of a
+    dispatch) of the workload's dominant kernel from two rocprofv3 --pmc runs of this
+    script, scaled by the copy calibration, into profiles/traffic.json with the digest
+    of the kernel's source (a later change of the source retires the record)."""
+    import csv
+    key, frag, src = TRAFFIC_KERNELS[workload]
+
+    def per_dispatch(path, counter):
+        vals, name = {}, None
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter or frag not in r["Kernel_Name"]:
+                    continue
+                name = short_kernel_name(r["Kernel_Name"])
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"{path}: no {counter} rows for a kernel named like {frag!r}")
+        return sum(vals.values()) / len(vals), len(vals), name
+
+    fetch, nf, name = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, nw, _ = per_dispatch(write_csv, "WRITE_SIZE")
+    rel = os.path.join("input_adaptive_reduced_amd", "csrc", src)
+    rec = {"kernel": name, "bytes_per_launch": fetch * 1024 * FETCH_SCALE + write * 1024 * WRITE_SCALE,
+           "read_bytes": fetch * 1024 * FETCH_SCALE, "write_bytes": write * 1024 * WRITE_SCALE,
+           "fetch_kib_raw": fetch, "write_kib_raw": write, "launches": [nf, nw],
+           "fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE,
+           "source": rel, "source_sha256": source_digest(os.path.join(ROOT, rel))}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(p):
+        with open(p) as f:
+            data = json.load(f)
+    data[f"{key}@{workload}"] = rec
+    with open(p, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({f"{key}@{workload}": rec}), flush=True)
+    return 0
+
+
 def load_traffic(kernel_key, workload):
     """HBM bytes per launch from committed rocprofv3 counters, if still current."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -560,6 +640,9 @@ class ClockSampler:
         if not self.paths or not self.samples["sclk"]:
             return None
         out = {"source": self.device + "/pp_dpm_{sclk,mclk} (the DPM level the driver marks current)",
+               "note": "the driver's reported level, polled between launches: it lags the hardware and "
+                       "often shows an idle level under load; the shader clock measured inside running "
+                       "waves is roofline.measured_peak_shader_mhz (matrix-core probe)",
                "samples": len(self.samples["sclk"]), "sclk_levels": getattr(self, "table", None)}
         for k, v in self.samples.items():
             if v:
@@ -737,7 +820,13 @@ def main(argv=None):
     ap.add_argument("--calibrate-mfma", action="store_true",
                     help="only run the matrix-core ceiling probe and print its TFLOP/s")
     ap.add_argument("--no-mfma-ceiling", action="store_true", help="skip the matrix-core ceiling probe")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: store the HBM bytes of --workload's dominant kernel from the counter_collection "
+                         "CSVs of two rocprofv3 runs of this script (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) "
+                         "in profiles/traffic.json, and exit")
     args = ap.parse_args(argv)
+    if args.record_traffic:
+        return record_traffic(args.workload, *args.record_traffic)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -845,7 +934,9 @@ def main(argv=None):
         else:      # kept B rows + a + fp32 partial row
             algo_bytes = k * runner.m * 2 + runner.d * 2 + runner.m * 4
         achieved = algo_bytes / (gemv_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "gemv_partial", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        # from 28 x 512 output columns on the library selects inside the GEMV (gemv.hip)
+        roof = {"bound": "hbm", "kernel": "decode_fused" if runner.m >= 28 * 512 else "gemv_partial",
+                "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": algo_bytes,
                 "kernel_ms": gemv_ms}
     elif runner.plan(rho)["gemm"] == "gcol":
