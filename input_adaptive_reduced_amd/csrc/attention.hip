@@ -201,6 +201,12 @@ __device__ __forceinline__ bool attn_block_masked(const AttnArgs &g, const AttnT
     return key0 + kKeyBlock > g.Lk || (g.causal && key0 + kKeyBlock - 1 > a.wfirst);
 }
 
+// False once the block starting at key0 lies past the causal limit of every
+// query of this wave (it and all later blocks add nothing for the wave)
+__device__ __forceinline__ bool attn_wave_live(const AttnArgs &g, const AttnTile &a, int key0) {
+    return !g.causal || key0 <= a.wfirst + 31;
+}
+
 // Key blocks of the slot's tiles from query tile qt on (this tile's and, on
 // the first pass, the paired tile's)
 template <int NW>
@@ -225,36 +231,46 @@ __device__ __forceinline__ void attn_priority(int remaining, int total) {
 
 // LDS-DMA copies of one group: the K operand blocks of key block kblk and the V
 // rows of key block vblk (vblk < 0 or past the end: zeros), shared by the NW
-// waves: attn_loads<KS, NW>() loads per thread, whatever the blocks.
+// waves: attn_loads<KS, NW>() loads per thread, whatever the blocks.  The
+// per-lane part of every copy offset is fixed (AttnCopies, computed once);
+// a block adds a scalar, or kAttnOob when it is past the end or before the
+// start.  Rows of the last V block past L_k lie past the buffer's end (V is
+// L_k rows of 256 bytes), so they read as zero too.
 template <int KS, int NW>
 constexpr int attn_loads() {
     return 2 * KS / NW + 16 / NW;
 }
 
 template <int KS, int NW>
-__device__ __forceinline__ void attn_issue(__amdgpu_buffer_rsrc_t rK, __amdgpu_buffer_rsrc_t rV, uint32_t ldv2, int Lk,
-                                           int nblk, int w, int lane, int kblk, int vblk, uint4 *dK, uint4 *dV) {
-    constexpr int KL = 2 * KS / NW;  // K operand blocks of 1 KB each wave copies per key block
-    constexpr int VL = 16 / NW;      // V copies of 1 KB (four rows) each wave makes per key block
+struct AttnCopies {
+    static constexpr int KL = 2 * KS / NW;  // K operand blocks of 1 KB each wave copies per key block
+    static constexpr int VL = 16 / NW;      // V copies of 1 KB (four rows) each wave makes per key block
     static_assert(KL * NW == 2 * KS && VL * NW == 16, "loads per wave");
-    const bool kreal = kblk < nblk;
+    uint32_t k[KL], v[VL];
+
+    __device__ __forceinline__ AttnCopies(uint32_t ldv2, int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-        const int b = w + NW * i;  // operand block within the key block
-        const uint32_t o = kreal ? (uint32_t)((kblk * 2 * KS + b) * 1024 + lane * 16) : kAttnOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (attn_lds_t *)&dK[b * 64], 16, o, 0, 0, 0);
-    }
-    const bool vreal = vblk >= 0 && vblk < nblk;
+        for (int i = 0; i < KL; ++i) k[i] = (uint32_t)((w + NW * i) * 1024 + lane * 16);
 #pragma unroll
-    for (int q = 0; q < VL; ++q) {
-        const int r = 4 * VL * w + 4 * q + (lane >> 4);
-        const uint32_t c = (uint32_t)((lane & 15) ^ ((r & 3) << 1));
-        const int key = vblk * kKeyBlock + r;
-        const uint32_t o = vreal && key < Lk ? (uint32_t)key * ldv2 + c * 16u : kAttnOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (attn_lds_t *)&dV[(4 * VL * w + 4 * q) * kVChunks], 16, o, 0, 0,
-                                                 0);
+        for (int q = 0; q < VL; ++q) {
+            const int r = 4 * VL * w + 4 * q + (lane >> 4);
+            v[q] = (uint32_t)r * ldv2 + (uint32_t)((lane & 15) ^ ((r & 3) << 1)) * 16u;
+        }
     }
-}
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rK, __amdgpu_buffer_rsrc_t rV, uint32_t ldv2, int nblk,
+                                          int w, int kblk, int vblk, uint4 *dK, uint4 *dV) const {
+        const uint32_t kb = kblk < nblk ? (uint32_t)kblk * (uint32_t)(2 * KS * 1024) : kAttnOob;
+        const uint32_t vb = vblk >= 0 && vblk < nblk ? (uint32_t)vblk * (uint32_t)kKeyBlock * ldv2 : kAttnOob;
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (attn_lds_t *)&dK[(w + NW * i) * 64], 16, k[i] + kb, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < VL; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (attn_lds_t *)&dV[(4 * VL * w + 4 * q) * kVChunks], 16,
+                                                     v[q] + vb, 0, 0, 0);
+    }
+};
 
 // S^T of one 64-key block for this wave's 32 queries: s[kb][r] is key
 // 32 kb + 8 (r / 4) + 4 hsel + r % 4 of the block for query lane % 32
@@ -409,6 +425,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_pipe_kernel(AttnArgs
     const __amdgpu_buffer_rsrc_t rK = attn_rsrc(g.K + (int64_t)sl.h * g.k_stride, g.k_bytes);
     const __amdgpu_buffer_rsrc_t rV = attn_rsrc(g.V + (int64_t)(sl.h / g.group) * g.v_stride, g.v_bytes);
     const uint32_t ldv2 = (uint32_t)(g.ldv * 2);
+    const AttnCopies<KS, NW> cp(ldv2, w, lane);
     const float c = g.scale_log2;
     const int second = sl.qt1 >= 0 ? attn_blocks<NW>(g, sl.qt1) : 0;
     const int total = attn_blocks<NW>(g, sl.qt0) + second;
@@ -421,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_pipe_kernel(AttnArgs
     const int later = pass == 0 ? second : 0;  // blocks of the paired tile after this one
 
     auto issue = [&](int j, uint4 *dK, uint4 *dV) __attribute__((always_inline)) {
-        attn_issue<KS, NW>(rK, rV, ldv2, g.Lk, nblk, w, lane, j + 2, j, dK, dV);
+        cp.issue(rK, rV, ldv2, nblk, w, j + 2, j, dK, dV);
     };
     auto publish = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0f70 | NL);  // vmcnt(NL): only the newest group in flight
@@ -455,6 +472,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_pipe_kernel(AttnArgs
         constexpr int S = decltype(Sc)::value;
         publish();  // G_e: V of block e, K of block e + 2
         attn_priority(nblk - e + later, total);
+        if (!attn_wave_live(g, a, e * kKeyBlock)) {
+            // past the causal limit of all of this wave's queries: blocks e and on add
+            // nothing (every copy still goes out: the other waves read these stages)
+            issue(e + 2, attn_stage<3, S + 1>(sK0, sK1, sK2), attn_stage<3, S + 2>(sV0, sV1, sV2));
+            return;
+        }
         // block e + 1 past the end is masked whole: its softmax changes nothing
         if (attn_block_masked(g, a, (e + 1) * kKeyBlock)) attn_mask(s, (e + 1) * kKeyBlock, a.lim, hsel);
         issue(e + 2, attn_stage<3, S + 1>(sK0, sK1, sK2), attn_stage<3, S + 2>(sV0, sV1, sV2));
@@ -473,9 +496,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_pipe_kernel(AttnArgs
             if (i < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
-        // the new scores reuse the registers of the ones just consumed
+        // the new scores reuse the registers of the ones just consumed; none past
+        // the last block (the masked softmax overwrites what s then holds)
         __builtin_amdgcn_sched_barrier(0);
-        attn_scores<KS>(attn_stage<3, S + 2>(sK0, sK1, sK2), qf, lane, s);
+        if (e + 2 < nblk) attn_scores<KS>(attn_stage<3, S + 2>(sK0, sK1, sK2), qf, lane, s);
         attn_rescale(o, fac);
 #pragma unroll
         for (int x = 0; x < 2; ++x)
@@ -516,6 +540,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
     const __amdgpu_buffer_rsrc_t rK = attn_rsrc(g.K + (int64_t)sl.h * g.k_stride, g.k_bytes);
     const __amdgpu_buffer_rsrc_t rV = attn_rsrc(g.V + (int64_t)(sl.h / g.group) * g.v_stride, g.v_bytes);
     const uint32_t ldv2 = (uint32_t)(g.ldv * 2);
+    const AttnCopies<KS, 4> cp(ldv2, w, lane);
     const float c = g.scale_log2;
     const int second = sl.qt1 >= 0 ? attn_blocks<4>(g, sl.qt1) : 0;
     const int total = attn_blocks<4>(g, sl.qt0) + second;
@@ -537,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
 
     abf16x8_t qf[KS];
     auto compute = [&](int blk, const uint4 *cK, const uint4 *cV) __attribute__((always_inline)) {
-        if (blk >= nblk) return;
+        if (blk >= nblk || !attn_wave_live(g, a, blk * kKeyBlock)) return;
         af32x16_t s[2];
         attn_scores<KS>(cK, qf, lane, s);
         uint32_t pk[2][2][4];
@@ -554,12 +579,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs g) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         attn_priority(nblk - e + later, total);
-        attn_issue<KS, 4>(rK, rV, ldv2, g.Lk, nblk, w, lane, min(e + 1, npad), min(e + 1, npad),
-                       attn_stage<NS, S + 1>(sK0, sK1, sK1), attn_stage<NS, S + 1>(sV0, sV1, sV1));
+        cp.issue(rK, rV, ldv2, nblk, w, min(e + 1, npad), min(e + 1, npad), attn_stage<NS, S + 1>(sK0, sK1, sK1),
+                 attn_stage<NS, S + 1>(sV0, sV1, sV1));
         compute(e, attn_stage<NS, S>(sK0, sK1, sK1), attn_stage<NS, S>(sV0, sV1, sV1));
     };
 
-    attn_issue<KS, 4>(rK, rV, ldv2, g.Lk, nblk, w, lane, 0, 0, sK0, sV0);
+    cp.issue(rK, rV, ldv2, nblk, w, 0, 0, sK0, sV0);
     attn_gather_q<KS>(g, a, hsel, qf);  // while the first copies are in flight
     for (int e = 0; e < npad; e += NS) {
         block(e, std::integral_constant<int, 0>{});
