@@ -100,9 +100,9 @@ def source_digest(path):
 FETCH_SCALE, WRITE_SCALE = 1.9999496949451407, 1.0
 # the dominant kernel of each workload: (roofline key, kernel name fragment, source file)
 TRAFFIC_KERNELS = {
-    "c2": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
-    "c3": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
-    "c5": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
+    "c2": ("gemm", "gemm_tdma8_kernel", "gemm.hip"),
+    "c3": ("gemm", "gemm_tdma8_kernel", "gemm.hip"),
+    "c5": ("gemm", "gemm_tdma8_kernel", "gemm.hip"),
     "c5-fp8": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
     "c5-int8": ("gemm", "gemm_tdma_kernel", "gemm.hip"),
     "c4": ("gemm", "gemm_stream_kernel", "gemm.hip"),

@@ -13,13 +13,14 @@ of them and before the wait.  The kernel fences its sub-steps with scheduling
 barriers so that this holds by construction; this test compiles the kernel
 to gfx950 assembly and checks it in every loop that contains the wait.
 
-gemm_tdma_kernel keeps two LDS stages per operand: each wave waits for all
-of its own LDS-DMA loads (vmcnt(0)) right before the workgroup barrier, and
-refills a stage only after that barrier, since only then has every wave
-read its last operands from it.  The test checks that in the compiled loop
-every barrier directly follows such a wait and that all LDS-DMA loads of a
-step (16 with bf16 weights, 12 with 8-bit weights) come after a barrier and
-before the next wait.  No GPU is used.
+gemm_tdma_kernel and gemm_tdma8_kernel keep two LDS stages per operand:
+each wave waits for all of its own LDS-DMA loads (vmcnt(0)) right before
+the workgroup barrier, and refills a stage only after that barrier, since
+only then has every wave read its last operands from it.  The test checks
+that in the compiled loop every barrier directly follows such a wait and
+that all LDS-DMA loads of a step (16 per wave with four waves and bf16
+weights, 12 with 8-bit weights, 8 with eight waves) come after a barrier
+and before the next wait.  No GPU is used.
 """
 import os
 import re
@@ -139,16 +140,19 @@ def loop_tokens(asm: str, kernel: str):
 
 
 TDMA = [
-    # (split K, epilogue, B format) instantiation, LDS-DMA loads per K step:
-    # bf16 B 8 + A 8; 8-bit B (FP8, int8) 4 + A 8
-    ("ILb0ELi0ELi0E", 16), ("ILb1ELi0ELi0E", 16), ("ILb0ELi1ELi0E", 16),
-    ("ILb0ELi0ELi1E", 12), ("ILb1ELi0ELi1E", 12), ("ILb0ELi0ELi2E", 12), ("ILb1ELi0ELi2E", 12),
+    # kernel and (split K, epilogue, B format) instantiation, LDS-DMA loads per
+    # K step per wave: four waves, SwiGLU epilogue B 8 + A 8, 8-bit B (FP8,
+    # int8) 4 + A 8; eight waves (bf16 B, plain or split) B 4 + A 4
+    ("gemm_tdma_kernelILb0ELi1ELi0E", 16),
+    ("gemm_tdma_kernelILb0ELi0ELi1E", 12), ("gemm_tdma_kernelILb1ELi0ELi1E", 12),
+    ("gemm_tdma_kernelILb0ELi0ELi2E", 12), ("gemm_tdma_kernelILb1ELi0ELi2E", 12),
+    ("gemm_tdma8_kernelILb0E", 8), ("gemm_tdma8_kernelILb1E", 8),
 ]
 
 
 @pytest.mark.parametrize("inst,loads", TDMA, ids=[t[0] for t in TDMA])
 def test_tdma_refills_a_stage_only_after_the_barrier(gemm_asm, inst, loads):
-    loops = list(loop_tokens(gemm_asm, "gemm_tdma_kernel" + inst))
+    loops = list(loop_tokens(gemm_asm, inst))
     assert loops, "no K loop with a barrier found"
     for seq in loops:
         assert seq.count("B") == 2, seq  # two K steps per iteration, one barrier each
