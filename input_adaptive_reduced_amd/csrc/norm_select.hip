@@ -1032,13 +1032,26 @@ hipError_t launch_norm_select(const float *part, int64_t chunks, int64_t d, int6
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (dev < 32 && !(g_norm_select_attr_done & (1u << dev))) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&norm_select_kernel<4>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
-        if (e != hipSuccess) return e;
+        const void *fns[3] = {reinterpret_cast<const void *>(&norm_select_kernel<4>),
+                              reinterpret_cast<const void *>(&norm_select_kernel<8>),
+                              reinterpret_cast<const void *>(&norm_select_kernel<16>)};
+        for (const void *f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+            if (e != hipSuccess) return e;
+        }
         g_norm_select_attr_done |= 1u << dev;
     }
-    norm_select_kernel<4><<<(unsigned)batch, 1024, (size_t)k * 4, stream>>>(part, (int)chunks, (int)d, (int)k, idx,
-                                                                            ld_idx, idx_pad, ld_pad);
+    // E keys per thread: 1024 threads cover d
+    const size_t lds = (size_t)k * 4;
+    if (d <= 4096)
+        norm_select_kernel<4><<<(unsigned)batch, 1024, lds, stream>>>(part, (int)chunks, (int)d, (int)k, idx, ld_idx,
+                                                                      idx_pad, ld_pad);
+    else if (d <= 8192)
+        norm_select_kernel<8><<<(unsigned)batch, 1024, lds, stream>>>(part, (int)chunks, (int)d, (int)k, idx, ld_idx,
+                                                                      idx_pad, ld_pad);
+    else
+        norm_select_kernel<16><<<(unsigned)batch, 1024, lds, stream>>>(part, (int)chunks, (int)d, (int)k, idx, ld_idx,
+                                                                       idx_pad, ld_pad);
     return hipGetLastError();
 }
 

@@ -115,8 +115,13 @@ ODD = [
     # partials) than it takes
     (64, 20480, 64, "bf16", 0.5, "d above the fused selection"),
     (33000, 1024, 64, "bf16", 0.5, "many row chunks"),
+    # the one-workgroup norm+select kernel with 8 and 16 keys per thread
+    # (4096 < d <= 16384, at most eight row chunks)
+    (64, 6000, 64, "bf16", 0.6, "fused selection, 8 keys per thread"),
+    (300, 14004, 40, "bf16", 0.3, "fused selection, 16 keys per thread"),
 ]
 SEPARATE_FINALIZE = {"d above the fused selection", "many row chunks"}
+FUSED_SELECT = {"fused selection, 8 keys per thread", "fused selection, 16 keys per thread"}
 
 
 @pytest.mark.parametrize("n,d,m,dtype,rho,note", ODD, ids=[o[-1] for o in ODD])
@@ -140,6 +145,8 @@ def test_odd_shapes(rmm, torch, n, d, m, dtype, rho, note):
         rmm.timing_enable(False)
     if note in SEPARATE_FINALIZE:  # the case reaches the path it is meant to cover
         assert launches["finalize"] == 1, launches
+    if note in FUSED_SELECT:
+        assert launches["finalize"] == 0 and launches["select"] == 1, launches
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
     B64 = B.astype(np.float64)
     assert_close(to_host(Y), oracle.reduced_product(A, B64, ref_idx),
