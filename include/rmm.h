@@ -43,7 +43,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations below have int as their underlying type in C++ too, so
+ * that any int a C caller passes (an unknown status or dtype code included)
+ * is a valid value of the parameter and is refused, not undefined. */
+#ifdef __cplusplus
+#define RMM_ENUM_INT : int
+#else
+#define RMM_ENUM_INT
+#endif
+
+typedef enum RMM_ENUM_INT {
     RMM_OK = 0,
     RMM_ERR_INVALID_ARG = 1, /* a size, pointer, stride or rho is invalid */
     RMM_ERR_UNSUPPORTED = 2, /* valid request the library cannot run */
@@ -51,7 +60,7 @@ typedef enum {
     RMM_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } rmm_status_t;
 
-typedef enum {
+typedef enum RMM_ENUM_INT {
     RMM_F32 = 0,  /* fp32 inputs, fp32 FMA accumulation, fp32 output */
     RMM_BF16 = 1  /* bf16 inputs, fp32 accumulation (MFMA), bf16 output */
 } rmm_dtype_t;

@@ -3,6 +3,10 @@
 Each ``csrc/*.hip`` translation unit is compiled separately with hipcc for
 gfx950 and linked into ``input_adaptive_reduced_amd/librmm.so``.  Packed
 fp32 vector instructions are disabled for every GPU compile.
+
+``build(sanitize=True, out=...)`` makes a separate copy whose host code runs
+under AddressSanitizer and UndefinedBehaviorSanitizer (GPU code unchanged),
+for the host-side tests; it needs the clang sanitizer runtime loaded first.
 """
 from __future__ import annotations
 
@@ -24,6 +28,11 @@ ARCH = "gfx950"
 GPU_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Wall", "-Wno-unused-result",
              "-I", INCLUDE, "-I", CSRC]
+# host code only: each sanitizer flag right after -Xarch_host
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+HOST_SANITIZE_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
 
 
 def _hipcc() -> str:
@@ -42,18 +51,25 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every HIP source and link librmm.so; returns the library path."""
+def build(verbose: bool = False, jobs: int = 4, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile every HIP source and link librmm.so; returns the library path.
+    With ``sanitize`` the host code is instrumented and the library goes to
+    ``out`` (required), objects to their own folder."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    if sanitize and not out:
+        raise ValueError("a sanitized build needs its own output path")
+    lib_path = out or LIB_PATH
+    build_dir = BUILD_DIR + ("_sanitize" if sanitize else "")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     objs = []
+    extra = HOST_SANITIZE if sanitize else []
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, "-c", src, "-o", obj] + CXX_FLAGS + GPU_FLAGS
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, "-c", src, "-o", obj] + CXX_FLAGS + GPU_FLAGS + extra
         warn = _run(cmd)
         if verbose and warn.strip():
             print(warn, file=sys.stderr)
@@ -61,10 +77,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-o", tmp] + objs)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + ".tmp%d" % os.getpid()
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-o", tmp] + objs +
+         (HOST_SANITIZE_LINK if sanitize else []))
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
