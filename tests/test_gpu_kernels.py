@@ -265,3 +265,127 @@ def test_non_default_streams(rmm, torch):
     assert torch.equal(Y1, Y0) and torch.equal(i1, i0)
     assert torch.equal(i2, i0)  # scaling A by 2 keeps the selection
     assert torch.equal(Y2.float(), (Y0.float() * 2))
+
+
+GUARDED = [
+    # (n, d, m, dtype, rho, route, gemm): every route's stores stay inside Y
+    # when Y's rows are a padded pitch apart inside a canary-filled buffer
+    (3104, 1504, 4000, "bf16", 0.5, "mfma", "tdma"),
+    (2048, 4200, 3080, "bf16", 0.5, "mfma", "tdma"),      # two K splits through the reduce
+    (3100, 1504, 4000, "bf16", 0.5, "mfma", "bdma"),
+    (3100, 1504, 4000, "bf16", 0.8, "mfma", "adirect"),
+    (2050, 4200, 3080, "bf16", 0.48, "mfma", "adirect"),  # split K
+    (300, 520, 264, "bf16", 0.5, "mfma", "tile128"),
+    (520, 2048, 128, "bf16", 0.5, "mfma", "gcol"),
+    (1, 8192, 28680, "bf16", 0.8, "decode", None),        # selection inside the GEMV, ragged last block
+    (1, 1000, 264, "bf16", 0.8, "decode", None),          # separate selection, split GEMV and reduce
+    (100, 300, 77, "f32", 0.5, "generic", None),
+]
+
+
+@pytest.mark.parametrize("n,d,m,dtype,rho,route,gemm", GUARDED,
+                         ids=[f"{g[6] or g[5]}-{g[0]}x{g[1]}x{g[2]}-rho{g[4]}" for g in GUARDED])
+def test_stores_stay_inside_a_padded_output(rmm, torch, n, d, m, dtype, rho, route, gemm):
+    """Canary guard bands: Y is a view with a row pitch of m + 280 inside a
+    buffer with 8 rows above and 256 below it (a whole tile of slack on every
+    side), all filled with a canary pattern; the kept-index output sits at
+    the start of a longer canary-filled array.  After the call every canary
+    outside Y and past k is intact, and Y equals, bit for bit, the output of
+    the same call into a contiguous tensor."""
+    rng = np.random.default_rng(n + d + m)
+    A = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    B = (rng.standard_normal((d, m)) / np.sqrt(d)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Ad = torch.from_numpy(A).to("cuda:0").to(tdt)
+    Bd = torch.from_numpy(B).to("cuda:0").to(tdt)
+    info = rmm.plan_info(Ad, Bd, rho)
+    assert info["route"] == route and info["gemm"] == gemm, info
+    Y0, i0 = rmm.matmul(Ad, Bd, rho)
+    k = rmm.k_of(rho, d)
+    top, bottom, left, right = 8, 256, 16, 264
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    canary = 0x5A5A if dtype == "bf16" else 0x5A5A5A5A
+    buf = torch.full((top + n + bottom, left + m + right), canary, dtype=itype, device="cuda:0")
+    Yv = buf.view(tdt)[top:top + n, left:left + m]
+    ibuf = torch.full((k + 256,), -7, dtype=torch.int32, device="cuda:0")
+    Y1, i1 = rmm.matmul(Ad, Bd, rho, out=Yv, idx_out=ibuf[:k])
+    torch.cuda.synchronize()
+    assert torch.equal(Yv.view(itype), Y0.view(itype))
+    outside = torch.ones(buf.shape, dtype=torch.bool, device="cuda:0")
+    outside[top:top + n, left:left + m] = False
+    assert bool((buf[outside] == canary).all())
+    assert torch.equal(ibuf[:k], i0) and bool((ibuf[k:] == -7).all())
+
+
+def _guarded(torch, shape, dtype, front=256, back=8192):
+    """A canary-filled 1-D buffer with a contiguous view of `shape` after
+    `front` elements (256 two-byte or four-byte elements: 16-byte aligned)."""
+    itype = torch.int16 if dtype in (torch.bfloat16,) else torch.int32
+    canary = 0x5A5A if itype == torch.int16 else 0x5A5A5A5A
+    numel = int(np.prod(shape))
+    buf = torch.full((front + numel + back,), canary, dtype=itype, device="cuda:0")
+    view = buf[front:front + numel].view(dtype).view(shape)
+
+    def intact():
+        return bool((buf[:front] == canary).all()) and bool((buf[front + numel:] == canary).all())
+
+    return view, intact
+
+
+def test_other_entry_points_stay_inside_their_outputs(rmm, torch):
+    """Canary guard bands before and after the outputs of the fused
+    attention, the 8-bit decode and GEMM (the GEMM's Y with a padded row
+    pitch) and the gated MLP block; each result equals the same call's
+    result into freshly allocated outputs, bit for bit."""
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    dev = "cuda:0"
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, device=dev, generator=g) * scale).to(torch.bfloat16)
+
+    # fused attention: 8 query heads over 2 key/value heads, 200 causal queries
+    q, kk, v = randn(8, 200, 128), randn(2, 200, 128), randn(2, 200, 128)
+    O0, I0 = rmm.attention(q, kk, v, 0.5)
+    O, o_ok = _guarded(torch, (8, 200, 128), torch.bfloat16)
+    I, i_ok = _guarded(torch, tuple(I0.shape), torch.int32)
+    rmm.attention(q, kk, v, 0.5, out=O, idx_out=I)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O0) and torch.equal(I, I0) and o_ok() and i_ok()
+
+    # 8-bit decode, wide enough for the selection inside the GEMV; ragged last column block
+    d, m = 1000, 14352
+    a = randn(d)
+    codes = torch.randint(-127, 128, (d, m), device=dev, generator=g, dtype=torch.int32).to(torch.int8)
+    scale = torch.rand(m, device=dev, generator=g) * 0.01
+    y0, j0 = rmm.decode_wq(a, codes, scale, 0.7, "int8")
+    y, y_ok = _guarded(torch, (m,), torch.bfloat16)
+    j, j_ok = _guarded(torch, tuple(j0.shape), torch.int32)
+    rmm.decode_wq(a, codes, scale, 0.7, "int8", out=y, idx_out=j)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(j, j0) and y_ok() and j_ok()
+
+    # 8-bit GEMM (n, d multiples of 8, m of 16; ragged against its tiles) with
+    # Y's rows m + 40 apart inside a canary-filled block
+    n, d, m = 296, 520, 272
+    A = randn(n, d)
+    codes = torch.randint(-127, 128, (d, m), device=dev, generator=g, dtype=torch.int32).to(torch.int8)
+    scale = torch.rand(m, device=dev, generator=g) * 0.01
+    Y0, _ = rmm.matmul_wq(A, codes, scale, 0.6, "int8")
+    buf = torch.full((n + 16, m + 40), 0x5A5A, dtype=torch.int16, device=dev)
+    Yv = buf.view(torch.bfloat16)[8:8 + n, 16:16 + m]
+    rmm.matmul_wq(A, codes, scale, 0.6, "int8", out=Yv)
+    torch.cuda.synchronize()
+    outside = torch.ones(buf.shape, dtype=torch.bool, device=dev)
+    outside[8:8 + n, 16:16 + m] = False
+    assert torch.equal(Yv, Y0) and bool((buf[outside] == 0x5A5A).all())
+
+    # gated MLP block
+    n, d, m = 64, 256, 512
+    x = randn(n, d)
+    Wgu = rmm.gated_weights(randn(d, m, scale=d ** -0.5), randn(d, m, scale=d ** -0.5))
+    Wd = randn(m, d, scale=m ** -0.5)
+    Y0 = rmm.gated_mlp(x, Wgu, Wd, 0.8, 0.8)[0]
+    Y, y_ok = _guarded(torch, (n, d), torch.bfloat16)
+    rmm.gated_mlp(x, Wgu, Wd, 0.8, 0.8, out=Y)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y0) and y_ok()
