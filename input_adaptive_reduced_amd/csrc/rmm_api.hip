@@ -284,9 +284,16 @@ rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n,
     p.chunks_h = (n + 255) / 256 * 2;
     p.gc_h = gemm_choose_transposed(n, d, p.k_h, m);
     if (p.gc_h.tile != 5) {
-        if (!gemm_tdma_fits(p.kpad_h, 1, m)) return RMM_ERR_UNSUPPORTED;
+        // few output tiles (a short block of tokens): the two-operand kernel
+        // with as many K splits as fill the chip (at least 16 K steps each)
+        // and at least as many as its LDS row list needs
+        const int64_t tiles = ((n + 255) / 256) * ((d + 255) / 256), ksteps = p.kpad_h / 64;
+        int64_t s = std::min((256 + tiles - 1) / tiles, ksteps / 16);
+        if (s < 1) s = 1;
+        while (s < 64 && !gemm_tdma_fits(p.kpad_h, (int)s, m)) ++s;
+        if (!gemm_tdma_fits(p.kpad_h, (int)s, m)) return RMM_ERR_UNSUPPORTED;
         p.gc_h.tile = 5;
-        p.gc_h.splits = 1;
+        p.gc_h.splits = (int)s;
     }
     size_t off = 0;
     auto take = [&](size_t bytes) {

@@ -138,6 +138,18 @@ def test_plan_info_on_host(lib):
     assert lib.rmm_plan_info(ctypes.byref(ds), 0.5, None) == 1          # NULL output
 
 
+def test_gated_mlp_sizes_on_host(lib):
+    """The gated block is supported for short token blocks too: the Down
+    stage then splits K so that its LDS row list fits (no GPU call)."""
+    SZ_MAX = ctypes.c_size_t(-1).value
+    ws = lib.rmm_gated_mlp_workspace_size
+    for n in (8, 64, 512, 768, 1024, 2048):
+        assert ws(n, 4096, 14336, 0.8, 0.8) != SZ_MAX, n
+    assert ws(64, 1024, 14336, 0.8, 0.8) != SZ_MAX
+    assert ws(6, 4096, 14336, 0.8, 0.8) == SZ_MAX         # n % 8 != 0
+    assert ws(64, 4096, 14330, 0.8, 0.8) == SZ_MAX        # m % 32 != 0
+
+
 def test_attention_and_decode_wq_host_checks(lib):
     """Workspace sizing and argument checks of rmm_attention and rmm_decode_wq
     are host-only: they return before any GPU call (fake, aligned pointers)."""

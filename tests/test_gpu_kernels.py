@@ -389,3 +389,54 @@ def test_other_entry_points_stay_inside_their_outputs(rmm, torch):
     rmm.gated_mlp(x, Wgu, Wd, 0.8, 0.8, out=Y)
     torch.cuda.synchronize()
     assert torch.equal(Y, Y0) and y_ok()
+
+
+RACE_PROBES = [
+    # (what, repeats): the hot kernels at their full workload shapes, each call
+    # compared bit for bit with the first (an LDS or cross-wave race shows up
+    # as a run-to-run difference)
+    ("tdma8 4096x4096x4096 rho 0.8", 100),
+    ("tdma8 split K 2048x14336x4096 rho 0.8", 50),
+    ("fused attention 32 heads x 4096 rho 0.5", 100),
+    ("decode 1x8192x28672 rho 0.8", 100),
+    ("gated MLP 512x4096x14336 rho 0.8", 30),
+]
+
+
+@pytest.mark.parametrize("what,repeats", RACE_PROBES, ids=[r[0].split()[0] + "-" + r[0].split()[1] for r in RACE_PROBES])
+def test_race_probe_repeats(rmm, torch, what, repeats):
+    g = torch.Generator(device="cuda:0").manual_seed(21)
+    dev = "cuda:0"
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, device=dev, generator=g) * scale).to(torch.bfloat16)
+
+    if what.startswith("tdma8"):
+        n, d, m = (4096, 4096, 4096) if "split" not in what else (2048, 14336, 4096)
+        A = (torch.randn(n, d, device=dev, generator=g) * torch.exp(torch.randn(d, device=dev, generator=g))).to(
+            torch.bfloat16)
+        B = randn(d, m, scale=d ** -0.5)
+        info = rmm.plan_info(A, B, 0.8)
+        assert info["gemm"] == "tdma" and (info["splits"] > 1) == ("split" in what), info
+        call = lambda: rmm.matmul(A, B, 0.8)  # noqa: E731
+    elif what.startswith("fused attention"):
+        q, k, v = randn(32, 4096, 128), randn(8, 4096, 128), randn(8, 4096, 128)
+        call = lambda: rmm.attention(q, k, v, 0.5, causal=True)  # noqa: E731
+    elif what.startswith("decode"):
+        a = (torch.randn(1, 8192, device=dev, generator=g) * torch.exp(torch.randn(8192, device=dev, generator=g))).to(
+            torch.bfloat16)
+        B = randn(8192, 28672, scale=8192 ** -0.5)
+        assert rmm.plan_info(a, B, 0.8)["route"] == "decode"
+        call = lambda: rmm.matmul(a, B, 0.8)  # noqa: E731
+    else:
+        n, d, m = 512, 4096, 14336
+        x = randn(n, d)
+        Wgu = rmm.gated_weights(randn(d, m, scale=d ** -0.5), randn(d, m, scale=d ** -0.5))
+        Wd = randn(m, d, scale=m ** -0.5)
+        call = lambda: rmm.gated_mlp(x, Wgu, Wd, 0.8, 0.8)  # noqa: E731
+    first = [t.clone() for t in call()]
+    for r in range(repeats - 1):
+        got = call()
+        for a_, b_ in zip(got, first):
+            assert torch.equal(a_, b_), (what, r)
+    torch.cuda.synchronize()

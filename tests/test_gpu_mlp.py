@@ -90,6 +90,8 @@ MLP = [
     (512, 1024, 2048, 0.8, 0.7, True),
     (264, 520, 1056, 0.5, 0.5, True),       # ragged tiles in every dimension
     (128, 256, 512, 1.0, 1.0, True),        # every index kept
+    (64, 1024, 14336, 0.8, 0.8, True),      # a short block: Down over 4 output tiles in 11 K splits
+    (512, 4096, 14336, 0.8, 0.8, False),    # the 8B block on 512 tokens: Down in 8 K splits
     (2048, 4096, 14336, 0.8, 0.8, False),   # the 8B MLP block, sampled rows of h and Y (sets in full)
 ]
 
