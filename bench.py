@@ -30,7 +30,14 @@ The same JSON line carries
     (full norms and selection, a sample of output rows, extrapolated), and
     ``parity``: the GPU's kept set and sampled output rows against it.
 
+With ``--jsonl FILE`` every measured (workload, rho) point is also appended
+to FILE as a record of its own (the sweep points and the headline, with the
+input digest, a digest of the library sources, ROCm and torch versions), and
+``--resume`` reuses sweep points already in FILE for the same inputs and
+sources instead of timing them again (the headline is always measured).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+                       [--jsonl FILE [--resume]]
 """
 from __future__ import annotations
 
@@ -93,6 +100,45 @@ def log(*a):
 def source_digest(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+def library_digest():
+    """sha256 over the library's HIP sources and headers, in name order."""
+    import glob
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "input_adaptive_reduced_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")) +
+                    [os.path.join(ROOT, "include", "rmm.h")]):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_jsonl(path):
+    rows = []
+    if path and os.path.exists(path):
+        with open(path) as f:
+            for ln in f:
+                ln = ln.strip()
+                if ln:
+                    try:
+                        rows.append(json.loads(ln))
+                    except ValueError:
+                        log(f"{path}: skipping a line that is not JSON")
+    return rows
+
+
+def reusable_point(rows, workload, rho, full_path, inputs, lib):
+    """The last sweep record of FILE for this point, inputs and library sources."""
+    if inputs is None:
+        return None
+    for r in reversed(rows):
+        if (r.get("kind") == "sweep" and r.get("workload") == workload and r.get("rho") == rho
+                and r.get("full_path") == full_path and r.get("inputs_sha256") == inputs
+                and r.get("library_sha256") == lib):
+            return r
+    return None
 
 
 # rocprofv3 FETCH_SIZE reads half the bytes a streaming read moves on this chip and
@@ -286,6 +332,7 @@ class WQRunner:
         dec = synthetic.make_decode_case(base)
         codes, scale = synthetic.quantize_columns(base.B, fmt)
         self.a_host, self.codes_host, self.scale_host = dec.A, codes, scale
+        self.sha256 = synthetic.sha256_of(synthetic.as_bf16_bits(dec.A), codes, scale)
 
         def up(x):
             bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
@@ -395,6 +442,7 @@ class AttnRunner:
         self.torch, self.rmm = torch, rmm
         dev = torch.device("cuda:0")
         Q, K, V = synthetic.make_attention_case()
+        self.sha256 = synthetic.sha256_of(*(synthetic.as_bf16_bits(x) for x in (Q, K, V)))
 
         def up(x):
             bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
@@ -457,6 +505,7 @@ class MLPRunner:
         self.torch, self.rmm = torch, rmm
         dev = torch.device("cuda:0")
         c = synthetic.make_mlp_case()
+        self.sha256 = synthetic.sha256_of(*(synthetic.as_bf16_bits(x) for x in (c.x, c.Wg, c.Wu, c.Wd)))
 
         def up(x):
             bits = synthetic.as_bf16_bits(np.ascontiguousarray(x)).view(np.int16)
@@ -820,11 +869,16 @@ def main(argv=None):
     ap.add_argument("--calibrate-mfma", action="store_true",
                     help="only run the matrix-core ceiling probe and print its TFLOP/s")
     ap.add_argument("--no-mfma-ceiling", action="store_true", help="skip the matrix-core ceiling probe")
+    ap.add_argument("--jsonl", metavar="FILE", help="also append one record per measured (workload, rho) point")
+    ap.add_argument("--resume", action="store_true",
+                    help="with --jsonl: reuse sweep points FILE already holds for the same inputs and sources")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: store the HBM bytes of --workload's dominant kernel from the counter_collection "
                          "CSVs of two rocprofv3 runs of this script (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) "
                          "in profiles/traffic.json, and exit")
     args = ap.parse_args(argv)
+    if args.resume and not args.jsonl:
+        ap.error("--resume needs --jsonl")
     if args.record_traffic:
         return record_traffic(args.workload, *args.record_traffic)
 
@@ -879,10 +933,27 @@ def main(argv=None):
     graph = not args.no_graph
     log(f"workload {args.workload}: {wl['label']}; copies={runner.copies} graph={graph}")
 
+    inputs_sha = getattr(runner, "sha256", None)
+    lib_sha = library_digest()
+    previous = read_jsonl(args.jsonl) if args.resume else []
+    common = {"workload": args.workload, "n": runner.n, "d": runner.d, "m": runner.m, "batch": runner.batch,
+              "inputs_sha256": inputs_sha, "library_sha256": lib_sha, "hip": getattr(torch.version, "hip", None),
+              "torch": torch.__version__, "graph": graph, "steps": args.steps, "warmup": args.warmup}
+
     # the dense comparison and the rho sweep run first: the headline below then starts
     # from a GPU at its working clock, not from the cold-start transient
     sweep = []
-    if not args.no_sweep:
+    points = [(r, full) for r in wl["sweep"]
+              for full in ((False, True) if r == 1.0 and not (is_mlp or is_wq or is_attn or is_wqgemm) else (False,))]
+    reused = {pt: reusable_point(previous, args.workload, pt[0], pt[1], inputs_sha, lib_sha) for pt in points}
+    if not args.no_sweep and all(reused.values()):
+        for pt in points:
+            ent = {kk: reused[pt][kk] for kk in ("rho", "k", "full_path", "ms", "tflops", "dense_ms",
+                                                  "speedup_vs_dense", "ideal_speedup") if kk in reused[pt]}
+            ent["reused"] = True
+            sweep.append(ent)
+        log(f"sweep: all {len(points)} points reused from {args.jsonl}")
+    elif not args.no_sweep:
         try:
             runner.dense(0)
             torch.cuda.synchronize()
@@ -892,19 +963,18 @@ def main(argv=None):
         else:
             dense_ms = time_steps(torch, runner.dense, args.steps, args.warmup, runner.copies, graph)
             log(f"dense {'fused attention' if is_attn else 'torch.matmul'}: {dense_ms * 1e3:.1f} us/step")
-        for r in wl["sweep"]:
-            for full in ((False, True) if r == 1.0 and not (is_mlp or is_wq or is_attn or is_wqgemm) else (False,)):
-                t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
-                               runner.copies, graph)
-                ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
-                       "tflops": runner.flops(r) / (t * 1e-3) / 1e12}
-                if dense_ms:
-                    ent["dense_ms"] = dense_ms
-                    ent["speedup_vs_dense"] = dense_ms / t
-                    ent["ideal_speedup"] = 1.0 / (ent["k"] / runner.d)
-                sweep.append(ent)
-                log(f"  rho={r}{' full' if full else ''}: {t * 1e3:.1f} us, {ent['tflops']:.1f} TFLOP/s"
-                    + (f", x{ent['speedup_vs_dense']:.2f} vs dense" if dense_ms else ""))
+        for r, full in points:
+            t = time_steps(torch, lambda i: runner.call(i, r, full), args.steps, args.warmup,
+                           runner.copies, graph)
+            ent = {"rho": r, "k": rmm.k_of(r, runner.d), "full_path": full, "ms": t,
+                   "tflops": runner.flops(r) / (t * 1e-3) / 1e12}
+            if dense_ms:
+                ent["dense_ms"] = dense_ms
+                ent["speedup_vs_dense"] = dense_ms / t
+                ent["ideal_speedup"] = 1.0 / (ent["k"] / runner.d)
+            sweep.append(ent)
+            log(f"  rho={r}{' full' if full else ''}: {t * 1e3:.1f} us, {ent['tflops']:.1f} TFLOP/s"
+                + (f", x{ent['speedup_vs_dense']:.2f} vs dense" if dense_ms else ""))
 
     clocks = ClockSampler(torch)
     ms, med = time_steps(torch, lambda i: runner.call(i, rho), args.steps, args.warmup, runner.copies, graph,
@@ -1030,6 +1100,16 @@ def main(argv=None):
     }
     if rank == 0:
         print(json.dumps(line), flush=True)
+        if args.jsonl:
+            now = time.strftime("%Y-%m-%dT%H:%M:%S%z")
+            with open(args.jsonl, "a") as f:
+                for ent in sweep:
+                    if not ent.get("reused"):
+                        f.write(json.dumps({"kind": "sweep", **common, **ent, "time": now}) + "\n")
+                f.write(json.dumps({"kind": "headline", **common, "rho": rho, "k": k, "full_path": False,
+                                    "ms": ms, "median_ms": med, "tflops": value, "roofline": roof,
+                                    "clocks": line["clocks"], "parity": line["parity"], "cpu_baseline": cpu,
+                                    "time": now}) + "\n")
     return 0
 
 
