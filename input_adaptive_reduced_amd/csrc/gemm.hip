@@ -503,12 +503,16 @@ __device__ __forceinline__ void store_tile_256(const GemmArgs &g, const f32x16_t
 //  * writes h^T to Yt when Yt is given (staged as 64 rows of the wave's 128
 //    h rows, 136 elements apart; 16 stores of 4 rows x 256 bytes), with the
 //    sums of squares of the bf16 values of each column over the wave's rows
-//    below n, in row order, into npart[128-row chunk][column]: the column
-//    norms of h for the next projection's selection, without another pass.
+//    below n, in row order; the wave of the lower 128 rows adds its sums to
+//    those of the upper wave (through `xch`, 128 floats of LDS) and writes
+//    npart[256-row chunk][column]: the column norms of h for the next
+//    projection's selection, without another pass.  Every wave of the
+//    workgroup must call this (it holds a workgroup barrier).
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
 
 __device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x16_t (&acc)[4][4], uint4 *stage,
-                                                  int64_t m0, int64_t hcol0, int tm, int wm, int lane) {
+                                                  float *xch, int64_t m0, int64_t hcol0, int tm, int wm, int wn,
+                                                  int lane) {
     constexpr int CPW = 8;  // 16-byte chunks per staged row (64 outputs)
     const int64_t mh = g.m / 2;
     uint32_t hp[4][2][4][2];  // [i][jj][q][half]: bf16 pairs of h
@@ -596,7 +600,10 @@ __device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x1
                 sq = fmaf(hi, hi, sq);
             }
         }
-        if (hcol0 + lane < mh) g.npart[(int64_t)(2 * tm + wm) * mh + hcol0 + lane] = sq;
+        // the tile's 256 rows in order: rows 0..127 (wave wm = 0), then 128..255
+        if (wm == 1) xch[wn * 64 + lane] = sq;
+        __syncthreads();
+        if (wm == 0 && hcol0 + lane < mh) g.npart[(int64_t)tm * mh + hcol0 + lane] = sq + xch[wn * 64 + lane];
     }
 }
 
@@ -1293,8 +1300,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
     static_assert(BQ == 0 || kTdmaListRowsQ * 2 >= 2 * BUF * 16, "the list region stages two 32 KB tiles");
     uint4 *stage = w == 0 ? sA0 : w == 1 ? sA1 : BQ ? reinterpret_cast<uint4 *>(sIdx) + (w - 2) * BUF
                                                     : w == 2 ? sB0 : sB1;
-    if constexpr (EPI == 1)
-        store_tile_swiglu(g, acc, stage, m0, n0 / 2 + wn * 64, tm, wm, lane);
+    if constexpr (EPI == 1)  // the row list is no longer read: its LDS takes the exchange of column sums
+        store_tile_swiglu(g, acc, stage, reinterpret_cast<float *>(sIdx), m0, n0 / 2 + wn * 64, tm, wm, wn, lane);
     else
         store_tile_256<SPLIT, BQ != 0>(g, acc, stage, m0, n0, b, split, wm, wn, lane);
 }

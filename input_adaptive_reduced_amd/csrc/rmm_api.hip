@@ -278,10 +278,10 @@ rmm_status_t mlp_plan(const void *x, const void *Wgu, const void *Wd, int64_t n,
     p.gc.tile = 5;
     p.gc.splits = 1;
     p.cp = colnorm_transpose_plan(n, d);
-    // Down: h^T and the column sums of h^2 per 128-row chunk come from the
+    // Down: h^T and the column sums of h^2 per 256-row chunk come from the
     // SwiGLU epilogue; its selection, then the two-operand GEMM over h^T rows
     p.kpad_h = (p.k_h + 127) / 128 * 128;
-    p.chunks_h = (n + 255) / 256 * 2;
+    p.chunks_h = (n + 255) / 256;
     p.gc_h = gemm_choose_transposed(n, d, p.k_h, m);
     if (p.gc_h.tile != 5) {
         // few output tiles (a short block of tokens): the two-operand kernel

@@ -138,7 +138,7 @@ struct GemmArgs {
     float alpha;
     int epi;             // tile 5 only: 0 = Y, 1 = SwiGLU of interleaved gate/up column blocks (see gemm.hip)
     uint16_t *Yt;        // epi 1: h^T (m/2 x n, rows n apart), or NULL
-    float *npart;        // epi 1 with Yt: column sums of h^2 per 128-row chunk [chunk][m/2]
+    float *npart;        // epi 1 with Yt: column sums of h^2 per 256-row chunk [chunk][m/2]
     int bq;              // tile 5 only: B element format, 0 = bf16, 1 = OCP FP8 E4M3 codes, 2 = int8 codes
                          // (8-bit B: ldb in bytes, rows of m codes; b_bytes in bytes)
     const float *colscale;  // bq != 0: one fp32 scale per output column (Y = alpha * scale[c] * sum)

@@ -73,11 +73,19 @@ def _sel_case(rng, d, kind):
         s[rng.integers(0, d, size=max(1, d // 7))] = 0.0
         s[rng.integers(0, d, size=max(1, d // 50))] = np.inf
         return s
+    if kind == "nan_and_inf":  # NaN ranks above +Inf (any payload or sign), NaNs tie among themselves
+        s = np.abs(rng.standard_normal(d)).astype(np.float32)
+        s[rng.integers(0, d, size=max(1, d // 40))] = np.inf
+        nan_at = rng.integers(0, d, size=max(1, d // 30))
+        s[nan_at] = np.nan
+        u = s.view(np.uint32)
+        u[nan_at[::2]] = np.uint32(0xffc00001)  # a negative NaN with a payload
+        return s
     raise KeyError(kind)
 
 
 @pytest.mark.parametrize("d", [1, 2, 7, 128, 1000, 1024, 2049, 2432, 3008, 4032, 4096, 14336, 30000])
-@pytest.mark.parametrize("kind", ["random", "ties", "bf16", "const", "zeros_and_inf"])
+@pytest.mark.parametrize("kind", ["random", "ties", "bf16", "const", "zeros_and_inf", "nan_and_inf"])
 def test_select_exact(rmm, torch, d, kind):
     rng = np.random.default_rng(d + len(kind))
     s = _sel_case(rng, d, kind)
