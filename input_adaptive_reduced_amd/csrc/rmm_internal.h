@@ -79,11 +79,12 @@ constexpr int64_t kFusedSelectMaxD = 16384;
 // Norms from the row-chunk partials and the selection in one launch (one
 // workgroup per batch entry, every partial load in flight at once).  One
 // workgroup reads all chunks x d partials, so this pays only while they are
-// few: d <= 4096 and at most 256 KB of partials, or d <= 16384 and at most
-// eight row chunks (beyond that, on MI355X, a wide finalize launch plus the
-// selection launch is faster).  d % 4 == 0, part 16-byte aligned.
+// few: d <= 16384 and at most 256 KB of partials (beyond that, on MI355X, a
+// wide finalize launch plus the selection launch is faster: 459 KB at
+// d = 14336 took 18.8 us against 3.7 + 12.0).  d % 4 == 0, part 16-byte
+// aligned.
 inline bool norm_select_ok(int64_t chunks, int64_t d) {
-    return d % 4 == 0 && ((d <= 4096 && chunks * d <= 65536) || (d <= 16384 && chunks <= 8));
+    return d % 4 == 0 && d <= 16384 && chunks * d <= 65536;
 }
 hipError_t launch_norm_select(const float *part, int64_t chunks, int64_t d, int64_t batch, int64_t k, int32_t *idx,
                               int64_t ld_idx, int32_t *idx_pad, int64_t ld_pad, hipStream_t stream);
