@@ -2276,13 +2276,19 @@ __global__ __launch_bounds__(256) void pack_short_rows_kernel(const uint16_t *__
     const int64_t row = r0 + tid;
     const int64_t blk = row >> 5;
     if (row >= ((rows + 31) & ~(int64_t)31)) return;  // past the last 32-row block of the output
+    // eight kept columns per piece: their numbers in one scalar load, then
+    // eight LDS reads issued together (padding entries read column 0 and are
+    // replaced by zero), so no read waits on another
+#pragma unroll 2
     for (int c = 0; c < (int)(kpad / 8); ++c) {
+        int32_t j[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) j[e] = idx[c * 8 + e];  // uniform: scalar loads
         uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int32_t j = idx[c * 8 + e];  // uniform: scalar load
-            h[e] = (j >= 0 && tid < nr) ? mine[j] : 0u;
-        }
+        for (int e = 0; e < 8; ++e) h[e] = mine[max(j[e], 0)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (j[e] >= 0 && tid < nr) ? h[e] : 0u;
         *reinterpret_cast<uint4 *>(Dp + ((blk * (kpad >> 4) + (c >> 1)) * 64 + (c & 1) * 32 + (row & 31)) * 8) =
             make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
     }
