@@ -607,6 +607,38 @@ __device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x1
     }
 }
 
+// The kept-row list of a workgroup's K range into LDS as 16-bit row numbers
+// (0xffff for list padding, whose rows then read as zero): entries
+// [0, nvalid) from src, the rest up to nlist padding.  16-byte loads of four
+// entries, four per thread in flight before the first store, so the list
+// costs one memory round trip per 16 NT entries instead of one per entry.
+// nvalid > 0 and nlist are multiples of 4; src is 16-byte aligned.  Every
+// load is unconditional (entries past nvalid load entry 0 and are replaced),
+// so the one wait before the stores covers all four.
+template <int NT>
+__device__ __forceinline__ void load_row_list(const int32_t *__restrict__ src, int nvalid, int nlist, uint16_t *dst,
+                                              int tid) {
+    const int nch = nlist / 4;
+    for (int base = 0; base < nch; base += 4 * NT) {
+        int4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ch = base + u * NT + tid;
+            q[u] = *reinterpret_cast<const int4 *>(src + (ch * 4 < nvalid ? ch * 4 : 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ch = base + u * NT + tid;
+            const bool ok = ch * 4 < nvalid;
+            const uint32_t e0 = (!ok || q[u].x < 0) ? 0xffffu : (uint32_t)q[u].x;
+            const uint32_t e1 = (!ok || q[u].y < 0) ? 0xffffu : (uint32_t)q[u].y;
+            const uint32_t e2 = (!ok || q[u].z < 0) ? 0xffffu : (uint32_t)q[u].z;
+            const uint32_t e3 = (!ok || q[u].w < 0) ? 0xffffu : (uint32_t)q[u].w;
+            if (ch < nch) *reinterpret_cast<uint2 *>(dst + ch * 4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        }
+    }
+}
+
 // Reduced product with A fragments loaded straight from HBM into registers
 // (256x256 output tile, 4 waves in a 2x2 grid, each wave 128x128).
 //
@@ -957,10 +989,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bdma_kernel(GemmArgs g) {
     if (kt0 < kt1) {
         // list entries for the padded range plus the two steps loaded past it
         const int nlist = (kte - kt0 + 2) * BK;  // <= kBdmaListRows (checked by the host)
-        for (int t = tid; t < nlist; t += 256) {
-            const int32_t v = t < (kt1 - kt0) * BK ? idx[kt0 * BK + t] : -1;
-            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
-        }
+        load_row_list<256>(idx + kt0 * BK, (kt1 - kt0) * BK, nlist, sIdx, tid);
         __syncthreads();
         load_rows(kt0, rows);
         dma_b(sB0, 0, 8, rows);
@@ -1265,10 +1294,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tdma_kernel(GemmArgs g) {
 
     if (kt0 < kt1) {
         const int nlist = (kte - kt0 + 2) * BK;
-        for (int t = tid; t < nlist; t += 256) {
-            const int32_t v = t < (kt1 - kt0) * BK ? idx[kt0 * BK + t] : -1;
-            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
-        }
+        load_row_list<256>(idx + kt0 * BK, (kt1 - kt0) * BK, nlist, sIdx, tid);
         __syncthreads();
         // steps kt0 (both operands) and kt0+1 (A; its B is loaded in step kt0's sub-step 0)
         load_rows(kt0, rows);
@@ -1516,10 +1542,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tdma8_kernel(GemmArgs g) {
 
     if (kt0 < kt1) {
         const int nlist = (kte - kt0 + 2) * BK;
-        for (int t = tid; t < nlist; t += 512) {
-            const int32_t v = t < (kt1 - kt0) * BK ? idx[kt0 * BK + t] : -1;
-            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
-        }
+        load_row_list<512>(idx + kt0 * BK, (kt1 - kt0) * BK, nlist, sIdx, tid);
         __syncthreads();
         // steps kt0 (both operands) and kt0+1 (A; its B is loaded in step kt0's sub-step 0)
         load_rows(kt0, rows);
@@ -2513,8 +2536,11 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
             gemm_stream_kernel<8><<<grid, 256, 0, stream>>>(a);
         return hipGetLastError();
     }
+    // the row-list kernels read their lists in 16-byte pieces
+    const bool list_aligned = ((uintptr_t)a.idx & 15) == 0 && a.ld_idx % 4 == 0;
     if (c.tile == 5) {
-        if (a.bmode != 0 || a.batch != 1 || !tdma_ok(a.kpad, a.splits, 0, a.bq)) return hipErrorInvalidValue;
+        if (a.bmode != 0 || a.batch != 1 || !list_aligned || !tdma_ok(a.kpad, a.splits, 0, a.bq))
+            return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
         dim3 grid((unsigned)tiles, (unsigned)a.splits, 1);
         if (a.bq != 0) {
@@ -2555,7 +2581,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
     }
     if (c.tile == 2 || c.tile == 4) {
         if (a.bmode != 0) return hipErrorInvalidValue;
-        if (c.tile == 4 && !bdma_ok(a.kpad, a.splits, 0, 0)) return hipErrorInvalidValue;
+        if (c.tile == 4 && (!list_aligned || !bdma_ok(a.kpad, a.splits, 0, 0))) return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
         dim3 grid((unsigned)tiles, (unsigned)a.splits, (unsigned)a.batch);
         if (c.tile == 4) {
