@@ -608,17 +608,18 @@ __device__ __forceinline__ void store_tile_swiglu(const GemmArgs &g, const f32x1
 }
 
 // The kept-row list of a workgroup's K range into LDS as 16-bit row numbers
-// (0xffff for list padding, whose rows then read as zero): entries
-// [0, nvalid) from src, the rest up to nlist padding.  16-byte loads of four
-// entries, four per thread in flight before the first store, so the list
-// costs one memory round trip per 16 NT entries instead of one per entry.
-// nvalid > 0 and nlist are multiples of 4; src is 16-byte aligned.  Every
-// load is unconditional (entries past nvalid load entry 0 and are replaced),
-// so the one wait before the stores covers all four.
+// (0xffff for -1 entries and list padding, whose rows then read as zero):
+// entries [0, nvalid) from src, the rest up to nlist (rounded up to a
+// multiple of 4) padding.  16-byte loads of four entries, four per thread in
+// flight before the first store, so the list costs one memory round trip per
+// 16 NT entries instead of one per entry.  nvalid > 0; src is 16-byte aligned
+// and readable up to nvalid rounded up to a multiple of 4.  Every load is
+// unconditional (pieces past nvalid load piece 0 and are replaced), so the
+// one wait before the stores covers all four.
 template <int NT>
 __device__ __forceinline__ void load_row_list(const int32_t *__restrict__ src, int nvalid, int nlist, uint16_t *dst,
                                               int tid) {
-    const int nch = nlist / 4;
+    const int nch = (nlist + 3) / 4;
     for (int base = 0; base < nch; base += 4 * NT) {
         int4 q[4];
 #pragma unroll
@@ -629,12 +630,12 @@ __device__ __forceinline__ void load_row_list(const int32_t *__restrict__ src, i
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int ch = base + u * NT + tid;
-            const bool ok = ch * 4 < nvalid;
-            const uint32_t e0 = (!ok || q[u].x < 0) ? 0xffffu : (uint32_t)q[u].x;
-            const uint32_t e1 = (!ok || q[u].y < 0) ? 0xffffu : (uint32_t)q[u].y;
-            const uint32_t e2 = (!ok || q[u].z < 0) ? 0xffffu : (uint32_t)q[u].z;
-            const uint32_t e3 = (!ok || q[u].w < 0) ? 0xffffu : (uint32_t)q[u].w;
-            if (ch < nch) *reinterpret_cast<uint2 *>(dst + ch * 4) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+            const int t = ch * 4;
+            const uint32_t e0 = (t >= nvalid || q[u].x < 0) ? 0xffffu : (uint32_t)q[u].x;
+            const uint32_t e1 = (t + 1 >= nvalid || q[u].y < 0) ? 0xffffu : (uint32_t)q[u].y;
+            const uint32_t e2 = (t + 2 >= nvalid || q[u].z < 0) ? 0xffffu : (uint32_t)q[u].z;
+            const uint32_t e3 = (t + 3 >= nvalid || q[u].w < 0) ? 0xffffu : (uint32_t)q[u].w;
+            if (ch < nch) *reinterpret_cast<uint2 *>(dst + t) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
         }
     }
 }
@@ -786,10 +787,7 @@ __global__ __launch_bounds__(256, 1) void gemm_adirect_kernel(GemmArgs g) {
     };
 
     if (kt0 < kt1) {
-        for (int t = tid; t < (kt1 - kt0) * BK; t += NT) {
-            const int32_t v = idx[kt0 * BK + t];
-            sIdx[t] = v < 0 ? (uint16_t)0xffff : (uint16_t)v;
-        }
+        load_row_list<NT>(idx + kt0 * BK, (kt1 - kt0) * BK, (kt1 - kt0) * BK, sIdx, tid);
         __syncthreads();
         load_rows(kt0, ix0);
         load_rows(kt0 + 1, ix1);
@@ -1649,7 +1647,7 @@ __global__ __launch_bounds__(512, 1) void gemm_gcol_kernel(GemmArgs g) {
     const uint32_t lda2 = (uint32_t)(g.lda * 2), ldb2 = (uint32_t)(g.ldb * 2);
 
     // set-up (entries -1 read as 0xffff, above every column)
-    for (int j = tid; j < k; j += NT) sIdx[j] = (uint16_t)idx[j];
+    load_row_list<NT>(idx, k, k, sIdx, tid);
     __syncthreads();
     if (tid <= MAXWIN) {
         int lo = 0, hi = k;
@@ -2572,7 +2570,8 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         return hipGetLastError();
     }
     if (c.tile == 6) {
-        if (a.bmode != 0 || a.splits != 1 || a.k > kGcolMaxD || a.m % 8 || a.n < 1 || a.batch < 1)
+        if (a.bmode != 0 || a.splits != 1 || a.k > kGcolMaxD || a.k < 1 || a.m % 8 || a.n < 1 || a.batch < 1 ||
+            !list_aligned || a.ld_idx < (a.k + 3) / 4 * 4)
             return hipErrorInvalidValue;
         const int64_t T = ((a.n + 255) / 256) * ((a.m + 127) / 128) * a.batch;
         if (T > INT32_MAX) return hipErrorInvalidValue;
@@ -2580,7 +2579,7 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, const GemmConfig &c, hipStream_t 
         return hipGetLastError();
     }
     if (c.tile == 2 || c.tile == 4) {
-        if (a.bmode != 0) return hipErrorInvalidValue;
+        if (a.bmode != 0 || !list_aligned) return hipErrorInvalidValue;
         if (c.tile == 4 && (!list_aligned || !bdma_ok(a.kpad, a.splits, 0, 0))) return hipErrorInvalidValue;
         const int64_t tiles = ((a.n + 255) / 256) * ((a.m + 255) / 256);
         dim3 grid((unsigned)tiles, (unsigned)a.splits, (unsigned)a.batch);
