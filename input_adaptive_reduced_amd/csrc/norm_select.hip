@@ -179,95 +179,126 @@ __global__ __launch_bounds__(kNormThreads) void colnorm_rows_kernel(const uint16
 // bf16 column sums of squares that also write the transposed copy At (d x n,
 // rows ldt apart) of the block: the gather source of the two-operand GEMM,
 // whose kept rows At[I_t, :] are then contiguous like the rows of B.  The
-// pass reads A once, as the plain partial kernel does, and writes it once.
-// Workgroup: a 64-column strip x a chunk of 4 * TPW * 64 rows; wave w takes
-// the 64-row tiles w, w + 4, ...  Lane l owns row block rb = l / 8 (eight
-// rows) and column chunk cc = l % 8 (eight columns): eight 16-byte loads,
-// all issued before the first use, give it an 8 x 8 block, which it
-// transposes in registers with byte permutes and writes as eight 16-byte
-// pieces of At (each store instruction: eight 128-byte row runs).  Squares
-// are summed per lane in row order, then over the eight row blocks of the
-// wave (xor 8, 16, 32) and over the four waves in order: the partial of a
-// column and chunk has a fixed summation order.  n % 8 == 0, so a row block
-// below the chunk end is whole.
-template <int TPW>
-__global__ __launch_bounds__(kNormThreads) void colnorm_transpose_kernel(const uint16_t *__restrict__ A, int64_t n,
+// pass reads A once and writes it once, both in long row runs.  A workgroup
+// takes a TC-column strip and a chunk of rows and walks the chunk in TR-row
+// tiles.  A tile is loaded in 2*TC-byte row runs (16 bytes a lane), its
+// squares are summed per lane, and it is stored to LDS; after one barrier
+// each lane reads back an 8 x 8 block (eight 16-byte reads), transposes it
+// with byte permutes and writes it as one 16-byte piece of each of eight rows
+// of At, the lanes of a wave forming 2*TR-byte runs.  The next tile's loads
+// go out right after the barrier and land while the current tile is
+// transposed and written; two LDS buffers leave one barrier per tile.  The
+// 16-byte slots of a row are XOR-swizzled by its 8-row block, so the row
+// writes and the block reads both spread over the LDS banks.  Squares are
+// summed per lane in row order, then over the lanes and waves that share a
+// column in a fixed order: the partial of a column and chunk has a fixed
+// summation order.  n % 8 == 0 and d % 8 == 0, so a 16-byte piece or an
+// 8 x 8 block lies wholly inside or wholly outside the block.
+template <int TC, int TR, int NT>
+__global__ __launch_bounds__(NT) void colnorm_transpose_kernel(const uint16_t *__restrict__ A, int64_t n,
                                                                         int64_t d, int64_t lda,
                                                                         int64_t rows_per_chunk, int64_t a_bytes,
                                                                         uint16_t *__restrict__ At, int64_t ldt,
                                                                         float *__restrict__ part) {
-    __shared__ float red[4][64];
+    constexpr int CPR = TC / 8;                       // 16-byte pieces per tile row
+    constexpr int RPL = NT / CPR;           // tile rows per round of loads
+    constexpr int NL = TR / RPL;                      // loads per lane per tile
+    constexpr int RB = TR / 8;                        // 8-row blocks per tile
+    constexpr int NB = (TC / 8) * RB / NT;  // 8 x 8 blocks per lane per tile
+    constexpr int NW = NT / 64;
+    static_assert(NL >= 1 && NB >= 1 && (CPR & (CPR - 1)) == 0 && CPR <= 64 && TR % RPL == 0, "tile shape");
+    __shared__ uint4 buf[2][TR * CPR];
+    __shared__ float red[NW][TC];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int rb = lane >> 3, cc = lane & 7;
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int lc = tid % CPR, lr = tid / CPR;
+    const int64_t c0 = (int64_t)blockIdx.x * TC;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t r1 = min(n, r0 + rows_per_chunk);
-    const int64_t col = c0 + 8 * cc;
+    const int ntiles = (int)((r1 - r0 + TR - 1) / TR);
+    const int64_t lcol = c0 + 8 * lc;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A), (short)0, (int)a_bytes, 0x00020000);
-    uint4 v[TPW][8];
+    uint4 v[NL];
+    // rows past the chunk end (and columns past d) read as zero, with no traffic
+    auto load_tile = [&](int t) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int64_t rbase = r0 + (int64_t)(w + 4 * t) * 64 + 8 * rb;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int64_t row = rbase + q;
-            const uint32_t off = (row < r1 && col < d) ? (uint32_t)((row * lda + col) * 2) : 0x80000000u;
-            v[t][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        for (int j = 0; j < NL; ++j) {
+            const int64_t row = r0 + (int64_t)t * TR + lr + RPL * j;
+            const uint32_t off = (row < r1 && lcol < d) ? (uint32_t)((row * lda + lcol) * 2) : 0x80000000u;
+            v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
         }
-    }
+    };
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+        uint4 *b = buf[t & 1];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int64_t rbase = r0 + (int64_t)(w + 4 * t) * 64 + 8 * rb;
-        uint32_t wd[8][4];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            wd[q][0] = v[t][q].x;
-            wd[q][1] = v[t][q].y;
-            wd[q][2] = v[t][q].z;
-            wd[q][3] = v[t][q].w;
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int j = 0; j < NL; ++j) {
+            const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                const float lo = __uint_as_float(wd[q][h] << 16), hi = __uint_as_float(wd[q][h] & 0xffff0000u);
+                const float lo = __uint_as_float(wv[h] << 16), hi = __uint_as_float(wv[h] & 0xffff0000u);
                 acc[2 * h] = fmaf(lo, lo, acc[2 * h]);
                 acc[2 * h + 1] = fmaf(hi, hi, acc[2 * h + 1]);
             }
-        if (rbase < r1 && col < d) {
-            // column e of the block: the low (e even) or high (e odd) halves
-            // of word e / 2 of rows 0..7, paired into four words
+            const int r = lr + RPL * j;
+            b[r * CPR + (lc ^ ((r >> 3) & (CPR - 1)))] = v[j];
+        }
+        __syncthreads();
+        load_tile(t + 1);
+        const int64_t tr0 = r0 + (int64_t)t * TR;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                uint4 o;
-                o.x = __builtin_amdgcn_perm(wd[1][e >> 1], wd[0][e >> 1], sel);
-                o.y = __builtin_amdgcn_perm(wd[3][e >> 1], wd[2][e >> 1], sel);
-                o.z = __builtin_amdgcn_perm(wd[5][e >> 1], wd[4][e >> 1], sel);
-                o.w = __builtin_amdgcn_perm(wd[7][e >> 1], wd[6][e >> 1], sel);
-                *reinterpret_cast<uint4 *>(At + (col + e) * ldt + rbase) = o;
+        for (int q = 0; q < NB; ++q) {
+            const int blk = tid + q * NT;
+            const int rb = blk % RB, cb = blk / RB;
+            uint32_t wd[8][4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 x = b[(8 * rb + i) * CPR + (cb ^ (rb & (CPR - 1)))];
+                wd[i][0] = x.x;
+                wd[i][1] = x.y;
+                wd[i][2] = x.z;
+                wd[i][3] = x.w;
+            }
+            const int64_t row = tr0 + 8 * rb, col = c0 + 8 * cb;
+            if (row < r1 && col < d) {
+                // column e of the block: the low (e even) or high (e odd)
+                // halves of word e / 2 of rows 0..7, paired into four words
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    uint4 o;
+                    o.x = __builtin_amdgcn_perm(wd[1][e >> 1], wd[0][e >> 1], sel);
+                    o.y = __builtin_amdgcn_perm(wd[3][e >> 1], wd[2][e >> 1], sel);
+                    o.z = __builtin_amdgcn_perm(wd[5][e >> 1], wd[4][e >> 1], sel);
+                    o.w = __builtin_amdgcn_perm(wd[7][e >> 1], wd[6][e >> 1], sel);
+                    *reinterpret_cast<uint4 *>(At + (col + e) * ldt + row) = o;
+                }
             }
         }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float x = acc[e];
-        x += __shfl_xor(x, 8, 64);
-        x += __shfl_xor(x, 16, 64);
-        x += __shfl_xor(x, 32, 64);
+#pragma unroll
+        for (int o = CPR; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
         acc[e] = x;
     }
-    if (rb == 0) {
+    if (lane < CPR) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[w][8 * cc + e] = acc[e];
+        for (int e = 0; e < 8; ++e) red[w][8 * lc + e] = acc[e];
     }
     __syncthreads();
-    if (tid < 64 && c0 + tid < d)
-        part[(int64_t)blockIdx.y * d + c0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    for (int c = tid; c < TC; c += NT) {
+        if (c0 + c < d) {
+            float sum = red[0][c];
+#pragma unroll
+            for (int y = 1; y < NW; ++y) sum += red[y][c];
+            part[(int64_t)blockIdx.y * d + c0 + c] = sum;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ block scan
@@ -988,17 +1019,32 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
     return hipGetLastError();
 }
 
-// 512-row chunks where that still gives at least 512 workgroups, else 256
-// (measured on MI355X: 14.2 us for the 4096 x 4096 block, 26.7 us for
-// 2048 x 14336, reading and writing 4.3-4.7 TB/s).
+// Tiles of 128 columns x 128 rows (256-byte runs on both sides, 64 KB of
+// LDS: two workgroups per CU).  A chunk takes 1, 2 or 4 tiles: as many as
+// still give at least 256 workgroups, and more where that keeps the
+// partials within what the fused norm+select kernel takes.  Measured on
+// MI355X inside the product's step (2 to 8 rotated input copies): 24.9 us
+// for the 2048 x 14336 block (4 tiles per chunk) and 29.5 us for 4096 x 8192
+// (4), against 29.4 and 32.3 us for 64-column strips read in 128-byte runs
+// with every load issued up front; 4096 x 4096 (4 tiles, 8 chunks) 18.9 us
+// against 19.8.  Two tiles per chunk there (512 workgroups) took 17.5 us but
+// doubles the partials, which the selection then reads in 1.1 us more.
+constexpr int kTransTC = 128, kTransTR = 128, kTransThreads = 256, kTransMaxTiles = 4;
+constexpr int64_t kTransMinGroups = 256;
+
 ColnormPlan colnorm_transpose_plan(int64_t n, int64_t d) {
     ColnormPlan p;
     p.tc = 0;
-    p.strips = (int)((d + 63) / 64);
-    const int64_t big = (int64_t)p.strips * ((n + 511) / 512);
-    p.rows_per_chunk = big >= 512 ? 512 : 256;
-    p.rpt = (int)(p.rows_per_chunk / 256);
-    p.chunks = (int)((n + p.rows_per_chunk - 1) / p.rows_per_chunk);
+    p.strips = (int)((d + kTransTC - 1) / kTransTC);
+    auto groups = [&](int64_t rows) { return (int64_t)p.strips * ((n + rows - 1) / rows); };
+    int64_t rows = kTransTR;
+    while (rows < (int64_t)kTransTR * kTransMaxTiles && groups(2 * rows) >= kTransMinGroups) rows *= 2;
+    while (rows < (int64_t)kTransTR * kTransMaxTiles && !norm_select_ok((n + rows - 1) / rows, d) &&
+           norm_select_ok((n + 2 * rows - 1) / (2 * rows), d) && groups(2 * rows) >= kTransMinGroups / 2)
+        rows *= 2;
+    p.rows_per_chunk = rows;
+    p.rpt = (int)(rows / kTransTR);
+    p.chunks = (int)((n + rows - 1) / rows);
     return p;
 }
 
@@ -1006,16 +1052,12 @@ hipError_t launch_colnorm_transpose(const void *A, int64_t n, int64_t d, int64_t
                                     uint16_t *At, int64_t ldt, float *part, hipStream_t stream) {
     const int64_t a_bytes = ((n - 1) * lda + d) * 2;
     if (n % 8 || d % 8 || lda % 8 || ldt % 8 || ((uintptr_t)A & 15) || ((uintptr_t)At & 15) ||
-        a_bytes >= 0x7fffffff || (p.rpt != 1 && p.rpt != 2))
+        a_bytes >= 0x7fffffff || p.rows_per_chunk % kTransTR || p.rows_per_chunk < kTransTR ||
+        p.strips != (d + kTransTC - 1) / kTransTC)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.strips, (unsigned)p.chunks);
-    const uint16_t *Ab = static_cast<const uint16_t *>(A);
-    if (p.rpt == 2)
-        colnorm_transpose_kernel<2><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, p.rows_per_chunk, a_bytes, At,
-                                                                       ldt, part);
-    else
-        colnorm_transpose_kernel<1><<<grid, kNormThreads, 0, stream>>>(Ab, n, d, lda, p.rows_per_chunk, a_bytes, At,
-                                                                       ldt, part);
+    colnorm_transpose_kernel<kTransTC, kTransTR, kTransThreads><<<grid, kTransThreads, 0, stream>>>(
+        static_cast<const uint16_t *>(A), n, d, lda, p.rows_per_chunk, a_bytes, At, ldt, part);
     return hipGetLastError();
 }
 
