@@ -65,7 +65,7 @@ hipError_t launch_colnorm_partial(const void *A, rmm_dtype_t dt, int64_t n, int6
 // The same partials (one batch entry, bf16) from a pass that also writes
 // At = A^T (d x n, rows ldt apart), the gather source of gemm_tdma_kernel.
 // n, d, lda and ldt multiples of 8; A and At 16-byte aligned.  The plan's
-// rpt field holds the 64-row tiles per wave (1 or 2).
+// rpt field holds the 128-row tiles per row chunk (1, 2 or 4).
 ColnormPlan colnorm_transpose_plan(int64_t n, int64_t d);
 hipError_t launch_colnorm_transpose(const void *A, int64_t n, int64_t d, int64_t lda, const ColnormPlan &p,
                                     uint16_t *At, int64_t ldt, float *part, hipStream_t stream);
