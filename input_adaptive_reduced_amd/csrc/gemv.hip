@@ -183,11 +183,13 @@ __global__ __launch_bounds__(512) void gemv_wq_partial_kernel(const uint8_t *__r
 }
 
 // ---------------------------------------------------------------- one-launch decode
-// The whole single-row step in one launch: every workgroup selects the kept
-// rows itself (the selection depends only on the d values of a, 16-32 KB
-// that every workgroup reads from the caches), then streams its own block
-// of columns over all kept rows, so no workgroup waits for another and no
-// partial sums leave the workgroup (no split over rows, no reduce launch).
+// The single-row step's selection and product in one launch: every
+// workgroup selects the kept rows itself (the selection depends only on the
+// d values of a, 16-32 KB that every workgroup reads from the caches), then
+// streams its own block of columns over its split of the kept rows, so no
+// workgroup waits for another.  With one split the workgroup writes y; with
+// several (about one workgroup per CU in all) it writes fp32 partial sums,
+// which one reduce launch adds in split order.
 //
 // Selection: the key of index j is the magnitude of a_j's bf16 pattern
 // (bits 14..0), which orders like |a_j| (NaN above +Inf, -0 = +0).  A
@@ -200,10 +202,11 @@ __global__ __launch_bounds__(512) void gemv_wq_partial_kernel(const uint8_t *__r
 // same set and order as the selection kernels produce.
 //
 // Stream: LPR lanes cover a 16-byte piece each of one kept row's column
-// block (256-byte pieces for bf16, 128-byte for 8-bit codes), so a wave
-// reads 64 / LPR rows per instruction with U instructions in flight; every
-// lane accumulates its EPL columns over its rows in a fixed order, and the
-// 64 row groups of the workgroup are added in a fixed order at the end:
+// block, so a wave reads 64 / LPR rows per instruction with U instructions
+// in flight (as launched, LPR = 64: one 1 KB piece of one row, 512 bf16 or
+// 1024 8-bit columns); every lane accumulates its EPL columns over its rows
+// in a fixed order, and the workgroup's (1024 / 64) * (64 / LPR) row groups
+// are added in a fixed order at the end:
 // bit-reproducible.  BQ: 0 = bf16 B, 1 = OCP FP8 E4M3 codes, 2 = int8 codes
 // (8-bit: y[c] also times scale[c]).
 constexpr int kFusedThreads = 1024;

@@ -624,17 +624,24 @@ rmm_status_t rmm_attention(const void *q, const void *k, const void *v, int64_t 
     uint16_t *Kp = reinterpret_cast<uint16_t *>(ws + p.off_k);
     // the dimensions each query head keeps: TopK of its columns' norms (one per head)
     RMM_LAUNCH(RMM_KERNEL_COLNORM, launch_colnorm_partial(q, RMM_BF16, Lq, dh, dh, H, Lq * dh, p.cp, part, stream));
-    if (norm_select_ok(p.cp.chunks, dh)) {
-        RMM_LAUNCH(RMM_KERNEL_SELECT,
-                   launch_norm_select(part, p.cp.chunks, dh, H, p.k, idx_out, p.k, pidx, p.kpad, stream));
-    } else {
-        RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, dh, H, s, stream));
-        RMM_LAUNCH(RMM_KERNEL_SELECT,
-                   launch_select(s, nullptr, RMM_F32, 0, H, dh, p.k, idx_out, p.k, pidx, p.kpad, nullptr, stream));
-    }
     // per query head K_g[:, I_h] in MFMA operand blocks (Q's kept columns are gathered in the kernel)
-    RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(k, RMM_BF16, Lk, dh, dh, Lk * dh, H / Hkv, pidx, p.kpad, p.kpad, Kp,
-                                            p.krows * p.kpad, H, 1, stream));
+    if (select_pack_short_ok(dh, p.k, p.kpad, p.cp.chunks)) {
+        // every pack workgroup ranks its head's norms itself: no selection launch
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_select_pack_short(part, p.cp.chunks, p.k, idx_out, p.k, pidx, p.kpad, k, Lk,
+                                                             dh, dh, Lk * dh, H / Hkv, Kp, p.krows * p.kpad, H,
+                                                             stream));
+    } else {
+        if (norm_select_ok(p.cp.chunks, dh)) {
+            RMM_LAUNCH(RMM_KERNEL_SELECT,
+                       launch_norm_select(part, p.cp.chunks, dh, H, p.k, idx_out, p.k, pidx, p.kpad, stream));
+        } else {
+            RMM_LAUNCH(RMM_KERNEL_FINALIZE, launch_colnorm_finalize(part, p.cp.chunks, dh, H, s, stream));
+            RMM_LAUNCH(RMM_KERNEL_SELECT,
+                       launch_select(s, nullptr, RMM_F32, 0, H, dh, p.k, idx_out, p.k, pidx, p.kpad, nullptr, stream));
+        }
+        RMM_LAUNCH(RMM_KERNEL_PACK, launch_pack(k, RMM_BF16, Lk, dh, dh, Lk * dh, H / Hkv, pidx, p.kpad, p.kpad, Kp,
+                                                p.krows * p.kpad, H, 1, stream));
+    }
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.Q = static_cast<const uint16_t *>(q);

@@ -108,6 +108,21 @@ hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d,
                        int64_t src_stride, int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad,
                        void *dst, int64_t dst_stride, int64_t batch, int layout, hipStream_t stream);
 
+// Selection and layout-1 pack in one launch for short rows (d = 64 or 128,
+// attention head dimensions): per batch entry b, the kept set of the column
+// norms whose row-chunk partials are part[b][chunk][0..d) (the same sums,
+// keys and tie order as launch_norm_select), written to idx[b * ld_idx ..]
+// (k entries, when idx is given) and pad[b * kpad ..] (kpad entries, -1 past
+// k), and dst[b] = src[b / group][:, kept] as launch_pack with layout 1.
+// Needs k <= kpad <= d, kpad % 64 == 0, at most kSelectPackMaxChunks chunks,
+// 16-byte aligned src rows and dst.
+constexpr int64_t kSelectPackMaxChunks = 64;
+bool select_pack_short_ok(int64_t d, int64_t k, int64_t kpad, int64_t chunks);
+hipError_t launch_select_pack_short(const float *part, int64_t chunks, int64_t k, int32_t *idx, int64_t ld_idx,
+                                    int32_t *pad, int64_t kpad, const void *src, int64_t rows, int64_t d,
+                                    int64_t ld_src, int64_t src_stride, int64_t group, void *dst, int64_t dst_stride,
+                                    int64_t batch, hipStream_t stream);
+
 // A caller-supplied index set (batch rows of k int32, row b at idx + b*k)
 // into the padded list: entries in [0, d) that exceed every earlier in-range
 // entry of their row, compacted ascending, then -1 up to ld_pad.  With a_row

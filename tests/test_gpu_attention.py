@@ -146,3 +146,32 @@ def test_attention_repeatable_and_null_index_output(rmm, torch):
     torch.cuda.synchronize()
     assert st == 0
     assert torch.equal(O1, O2) and torch.equal(i1, i2) and torch.equal(O1, O3)
+
+
+def test_attention_tied_norms_at_the_boundary(rmm, torch):
+    """Exactly tied column norms across the TopK boundary: every odd column of
+    Q repeats the even column before it, so the norms come in equal pairs and
+    k = 77 (rho = 0.6 of 128) splits one pair; the lower index must be kept.
+    The per-head selection runs inside the K pack here (the pack workgroups
+    rank the norms themselves), so this pins its tie order to the oracle's."""
+    Q, K, V = synthetic.make_attention_case(dict(heads=4, kv_heads=2, L=320, dh=128))
+    # the even columns' gaps opened around pair ranks 38 and 39 (so only the
+    # exact pair ties decide the boundary), then every pair made equal
+    Qe, _ = enforce_gap_batched(np.ascontiguousarray(Q[:, :, 0::2]), [38, 39], "bf16")
+    Q = np.array(Q)
+    Q[:, :, 0::2] = Qe
+    Q[:, :, 1::2] = Qe
+    s = oracle.colnorm(Q[0])
+    k = oracle.k_of(0.6, 128)
+    order = np.argsort(-s, kind="stable")
+    assert s[order[k - 1]] == s[order[k]], "the boundary falls inside a tied pair"
+    check(rmm, torch, Q, K, V, 0.6, True)
+
+
+def test_attention_many_row_chunks(rmm, torch):
+    """A query block long enough (33024 rows) that its column norms come in
+    more row-chunk partials than the pack's own ranking takes: the separate
+    norm+select and pack launches run instead; kept dimensions exact, outputs
+    on sampled rows."""
+    Q, K, V = case(dict(heads=1, kv_heads=1, L=33024, dh=128), 0.5)
+    check(rmm, torch, Q, K, V, 0.5, True, rows=sample_rows(33024, 6, seed=8, tile=128))
