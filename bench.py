@@ -102,6 +102,22 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def code_text(text):
+    """C++/HIP source without its comments and with whitespace runs collapsed:
+    what decides the compiled kernels (string literals in these sources hold no
+    comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def code_digest(path):
+    """sha256 of code_text(path): unchanged by edits to comments or layout only."""
+    with open(path, encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()
+
+
 def library_digest():
     """sha256 over the library's HIP sources and headers, in name order."""
     import glob
@@ -183,8 +199,9 @@ def short_kernel_name(name):
 def record_traffic(workload, fetch_csv, write_csv):
     """Average FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the rows of a
     dispatch) of the workload's dominant kernel from two rocprofv3 --pmc runs of this
-    script, scaled by the copy calibration, into profiles/traffic.json with the digest
-    of the kernel's source (a later change of the source retires the record)."""
+    script, scaled by the copy calibration, into profiles/traffic.json with the digests
+    of the kernel's source file: the whole file's, and its code's without comments
+    (code_digest; a later change of the code retires the record)."""
     import csv
     key, frag, src = TRAFFIC_KERNELS[workload]
 
@@ -207,7 +224,8 @@ def record_traffic(workload, fetch_csv, write_csv):
            "read_bytes": fetch * 1024 * FETCH_SCALE, "write_bytes": write * 1024 * WRITE_SCALE,
            "fetch_kib_raw": fetch, "write_kib_raw": write, "launches": [nf, nw],
            "fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE,
-           "source": rel, "source_sha256": source_digest(os.path.join(ROOT, rel))}
+           "source": rel, "source_sha256": source_digest(os.path.join(ROOT, rel)),
+           "code_sha256": code_digest(os.path.join(ROOT, rel))}
     p = os.path.join(ROOT, "profiles", "traffic.json")
     data = {}
     if os.path.exists(p):
@@ -234,7 +252,7 @@ def load_traffic(kernel_key, workload):
     if not rec:
         return None
     src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or source_digest(src) != rec.get("source_sha256"):
+    if not os.path.exists(src) or code_digest(src) != rec.get("code_sha256"):
         return None
     return rec.get("bytes_per_launch")
 

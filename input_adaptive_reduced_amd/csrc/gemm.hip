@@ -2315,121 +2315,6 @@ __global__ __launch_bounds__(256) void pack_short_rows_kernel(const uint16_t *__
     }
 }
 
-// Attention's selection and K pack in one launch.  Workgroup (x, b) of
-// query head b ranks the head's D column norms itself from the row-chunk
-// partials of Q: the same fp32 sum in ascending chunk order, correctly
-// rounded square root and order-preserving key as norm_select_kernel, so the
-// same kept set (the k largest keys, ties to the lower index, listed in
-// ascending order).  It then packs K_g[:, I_b] for its 256 rows as
-// pack_short_rows_kernel does, reading the kept columns from LDS.  Workgroup
-// (0, b) also writes the head's kept list (idx, k entries, when given) and
-// the padded list (pad, kpad entries, -1 past k) that the attention kernel
-// reads.  The rows' loads are issued first, so the ranking runs while they
-// are in flight.  Ranking: key t's rank is the number of keys above it plus
-// the equal keys at lower indices (a strict total order, so exactly k ranks
-// fall below k); its position in the list is the number of kept indices
-// below t.
-template <int D>
-__global__ __launch_bounds__(256) void select_pack_short_kernel(const float *__restrict__ part_all, int chunks, int k,
-                                                                int32_t *__restrict__ idx_all, int64_t ld_idx,
-                                                                int32_t *__restrict__ pad_all, int64_t kpad,
-                                                                const uint16_t *__restrict__ src, int64_t rows,
-                                                                int64_t ld_src, int64_t src_stride, int64_t group,
-                                                                uint16_t *__restrict__ dst, int64_t dst_stride) {
-    constexpr int CPR = D / 8;         // 16-byte chunks per row
-    constexpr int STRIDE = D / 4 + 1;  // 8-byte words per LDS row (odd)
-    constexpr int PER = CPR;           // chunk loads per thread
-    constexpr int PF = 8;              // partials loaded ahead of the rows
-    __shared__ uint2 rowl[256 * STRIDE];
-    __shared__ __align__(16) uint32_t skey[D];
-    __shared__ int32_t ssel[D];  // kept columns ascending, then -1 (kpad <= D)
-    __shared__ int swave0;       // kept columns among the first 64
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t b = blockIdx.y;
-    const int64_t r0 = (int64_t)blockIdx.x * 256;
-    const uint16_t *S = src + (b / group) * src_stride;
-    uint16_t *Dp = dst + b * dst_stride;
-    const int nr = (int)min((int64_t)256, rows - r0);
-    const float *part = part_all + b * (int64_t)chunks * D + tid;
-
-    // the first PF partials of column tid go out before the rows' loads, so
-    // their wait does not cover the rows
-    float pv[PF];
-#pragma unroll
-    for (int u = 0; u < PF; ++u) pv[u] = (tid < D && u < chunks) ? part[(int64_t)u * D] : 0.f;
-    uint4 v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = u * 256 + tid;  // chunk e: row e / CPR, chunk e % CPR
-        const int r = e / CPR, c = e % CPR;
-        v[u] = r < nr ? *reinterpret_cast<const uint4 *>(S + (r0 + r) * ld_src + c * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < D) {
-        // ascending chunk order; the zeros past the last chunk leave the sum unchanged
-        float sum = 0.f;
-#pragma unroll
-        for (int u = 0; u < PF; ++u) sum += pv[u];
-        for (int c = PF; c < chunks; ++c) sum += part[(int64_t)c * D];
-        skey[tid] = score_key(__fsqrt_rn(sum));
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = u * 256 + tid;
-        const int r = e / CPR, c = e % CPR;
-        rowl[r * STRIDE + 2 * c] = make_uint2(v[u].x, v[u].y);
-        rowl[r * STRIDE + 2 * c + 1] = make_uint2(v[u].z, v[u].w);
-    }
-    __syncthreads();
-    bool kept = false;
-    uint64_t mask = 0;
-    if (tid < D) {  // whole waves: D is 64 or 128
-        const uint32_t key = skey[tid];
-        int rank = 0;
-        const uint4 *k4 = reinterpret_cast<const uint4 *>(skey);
-#pragma unroll 8
-        for (int q = 0; q < D / 4; ++q) {
-            const uint4 kq = k4[q];
-            const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rank += (kj[e] > key) || (kj[e] == key && 4 * q + e < tid);
-        }
-        kept = rank < k;
-        mask = __ballot(kept);
-        if (tid == 0) swave0 = __popcll(mask);
-    }
-    __syncthreads();
-    if (tid < D) {
-        const int pos = __popcll(mask & ((1ull << lane) - 1)) + (tid >= 64 ? swave0 : 0);
-        if (kept) ssel[pos] = tid;
-        if (tid >= k) ssel[tid] = -1;
-    }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-        for (int t = tid; t < kpad; t += 256) {
-            const int32_t j = ssel[t];
-            pad_all[b * kpad + t] = j;
-            if (idx_all && t < k) idx_all[b * ld_idx + t] = j;
-        }
-    }
-    const uint16_t *mine = reinterpret_cast<const uint16_t *>(rowl + tid * STRIDE);
-    const int64_t row = r0 + tid;
-    const int64_t blk = row >> 5;
-    if (row >= ((rows + 31) & ~(int64_t)31)) return;  // past the last 32-row block of the output
-#pragma unroll 2
-    for (int c = 0; c < (int)(kpad / 8); ++c) {
-        int32_t j[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) j[e] = ssel[c * 8 + e];
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = mine[max(j[e], 0)];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (j[e] >= 0 && tid < nr) ? h[e] : 0u;
-        *reinterpret_cast<uint4 *>(Dp + ((blk * (kpad >> 4) + (c >> 1)) * 64 + (c & 1) * 32 + (row & 31)) * 8) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-    }
-}
-
 // ------------------------------------------------------------------ generic SIMT path
 template <typename T>
 struct Elem;
@@ -2759,31 +2644,6 @@ hipError_t launch_splitk_reduce(const float *part, int splits, int64_t n, int64_
 
 // LDS budget for staged rows in pack_kernel.
 static constexpr int64_t kPackLdsBytes = 64 * 1024;
-
-bool select_pack_short_ok(int64_t d, int64_t k, int64_t kpad, int64_t chunks) {
-    return (d == 64 || d == 128) && k >= 1 && k <= d && kpad % 64 == 0 && kpad >= k && kpad <= d && chunks >= 1 &&
-           chunks <= kSelectPackMaxChunks;
-}
-
-hipError_t launch_select_pack_short(const float *part, int64_t chunks, int64_t k, int32_t *idx, int64_t ld_idx,
-                                    int32_t *pad, int64_t kpad, const void *src, int64_t rows, int64_t d,
-                                    int64_t ld_src, int64_t src_stride, int64_t group, void *dst, int64_t dst_stride,
-                                    int64_t batch, hipStream_t stream) {
-    if (!select_pack_short_ok(d, k, kpad, chunks) || !part || !pad || !src || !dst || rows < 1 || group < 1 ||
-        batch < 1 || batch > 65535 || (uintptr_t)src % 16 || ld_src % 8 || src_stride % 8 || (uintptr_t)dst % 16 ||
-        (rows + 255) / 256 > INT32_MAX)
-        return hipErrorInvalidValue;
-    dim3 grid((unsigned)((rows + 255) / 256), (unsigned)batch);
-    const uint16_t *sp = static_cast<const uint16_t *>(src);
-    uint16_t *dp = static_cast<uint16_t *>(dst);
-    if (d == 64)
-        select_pack_short_kernel<64><<<grid, 256, 0, stream>>>(part, (int)chunks, (int)k, idx, ld_idx, pad, kpad, sp,
-                                                               rows, ld_src, src_stride, group, dp, dst_stride);
-    else
-        select_pack_short_kernel<128><<<grid, 256, 0, stream>>>(part, (int)chunks, (int)k, idx, ld_idx, pad, kpad, sp,
-                                                                rows, ld_src, src_stride, group, dp, dst_stride);
-    return hipGetLastError();
-}
 
 hipError_t launch_pack(const void *src, rmm_dtype_t dt, int64_t rows, int64_t d, int64_t ld_src, int64_t src_stride,
                        int64_t group, const int32_t *idx, int64_t ld_idx, int64_t kpad, void *dst,

@@ -58,3 +58,21 @@ def test_every_workload_names_its_dominant_kernel():
     for key, frag, src in bench.TRAFFIC_KERNELS.values():
         assert key in ("gemm", "gemv") and os.path.exists(
             os.path.join(ROOT, "input_adaptive_reduced_amd", "csrc", src)), (key, frag, src)
+
+
+def test_traffic_record_survives_comment_edits_only(tmp_path, monkeypatch):
+    # a counter record stays current while only comments or layout of its
+    # kernel's source change, and is retired by any change of the code
+    src = tmp_path / "k.hip"
+    src.write_text("// note\n__global__ void k(int *p) { p[0] = 1; }  /* end */\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"source": "k.hip", "code_sha256": bench.code_digest(str(src)), "bytes_per_launch": 123.0}
+    (prof / "traffic.json").write_text(json.dumps({"gemm@c2": rec}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_traffic("gemm", "c2") == 123.0
+    src.write_text("// a longer note\n/* and a block\n   comment */\n__global__ void k(int *p)\n{\n    p[0] = 1;\n}\n")
+    assert bench.load_traffic("gemm", "c2") == 123.0
+    src.write_text("__global__ void k(int *p) { p[0] = 2; }\n")
+    assert bench.load_traffic("gemm", "c2") is None
+    assert bench.load_traffic("gemm", "c3") is None
