@@ -175,3 +175,13 @@ def test_attention_many_row_chunks(rmm, torch):
     on sampled rows."""
     Q, K, V = case(dict(heads=1, kv_heads=1, L=33024, dh=128), 0.5)
     check(rmm, torch, Q, K, V, 0.5, True, rows=sample_rows(33024, 6, seed=8, tile=128))
+
+
+@pytest.mark.parametrize("dh,L", [(128, 8192), (64, 16384)], ids=["d128-16chunks", "d64-16chunks"])
+def test_attention_sixteen_row_chunks(rmm, torch, dh, L):
+    """Queries long enough for 16 row-chunk partials per head (more than the
+    K pack's ranking loads ahead of its rows, within what it takes): the
+    chunks past the eighth are added in order by the pack's own loop; kept
+    dimensions exact, outputs on sampled rows."""
+    Q, K, V = case(dict(heads=2, kv_heads=1, L=L, dh=dh), 0.5)
+    check(rmm, torch, Q, K, V, 0.5, True, rows=sample_rows(L, 6, seed=9, tile=128))
